@@ -1,0 +1,196 @@
+"""CPU oracle for the MXFP8 ragged weight-gradient grouped GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``mxfp8_ragged_grouped_amd``) never imports it, and it imports nothing from the
+product path: the two share no code.
+
+The arithmetic lives in ``mxw_oracle.c`` (plain C, fp64, ascending-token
+accumulation; see its header for the definition and the format readings).  This
+module only marshals numpy arrays into it through ``ctypes`` and builds it with
+``gcc`` when asked.
+
+What the oracle computes (blog post "Ragged MXFP8 Weight Gradients: A FlyDSL
+Grouped GEMM on MI355X", section 1; ROCm blog "Group-GEMM in XLA", section
+"Contracting"):
+
+    dW[g][n][k] = sum_{m in [start_g, end_g)} e4m3(A[n][m]) 2^(sA[n][m/32]-127)
+                                             * e4m3(B[k][m]) 2^(sB[k][m/32]-127)
+
+Pins (all in ``tests/test_oracle_*.py``): every E4M3 and E8M0 code against the
+format definition; a hand-computed two-expert case; exact rational brute force
+on tiny random problems; the invariants (empty expert, scale-exponent doubling,
+single expert = dense product, operand swap = transpose, expert split = sum,
+padding garbage ignored); the XLA blog's small ragged-dot example in its
+forward and weight-gradient forms; the XLA blog's group-lookup table.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxw_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libmxw_oracle.so")
+_lib = None
+
+ERRORS = {0: "ok", -1: "null pointer", -2: "bad dimension", -3: "malformed offs", -4: "out of memory"}
+
+
+def build(force=True):
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math, no FP contraction)."""
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.mxw_oracle_e4m3.restype = ctypes.c_double
+    lib.mxw_oracle_e4m3.argtypes = [ctypes.c_uint]
+    lib.mxw_oracle_e8m0.restype = ctypes.c_double
+    lib.mxw_oracle_e8m0.argtypes = [ctypes.c_uint]
+    lib.mxw_oracle_windows.argtypes = [P, I, I64, I, P, P]
+    lib.mxw_oracle_ragged_contract_f64.argtypes = [P, P, P, P, I, I64, I, I, P]
+    lib.mxw_oracle_decode_plane.argtypes = [P, P, I, I64, I64, P]
+    lib.mxw_oracle_wgrad_f64.argtypes = [P, P, P, P, P, I, I64, I, I, P]
+    lib.mxw_oracle_wgrad_points.argtypes = [P, P, P, P, P, I, I64, I, I, P, P, P, I64, P]
+    lib.mxw_oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.mxw_oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.mxw_oracle_to_bf16.argtypes = [P, I64, P]
+    lib.mxw_oracle_max_threads.restype = I
+    lib.mxw_oracle_set_threads.argtypes = [I]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError("oracle error %d: %s" % (rc, ERRORS.get(rc, "?")))
+
+
+def _u8(a, shape=None):
+    a = np.ascontiguousarray(np.asarray(a).view(np.uint8) if np.asarray(a).dtype != np.uint8 else np.asarray(a))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (shape, a.shape))
+    return a
+
+
+def e4m3(code):
+    """Decode one OCP E4M3FN code to a Python float (NaN for S.1111.111)."""
+    return _load().mxw_oracle_e4m3(int(code))
+
+
+def e8m0(code):
+    """Decode one E8M0 scale code: 2**(code-127); NaN for 0xFF."""
+    return _load().mxw_oracle_e8m0(int(code))
+
+
+def windows(offs, M, align=32):
+    """(start, end) int64 arrays from the cumulative ends `offs`, validated:
+    non-decreasing, <= M, multiples of `align` (32 for MXFP8 operands)."""
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    E = offs.shape[0]
+    start = np.zeros(E, np.int64)
+    end = np.zeros(E, np.int64)
+    _check(_load().mxw_oracle_windows(_ptr(offs), E, int(M), int(align), _ptr(start), _ptr(end)))
+    return start, end
+
+
+def ragged_contract_f64(Ad, Bd, start, end):
+    """Core contraction on decoded fp64 operands Ad [N,M], Bd [K,M] -> [E,N,K]."""
+    Ad = np.ascontiguousarray(Ad, dtype=np.float64)
+    Bd = np.ascontiguousarray(Bd, dtype=np.float64)
+    start = np.ascontiguousarray(start, dtype=np.int64)
+    end = np.ascontiguousarray(end, dtype=np.int64)
+    N, M = Ad.shape
+    K, M2 = Bd.shape
+    if M2 != M or start.shape != end.shape:
+        raise ValueError("shape mismatch")
+    E = start.shape[0]
+    out = np.empty((E, N, K), np.float64)
+    _check(_load().mxw_oracle_ragged_contract_f64(_ptr(Ad), _ptr(Bd), _ptr(start), _ptr(end), E, M, N, K, _ptr(out)))
+    return out
+
+
+def decode_plane(q, s, used=None):
+    """Decode an MXFP8 plane q [rows, M] (uint8 codes) with scales s [rows, M/32] to fp64."""
+    q = _u8(q)
+    rows, M = q.shape
+    s = _u8(s, (rows, M // 32))
+    used = M if used is None else int(used)
+    out = np.empty((rows, M), np.float64)
+    _check(_load().mxw_oracle_decode_plane(_ptr(q), _ptr(s), rows, M, used, _ptr(out)))
+    return out
+
+
+def wgrad_f64(A, sA, B, sB, offs):
+    """Full fp64 weight gradient [E, N, K] of the MXFP8 operands."""
+    A = _u8(A)
+    N, M = A.shape
+    B = _u8(B)
+    K = B.shape[0]
+    if B.shape[1] != M:
+        raise ValueError("A and B disagree on M")
+    sA = _u8(sA, (N, M // 32))
+    sB = _u8(sB, (K, M // 32))
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    E = offs.shape[0]
+    out = np.empty((E, N, K), np.float64)
+    _check(_load().mxw_oracle_wgrad_f64(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(offs), E, M, N, K, _ptr(out)))
+    return out
+
+
+def wgrad_points(A, sA, B, sB, offs, g, n, k):
+    """dW[g[i], n[i], k[i]] in fp64 for each i, straight from the definition."""
+    A = _u8(A)
+    N, M = A.shape
+    B = _u8(B)
+    K = B.shape[0]
+    sA = _u8(sA, (N, M // 32))
+    sB = _u8(sB, (K, M // 32))
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    g = np.ascontiguousarray(g, dtype=np.int32)
+    n = np.ascontiguousarray(n, dtype=np.int32)
+    k = np.ascontiguousarray(k, dtype=np.int32)
+    if not (g.shape == n.shape == k.shape) or g.ndim != 1:
+        raise ValueError("point index arrays must be 1-D and of equal length")
+    out = np.empty(g.shape[0], np.float64)
+    _check(_load().mxw_oracle_wgrad_points(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(offs), offs.shape[0], M, N, K,
+                                           _ptr(g), _ptr(n), _ptr(k), g.shape[0], _ptr(out)))
+    return out
+
+
+def to_bf16_bits(x):
+    """Round fp64 values to bfloat16 bit patterns (uint16), nearest-even, in one step."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().mxw_oracle_to_bf16(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def max_threads():
+    return _load().mxw_oracle_max_threads()
+
+
+def set_threads(n):
+    _load().mxw_oracle_set_threads(int(n))
