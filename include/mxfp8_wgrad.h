@@ -1,0 +1,109 @@
+/*
+ * mxfp8_wgrad.h -- C ABI of the MI355X (gfx950) MXFP8 ragged weight-gradient
+ * grouped GEMM.
+ *
+ * The operation (blog post "Ragged MXFP8 Weight Gradients: A FlyDSL Grouped
+ * GEMM on MI355X", section 1): after expert-parallel dispatch the routed tokens
+ * are sorted by expert, and offs[g] is where expert g's run of tokens ends.
+ * For every expert g the weight gradient is
+ *
+ *     dW[g] = dY[g]^T * X[g]          (contraction over expert g's tokens)
+ *
+ * so the ragged axis is the contraction axis and the output [E, N, K] is
+ * dense.  The operands are MXFP8 and quantised along tokens (same section):
+ * FP8 E4M3 codes with one E8M0 scale per 32 tokens, passed as A = dY^T [N, M]
+ * and B = X^T [K, M] with the token axis contiguous, plus row-major scale
+ * planes [N, M/32] and [K, M/32].  Element by element:
+ *
+ *     dW[g][n][k] = sum_{m = start_g}^{end_g - 1}
+ *                     e4m3(A[n][m]) 2^(sA[n][m/32] - 127) *
+ *                     e4m3(B[k][m]) 2^(sB[k][m/32] - 127)
+ *
+ * with start_0 = 0, start_g = offs[g-1], end_g = offs[g] (the XLA blog
+ * "Group-GEMM in XLA", section "Contracting": group start = exclusive prefix,
+ * end = inclusive prefix).  E4M3 is the OCP E4M3FN flavour; E8M0 is 2^(s-127),
+ * 0xFF = NaN.  Accumulation is FP32 on the block-scaled MFMA; the result is
+ * rounded once to bfloat16, round-to-nearest-even (blog section 5.5).
+ *
+ * Every function is callable from C; no exception crosses the boundary.
+ */
+#ifndef MXFP8_WGRAD_H
+#define MXFP8_WGRAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MXW_OK 0
+#define MXW_ERR_NULL (-1)   /* a required pointer is NULL */
+#define MXW_ERR_DIM (-2)    /* E, M, N or K outside the supported range */
+#define MXW_ERR_ALIGN (-3)  /* A, B or out not 16-byte aligned */
+#define MXW_ERR_DEVICE (-4) /* current device is not gfx950, or no device */
+#define MXW_ERR_LAUNCH (-5) /* the kernel launch failed (hipGetLastError) */
+
+/* Supported ranges (checked on the host, no device access). */
+#define MXW_MAX_EXPERTS 256
+#define MXW_MAX_TOKENS (8 * 1024 * 1024)
+
+/*
+ * mxfp8_wgrad_grouped -- the weight-gradient grouped GEMM above.
+ *
+ * Arguments (every pointer is caller-owned DEVICE memory on the current HIP
+ * device; the library allocates nothing and keeps no state between calls):
+ *   A     uint8  [N, M]    E4M3 codes of dY^T, row stride M bytes.
+ *   sA    uint8  [N, M/32] E8M0 scales of A, row stride M/32 bytes.
+ *   B     uint8  [K, M]    E4M3 codes of X^T, row stride M bytes.
+ *   sB    uint8  [K, M/32] E8M0 scales of B, row stride M/32 bytes.
+ *   offs  int32  [E]       cumulative end of each expert's token run.
+ *   E     number of experts, 1 <= E <= MXW_MAX_EXPERTS.
+ *   M     token-axis length of A and B (routed tokens plus any padding),
+ *         0 <= M <= MXW_MAX_TOKENS, M % 32 == 0.
+ *   N, K  output dimensions, each >= 16 and a multiple of 16.
+ *   out   bf16 bit patterns [E, N, K], row-major (k contiguous).
+ *   stream  a hipStream_t (NULL = the default stream), passed as void*.
+ *
+ * Host-checked preconditions (violations return an error code and launch
+ * nothing): non-NULL pointers; A, B and out 16-byte aligned; the ranges above;
+ * the current device is gfx950.
+ *
+ * Device-data preconditions (not checked on the host, which never reads
+ * offs): offs non-decreasing, every offs[g] a multiple of 32, offs[E-1] <= M.
+ * Tokens in [offs[E-1], M) belong to no expert and may hold anything (NaN
+ * codes, 0xFF scales): they never reach the result.  Malformed offs give
+ * unspecified values but no out-of-bounds access: windows are clamped to
+ * [0, M] and every load is range-checked.
+ *
+ * Effects: enqueues one kernel on `stream` and returns without synchronising.
+ * `out` is completely overwritten; an expert with no tokens gets exact +0.0.
+ * Inputs are never written.  The result is bitwise reproducible run to run
+ * (each output element has exactly one owner and a fixed summation order; no
+ * atomics).  The compiled kernel serves every shape: E, M, N, K and offs are
+ * runtime arguments.
+ *
+ * Returns MXW_OK or a negative MXW_ERR_* code.
+ */
+int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                        const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream);
+
+/*
+ * mxw_grid_size -- the number of workgroups mxfp8_wgrad_grouped launches for
+ * (E, N, K): one per (expert, 256 x 256 output tile), i.e.
+ * E * ceil(N/256) * ceil(K/256) (blog section 4: one block per expert per
+ * output tile, which owns its tile for life).  Returns 0 for invalid sizes.
+ */
+int64_t mxw_grid_size(int E, int N, int K);
+
+/* mxw_strerror -- a static, human-readable message for a return code. */
+const char* mxw_strerror(int code);
+
+/* mxw_version -- library ABI version (major * 10000 + minor * 100 + patch). */
+int mxw_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_WGRAD_H */

@@ -1,0 +1,124 @@
+"""MI355X-native MXFP8 ragged weight-gradient grouped GEMM.
+
+    out = wgrad(A, sA, B, sB, offs)        # bf16 [E, N, K]
+
+computes, for every expert g (blog "Ragged MXFP8 Weight Gradients: A FlyDSL
+Grouped GEMM on MI355X", section 1),
+
+    dW[g] = dY[g]^T X[g]   over expert g's tokens [offs[g-1], offs[g])
+
+from MXFP8 operands A = dY^T [N, M] and B = X^T [K, M] (E4M3 codes, token axis
+contiguous) with E8M0 scale planes sA [N, M/32] and sB [K, M/32].  Everything
+runs in the HIP library ``lib/libmxfp8_wgrad.so`` (C ABI in
+``include/mxfp8_wgrad.h``); this module only checks tensor metadata and passes
+device pointers and the current stream.  There is no fallback: if the library
+is missing, or the device is not a gfx950, calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+from .build import LIB as _LIB_PATH
+
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "strerror", "version", "library_path", "MxwError"]
+
+_lib = None
+
+
+class MxwError(RuntimeError):
+    pass
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise MxwError("HIP library not built: %s (run python -m mxfp8_ragged_grouped_amd.build)" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.mxfp8_wgrad_grouped.restype = I
+    lib.mxfp8_wgrad_grouped.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
+    lib.mxw_grid_size.restype = ctypes.c_int64
+    lib.mxw_grid_size.argtypes = [I, I, I]
+    lib.mxw_strerror.restype = ctypes.c_char_p
+    lib.mxw_strerror.argtypes = [I]
+    lib.mxw_version.restype = I
+    lib.mxw_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def strerror(code):
+    return _load().mxw_strerror(int(code)).decode()
+
+
+def version():
+    return _load().mxw_version()
+
+
+def grid_size(E, N, K):
+    return int(_load().mxw_grid_size(int(E), int(N), int(K)))
+
+
+def mxfp8_wgrad_grouped(A, sA, B, sB, offs, E, M, N, K, out, stream=0):
+    """Raw C-ABI call on device addresses (ints).  Returns the status code."""
+    lib = _load()
+    return lib.mxfp8_wgrad_grouped(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, stream)
+
+
+def _as_u8(t, name):
+    if t.dtype == torch.uint8:
+        return t
+    if t.dtype == getattr(torch, "float8_e4m3fn", None) and name in ("A", "B"):
+        return t.view(torch.uint8)
+    raise TypeError("%s must be uint8 (or float8_e4m3fn for data), got %s" % (name, t.dtype))
+
+
+def wgrad(A, sA, B, sB, offs, out=None, stream=None):
+    """dW [E, N, K] bf16 from MXFP8 operands (see module docstring).
+
+    A: [N, M] uint8/float8_e4m3fn, sA: [N, M/32] uint8, B: [K, M], sB: [K, M/32],
+    offs: [E] int32 cumulative expert ends, all on one CUDA(HIP) device and
+    contiguous.  `out` (optional) is a contiguous bf16 [E, N, K] tensor that is
+    fully overwritten.  Runs on `stream` (default: the current stream) and does
+    not synchronise.
+    """
+    A = _as_u8(A, "A")
+    B = _as_u8(B, "B")
+    sA = _as_u8(sA, "sA")
+    sB = _as_u8(sB, "sB")
+    if A.dim() != 2 or B.dim() != 2 or sA.dim() != 2 or sB.dim() != 2 or offs.dim() != 1:
+        raise ValueError("A, sA, B, sB must be 2-D and offs 1-D")
+    N, M = A.shape
+    K = B.shape[0]
+    E = offs.shape[0]
+    if B.shape[1] != M or sA.shape != (N, M // 32) or sB.shape != (K, M // 32):
+        raise ValueError("shape mismatch: A %s sA %s B %s sB %s" % (tuple(A.shape), tuple(sA.shape),
+                                                                     tuple(B.shape), tuple(sB.shape)))
+    if offs.dtype != torch.int32:
+        raise TypeError("offs must be int32")
+    dev = A.device
+    for name, t in (("A", A), ("sA", sA), ("B", B), ("sB", sB), ("offs", offs)):
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("%s must be on the same GPU as A" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (E, N, K) or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bf16 [E, N, K] tensor on the same device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = mxfp8_wgrad_grouped(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
+                                 E, M, N, K, out.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise MxwError("mxfp8_wgrad_grouped failed (%d): %s" % (rc, strerror(rc)))
+    return out

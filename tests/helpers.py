@@ -1,0 +1,88 @@
+"""Shared test helpers: running the HIP path and comparing it with the oracle.
+
+Tolerance (per element, floating-point result): |gpu - ref| <= 2^-7 |ref| +
+2^-10 rms(ref), with rms over the whole [E, N, K] reference (estimated from the
+sampled points where only samples are computed).  The 2^-7 term covers the
+one bf16 rounding of the output (half an ulp is <= 2^-8 relative) plus FP32
+accumulation-order differences; the rms term absorbs cancellation near zero.
+"""
+import numpy as np
+import torch
+
+import mxfp8_ragged_grouped_amd as mxw
+import oracle
+
+REL_TOL = 2.0 ** -7
+RMS_TOL = 2.0 ** -10
+BF16_NAN = 0x7FC0
+
+
+def bf16_bits(t):
+    """uint16 numpy array of the bf16 bit patterns of a (device) bf16 tensor."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_gpu(cfg, poison=True, out=None):
+    """Run the HIP path on the config's device tensors; out is NaN-poisoned first."""
+    E, N, K = cfg["E"], cfg["N"], cfg["K"]
+    dev = cfg["A"].device
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    if poison:
+        out.view(torch.int16).fill_(BF16_NAN)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    torch.cuda.synchronize(dev)
+    return out
+
+
+def host(cfg):
+    """numpy copies of the operands for the oracle."""
+    return (cfg["A"].cpu().numpy(), cfg["sA"].cpu().numpy(), cfg["B"].cpu().numpy(), cfg["sB"].cpu().numpy(),
+            cfg["offs"].cpu().numpy())
+
+
+def check_close(got_bits, ref, rms=None, what=""):
+    """Assert the benchmark spec's tolerance element by element; returns stats."""
+    got = bf16_to_f64(np.asarray(got_bits))
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), "%s: non-finite output (skipped store or NaN leak)" % what
+    if rms is None:
+        rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    tol = REL_TOL * np.abs(ref) + RMS_TOL * rms
+    bad = err > tol
+    if bad.any():
+        idx = np.argwhere(bad)[:8]
+        raise AssertionError("%s: %d of %d elements outside tolerance; first %s; got %s ref %s" % (
+            what, int(bad.sum()), bad.size, idx.tolist(), got[bad][:8].tolist(), ref[bad][:8].tolist()))
+    # relative error where the value is not tiny next to the tensor's rms
+    big = np.abs(ref) >= 0.125 * rms
+    max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    return dict(max_abs=float(err.max()) if err.size else 0.0, max_rel=max_rel, rms=rms)
+
+
+def sample_points(cfg, per_expert=256, seed=0):
+    """Seeded output coordinates: random points per expert plus the corners and
+    edges of every edge tile (last partial N/K tile, first and last tiles)."""
+    rng = np.random.default_rng(seed)
+    E, N, K = cfg["E"], cfg["N"], cfg["K"]
+    g, n, k = [], [], []
+    edge_n = sorted({0, 1, 15, 16, 127, 128, 255, 256, N - 1, N - 2, N - 16, (N // 256) * 256 % N, N - 129})
+    edge_k = sorted({0, 1, 15, 16, 127, 128, 255, 256, K - 1, K - 4, K - 16, (K // 256) * 256 % K, K - 129})
+    edge_n = [x for x in edge_n if 0 <= x < N]
+    edge_k = [x for x in edge_k if 0 <= x < K]
+    for e in range(E):
+        g += [e] * per_expert
+        n += rng.integers(0, N, per_expert).tolist()
+        k += rng.integers(0, K, per_expert).tolist()
+        for a in edge_n:
+            for b in edge_k[::3]:
+                g.append(e)
+                n.append(a)
+                k.append(b)
+    return np.array(g, np.int32), np.array(n, np.int32), np.array(k, np.int32)

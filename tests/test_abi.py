@@ -1,0 +1,95 @@
+"""The C-ABI library: loads, exports every declared symbol, and rejects bad
+arguments on the host (CPU only; no call here reaches a device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mxfp8_ragged_grouped_amd as mxw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8_wgrad.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(mx\w+)\s*\(", text, flags=re.M)))
+
+
+def declared_macros():
+    text = open(HEADER).read()
+    return {m: int(v) for m, v in re.findall(r"#define\s+(MXW_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+def test_library_built():
+    assert os.path.exists(mxw.library_path()), "run __graft_entry__.build() first"
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_strerror", "mxw_version"}
+    lib = ctypes.CDLL(mxw.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", mxw.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_grid_size():
+    # one workgroup per (expert, 256 x 256 tile)
+    assert mxw.grid_size(4, 128, 256) == 4
+    assert mxw.grid_size(8, 1408, 2048) == 8 * 6 * 8
+    assert mxw.grid_size(32, 4096, 7168) == 32 * 16 * 28
+    assert mxw.grid_size(32, 7168, 2048) == 32 * 28 * 8
+    assert mxw.grid_size(0, 128, 128) == 0
+    assert mxw.grid_size(257, 128, 128) == 0
+
+
+def test_strerror_and_version():
+    codes = declared_macros()
+    for name in ("MXW_OK", "MXW_ERR_NULL", "MXW_ERR_DIM", "MXW_ERR_ALIGN", "MXW_ERR_DEVICE", "MXW_ERR_LAUNCH"):
+        assert name in codes
+        assert mxw.strerror(codes[name])
+    assert mxw.strerror(-99) == "unknown error"
+    assert mxw.version() >= 100
+
+
+# fake, never-dereferenced device addresses: the host checks run before any device access
+P = 0x10000
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, P, P, P, P, 4, 512, 128, 256, P), -1),            # NULL A
+    ((P, P, P, P, P, 4, 512, 128, 256, 0), -1),            # NULL out
+    ((P, P, P, P, P, 0, 512, 128, 256, P), -2),            # E = 0
+    ((P, P, P, P, P, 257, 512, 128, 256, P), -2),          # E too large
+    ((P, P, P, P, P, 4, 500, 128, 256, P), -2),            # M % 32 != 0
+    ((P, P, P, P, P, 4, -32, 128, 256, P), -2),            # M < 0
+    ((P, P, P, P, P, 4, 512, 120, 256, P), -2),            # N % 16 != 0
+    ((P, P, P, P, P, 4, 512, 128, 8, P), -2),              # K < 16
+    ((P, P, P, P, P, 4, 16 * 1024 * 1024, 128, 256, P), -2),  # M beyond the supported range
+    ((P + 8, P, P, P, P, 4, 512, 128, 256, P), -3),        # A misaligned
+    ((P, P, P, P, P, 4, 512, 128, 256, P + 2), -3),        # out misaligned
+])
+def test_host_argument_checks(args, code):
+    assert mxw.mxfp8_wgrad_grouped(*args) == code
+
+
+def test_python_face_validates_shapes():
+    import torch
+    A = torch.zeros((128, 512), dtype=torch.uint8)
+    sA = torch.zeros((128, 16), dtype=torch.uint8)
+    B = torch.zeros((256, 512), dtype=torch.uint8)
+    sB = torch.zeros((256, 15), dtype=torch.uint8)
+    offs = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mxw.wgrad(A, sA, B, sB, offs)          # sB has the wrong shape
+    sB = torch.zeros((256, 16), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mxw.wgrad(A, sA, B, sB, offs)          # CPU tensors are refused: no host fallback
+    with pytest.raises(TypeError):
+        mxw.wgrad(A, sA, B, sB, offs.to(torch.int64))

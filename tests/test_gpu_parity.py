@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path against the CPU oracle (needs an MI355X).
+
+Every case runs the C-ABI library through the Python binding on seeded inputs
+that the oracle also consumes, with the output NaN-poisoned before the launch so
+that a skipped store shows.  Small cases are compared element by element over
+the whole output; the full-size workloads (the launch configuration the
+benchmark times) on seeded sample points plus edge-tile points.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_ragged_grouped_amd as mxw
+import oracle
+import workloads as W
+from helpers import bf16_bits, check_close, host, run_gpu, sample_points
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+EXACT_CODES = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x3C, 0xBC, 0x40, 0xC0], np.uint8)  # 0, +-.5, +-1, +-1.5, +-2
+
+
+def say(msg):
+    print("[gpu-case] " + msg, flush=True)
+
+
+def full_compare(cfg, what):
+    say("%s: launch E=%d N=%d K=%d M=%d" % (what, cfg["E"], cfg["N"], cfg["K"], cfg["M"]))
+    out = run_gpu(cfg)
+    bits = bf16_bits(out)
+    ref = oracle.wgrad_f64(*host(cfg))
+    stats = check_close(bits, ref, what=what)
+    for g in range(cfg["E"]):
+        if int(cfg["sizes"][g]) == 0:
+            assert (bits[g] == 0).all(), "%s: empty expert %d not exact +0" % (what, g)
+    return out, bits, ref, stats
+
+
+def from_numpy(A, sA, B, sB, offs, sizes, device=DEV):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    N, M = A.shape
+    return dict(E=len(offs), N=N, K=B.shape[0], M=M, A=t(A), sA=t(sA), B=t(B), sB=t(sB),
+                offs=t(np.asarray(offs, np.int32)), sizes=np.asarray(sizes))
+
+
+# ----------------------------------------------------------------------------
+# small cases, whole output
+# ----------------------------------------------------------------------------
+
+
+def test_tiny_config():
+    cfg = W.make_config("tiny", device=DEV)
+    out, bits, ref, stats = full_compare(cfg, "tiny")
+    print("tiny max_rel %.3e" % stats["max_rel"])
+    assert stats["max_rel"] < 2 ** -7
+
+
+def test_hand_case_embedded(golden_dir):
+    """The hand-computed two-expert case, zero-padded into a 16 x 16 output."""
+    import json, os
+    h = json.load(open(os.path.join(golden_dir, "hand_two_expert.json")))
+    N = K = 16
+    M = h["M"]
+    A = np.zeros((N, M), np.uint8)
+    B = np.zeros((K, M), np.uint8)
+    sA = np.full((N, M // 32), 127, np.uint8)
+    sB = np.full((K, M // 32), 127, np.uint8)
+    for r, row in enumerate(h["A_rows"]):
+        for lo, hi, code in row["codes"]:
+            A[r, lo:hi] = int(code, 16)
+    for r, row in enumerate(h["B_rows"]):
+        for lo, hi, code in row["codes"]:
+            B[r, lo:hi] = int(code, 16)
+    sA[:2] = np.array(h["sA"], np.uint8)
+    sB[:1] = np.array(h["sB"], np.uint8)
+    cfg = from_numpy(A, sA, B, sB, h["offs"], [32, 64])
+    say("hand case")
+    bits = bf16_bits(run_gpu(cfg))
+    want = np.zeros((2, N, K), np.uint16)
+    for g in range(2):
+        for n in range(2):
+            want[g, n, 0] = int(h["expected_bf16"][g][n][0], 16)
+    np.testing.assert_array_equal(bits, want)
+
+
+RAGGED_CASES = [
+    # E, N, K, M, sizes (sum <= M; the rest is padding)
+    (3, 272, 528, 1024, [96, 0, 800]),          # partial N and K tiles, empty expert, padding
+    (5, 256, 256, 1056, [32, 160, 64, 352, 416]),  # M % 128 != 0 (byte scale path), short groups
+    (2, 512, 256, 2048, [1888, 160]),           # long group, tail step inside the last 128 tokens
+    (4, 144, 400, 640, [0, 0, 608, 0]),         # only one live expert, odd start
+    (1, 16, 16, 32, [32]),                      # the smallest problem
+    (6, 256, 768, 4096, [64, 1184, 0, 32, 2400, 224]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED_CASES)))
+def test_ragged_shapes(case):
+    E, N, K, M, sizes = RAGGED_CASES[case]
+    cfg = W.make_random(E, N, K, M, sizes, seed=500 + case, device=DEV)
+    full_compare(cfg, "ragged case %d" % case)
+
+
+def test_16b_1k_full():
+    """The 16B expert shape at 1,024 tokens/expert, whole output."""
+    cfg = W.make_config("16b_1k", device=DEV)
+    out, bits, ref, stats = full_compare(cfg, "16b_1k")
+    print("16b_1k max_rel %.3e" % stats["max_rel"])
+
+
+def _exact_problem(rng, E, N, K, M, sizes):
+    A = rng.choice(EXACT_CODES, (N, M))
+    B = rng.choice(EXACT_CODES, (K, M))
+    sA = rng.integers(126, 129, (N, M // 32)).astype(np.uint8)
+    sB = rng.integers(126, 129, (K, M // 32)).astype(np.uint8)
+    offs = np.cumsum(sizes).astype(np.int32)
+    return A, sA, B, sB, offs
+
+
+def test_exact_regime_bitwise():
+    """All partial sums exactly representable in FP32: GPU bf16 == RNE(oracle)
+    bit for bit, whatever the MFMA's summation order.  A misplaced scale or
+    lane shows as whole wrong rows."""
+    rng = np.random.default_rng(77)
+    sizes = [96, 0, 448, 1024, 32, 160]
+    A, sA, B, sB, offs = _exact_problem(rng, 6, 272, 528, 1920, sizes)
+    cfg = from_numpy(A, sA, B, sB, offs, sizes)
+    say("exact regime")
+    bits = bf16_bits(run_gpu(cfg))
+    ref = oracle.wgrad_f64(A, sA, B, sB, offs)
+    np.testing.assert_array_equal(bits, oracle.to_bf16_bits(ref))
+
+
+def test_bitwise_repeat():
+    cfg = W.make_random(4, 528, 784, 3072, [1056, 0, 992, 960], seed=31, device=DEV)
+    say("bitwise repeat")
+    a = bf16_bits(run_gpu(cfg))
+    b = bf16_bits(run_gpu(cfg))
+    c = bf16_bits(run_gpu(cfg, poison=False))
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a, c)
+
+
+def test_padding_garbage_ignored():
+    """NaN codes and 0xFF scales past offs[E-1] never reach the result (bitwise)."""
+    sizes = [160, 0, 288, 96]
+    cfg = W.make_random(4, 272, 272, 1024, sizes, seed=9, device=DEV)
+    used = int(np.sum(sizes))
+    say("padding garbage")
+    clean = bf16_bits(run_gpu(cfg))
+    for key, val in (("A", 0x7F), ("B", 0xFF)):
+        cfg[key][:, used:] = val
+    for key in ("sA", "sB"):
+        cfg[key][:, used // 32:] = 0xFF
+    dirty = bf16_bits(run_gpu(cfg))
+    np.testing.assert_array_equal(dirty, clean)
+
+
+def test_scale_shift_doubles_bitwise():
+    """+1 on every scale exponent of one expert's blocks doubles that expert's
+    output exactly (power-of-two scaling commutes with FP32 sums and bf16
+    rounding) and leaves the others unchanged."""
+    sizes = [192, 416, 96, 320]
+    cfg = W.make_random(4, 400, 272, 1024, sizes, seed=17, device=DEV)
+    say("scale shift")
+    base = bf16_bits(run_gpu(cfg)).astype(np.uint32)
+    lo, hi = 192, 192 + 416  # expert 1
+    cfg["sA"][:, lo // 32:hi // 32] += 1
+    shifted = bf16_bits(run_gpu(cfg)).astype(np.uint32)
+    nonzero = (base[1] & 0x7FFF) != 0
+    # doubling a bf16 = +1 in the exponent field (no overflow/underflow here)
+    np.testing.assert_array_equal(shifted[1][nonzero], base[1][nonzero] + 0x80)
+    np.testing.assert_array_equal(shifted[1][~nonzero], base[1][~nonzero])
+    for g in (0, 2, 3):
+        np.testing.assert_array_equal(shifted[g], base[g])
+
+
+def test_out_fully_overwritten_and_empty_zero():
+    cfg = W.make_random(3, 256, 512, 512, [0, 512, 0], seed=3, device=DEV)
+    say("empty experts")
+    out = torch.empty((3, 256, 512), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(0x7FC0)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    torch.cuda.synchronize()
+    bits = bf16_bits(out)
+    assert (bits[0] == 0).all() and (bits[2] == 0).all()
+    assert np.isfinite(bits[1].astype(np.uint32)).all() and (bits[1] != 0x7FC0).all()
+
+
+def test_all_experts_empty():
+    cfg = W.make_random(2, 256, 256, 64, [0, 0], seed=1, device=DEV)
+    say("all experts empty")
+    bits = bf16_bits(run_gpu(cfg))
+    assert (bits == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads, sampled
+# ----------------------------------------------------------------------------
+
+FULL = ["16b_24k", "671b_gateup", "671b_down", "671b_down_zipf", "16b_24k_skew1.7", "16b_24k_ramp"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = W.make_config(name, device=DEV)
+    say("%s: launch E=%d N=%d K=%d M=%d" % (name, cfg["E"], cfg["N"], cfg["K"], cfg["M"]))
+    out = run_gpu(cfg)
+    # every element finite (no skipped store), empty experts exact zero
+    assert torch.isfinite(out.float()).all().item()
+    for g in range(cfg["E"]):
+        if int(cfg["sizes"][g]) == 0:
+            assert (out[g].view(torch.int16) == 0).all().item()
+    g, n, k = sample_points(cfg, per_expert=192, seed=1)
+    got = bf16_bits(out)[g, n, k]
+    say("%s: oracle on %d points" % (name, len(g)))
+    ref = oracle.wgrad_points(*host(cfg), g, n, k)
+    stats = check_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what=name)
+    print("%s sampled max_rel %.3e" % (name, stats["max_rel"]))
