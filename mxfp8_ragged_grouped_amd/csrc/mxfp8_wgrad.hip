@@ -9,29 +9,34 @@
 // Structure of one launch:
 //   * grid = one 256-thread workgroup (4 wave64) per (expert, 256 x 256 output
 //     tile); a workgroup owns its tile for life, walks its expert's tokens in
-//     128-token K-steps, keeps the tile's 65,536 FP32 sums in registers and
-//     stores once (blog section 4).  No atomics: bit-reproducible.
+//     128-token K-steps, keeps the tile's 65,536 FP32 sums in accumulator
+//     registers and stores once (blog section 4).  No atomics:
+//     bit-reproducible.
 //   * tile scheduler: every workgroup reads offs itself, ranks the experts by
 //     window length with one lane per expert (longest first, ties to the lower
 //     index; blog section 5.4), and numbers tiles so that the workgroups the
 //     dispatcher deals to one XCD (block index mod 8, blog section 3) cover a
 //     compact group of 2 x 2 supertiles of the same expert (blog section 5.5).
 //   * staging: each K-step's operand stripes (256 rows x 128 tokens of A and
-//     of B) go HBM -> LDS with 16-byte LDS-direct buffer loads into a
-//     ping-pong pair of stages (blog section 4), laid out with an XOR swizzle
-//     of the 16-byte chunk index so that MFMA fragment reads are free of bank
-//     conflicts.
+//     of B, 64 KiB) go HBM -> LDS with 16-byte LDS-direct buffer loads into a
+//     ping-pong pair of stages (blog section 4); the 16-byte chunk c of row r
+//     sits at position c ^ (r & 7), which makes the MFMA fragment reads free
+//     of LDS bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT).  Each wave pulls all
+//     of a step's fragments into registers at the top of the step; a
+//     mid-step barrier then frees the stage, which is refilled for the step
+//     after next while this step's MFMAs run.  Up to two steps are in flight
+//     while one computes (the blog's "refill as soon as read", section 4).
 //   * ragged head/tail: a 32-token sub-block of a step is live iff it lies
 //     inside [start, end) (group boundaries are 32-aligned, blog section 1).
 //     Dead sub-blocks are removed twice: their data loads are pointed out of
-//     the buffer range, so the hardware returns zeros (NaN padding never
-//     reaches the MFMA, blog section 5.3), and both operands' scales are set
-//     to 0x00.
-//   * scales: one dword per row per K-step (4 sub-blocks) is loaded
-//     cooperatively (lane <-> row) and re-laid in LDS into MFMA-ready words:
-//     byte i of a word is 16-row tile i of one K-step, picked with op_sel
-//     (blog sections 3, 5.2 and 5.6), so the hot loop reads two dwords per
-//     operand per K-step and does no unpacking.
+//     the buffer range, so the hardware writes zeros (padding that holds NaN
+//     never reaches the MFMA, blog section 5.3), and both operands' scales are
+//     set to 0x00.
+//   * scales: the raw E8M0 bytes of a step (4 sub-blocks per row) also arrive
+//     by LDS-direct loads, one step ahead of the data, and each thread re-lays
+//     its row's 4 bytes into MFMA-ready words (blog sections 5.2 and 5.6):
+//     byte i of a word is 16-row tile i of one K-step, picked by op_sel, so
+//     the MFMA loop reads two dwords per operand per step and unpacks nothing.
 //   * contraction: v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3 with
 //     per-32 E8M0 scales, FP32 accumulation (blog section 3).  Operand roles
 //     are swapped (B feeds the instruction's first operand) so that each lane
@@ -46,6 +51,10 @@
 // section 3); the scale word of lane l carries the E8M0 of row l % 16 and
 // 32-token block l / 16; the result's lane l holds rows 4(l/16) .. 4(l/16)+3
 // of column l % 16.
+//
+// Every global read in the K-loop is an LDS-direct load issued through asm,
+// and the kernel waits on vmcnt itself: the compiler's wait insertion cannot
+// tell the stages apart and would drain the prefetch before each LDS read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -59,45 +68,50 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kTile = 256;              // output tile edge, N and K
-constexpr int kStep = 128;              // tokens per K-step
-constexpr int kThreads = 256;           // 4 wave64
-constexpr int kRowBytes = kStep;        // one staged row = 128 E4M3 codes
+constexpr int kTile = 256;                   // output tile edge, N and K
+constexpr int kStep = 128;                   // tokens per K-step
+constexpr int kThreads = 256;                // 4 wave64
+constexpr int kRowBytes = kStep;             // one staged row = 128 E4M3 codes
 constexpr int kOpBytes = kTile * kRowBytes;  // 32 KiB per operand per stage
-constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past any range used here
+constexpr uint32_t kOob = 0x80000000u;       // a buffer offset past any range used here
+// DMA instructions per wave per batch: 8 A + 8 B row groups, 2 x 2 scale dwords
+constexpr int kDmaPerBatch = 20;
 // raw buffer descriptor word 3 for gfx9-family: 32-bit data format, no swizzle,
 // range checking on the byte offset
 constexpr int kRsrcWord3 = 0x00020000;
 
-// One pipeline stage in LDS.
-struct Stage {
-  uint8_t a[kOpBytes];  // A stripe: 256 n-rows x 128 tokens (swizzled chunks)
-  uint8_t b[kOpBytes];  // B stripe: 256 k-rows x 128 tokens
-  // MFMA-ready scale words, index (half * 64 + lane) * 2 + word: byte i of
-  // word w is 16-row tile 4w + i of that half's 128 rows, for the sub-block
-  // lane / 16 and row lane % 16.
-  uint32_t sa[256];
-  uint32_t sb[256];
+// LDS layout (151 KiB of the 160 KiB per CU).
+struct Smem {
+  // [stage][0 = A n-rows, 1 = B k-rows]: 256 rows x 128 tokens, chunk-swizzled
+  uint8_t data[2][2][kOpBytes];
+  // raw scale dwords [step % 4][op][0 = dword at floor4(addr), 1 = the next][row]
+  uint32_t raw[4][2][2][kTile];
+  // MFMA-ready scale words [buf][op][(half * 64 + lane) * 2 + word]: byte i of
+  // word w is 16-row tile 4w + i of that half's 128 rows, for sub-block
+  // lane / 16 and row lane % 16
+  uint32_t words[2][2][256];
+  int start[MXW_MAX_EXPERTS];
+  int len[MXW_MAX_EXPERTS];
+  int order[MXW_MAX_EXPERTS];
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
-// 16-byte LDS-direct load: lane l's 16 bytes from the buffer at voff (range
-// checked; out-of-range lanes write zeros) land at LDS byte lds + 16 l.  Issued
-// through asm so that the compiler's alias-blind wait insertion does not drain
-// the prefetch before every LDS read; the kernel waits on vmcnt itself.  M0
-// carries the LDS base and needs one instruction before the load.
-// (M0 has no other user in this kernel, so clobbering it is safe.)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// LDS-direct loads: lane l's 16 (or 4) bytes from the buffer at voff (range
+// checked against the descriptor; out-of-range lanes write zeros) land at LDS
+// byte lds + 16 l (or 4 l).  M0 carries the wave-uniform LDS base and needs
+// one instruction before the load.  (M0 has no other user in this kernel.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_load16(const __amdgpu_buffer_rsrc_t& rsrc, uint32_t lds, uint32_t voff,
-                                           uint32_t soff) {
+__device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& rsrc, uint32_t lds, uint32_t voff,
+                                      uint32_t soff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
@@ -106,7 +120,24 @@ __device__ __forceinline__ void lds_load16(const __amdgpu_buffer_rsrc_t& rsrc, u
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory", "m0");
 }
+__device__ __forceinline__ void dma4(const __amdgpu_buffer_rsrc_t& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// counter waits (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; the counters not waited on are left at their maxima)
+__device__ __forceinline__ void wait_vm_batch() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerBatch & 15) | ((kDmaPerBatch >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // live-sub-block mask of K-step s for window [start, end): bit b set iff tokens
 // [128 s + 32 b, 128 s + 32 b + 32) lie inside the window.
@@ -114,7 +145,7 @@ __device__ __forceinline__ uint32_t live_mask(int s, int start, int end) {
   uint32_t m = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    int t0 = s * kStep + 32 * b;
+    const int t0 = s * kStep + 32 * b;
     m |= (uint32_t)(t0 >= start && t0 + 32 <= end) << b;
   }
   return m;
@@ -160,6 +191,13 @@ __device__ __forceinline__ v4f mfma_e4m3_sel(int oa, int ob, const v8i& a, const
   }
 }
 
+// one MFMA operand fragment: the lane's two 16-byte runs of a 16-row tile
+__device__ __forceinline__ v8i frag(const uint8_t* tile, int lo, int hi) {
+  const v4i a = *(const v4i*)(tile + lo);
+  const v4i b = *(const v4i*)(tile + hi);
+  return (v8i){a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
 struct Params {
   const uint8_t* A;
   const uint8_t* sA;
@@ -169,15 +207,14 @@ struct Params {
   uint16_t* out;
   int E, M, N, K;
   int tilesN, tilesK;
-  int xcd_map;  // 1: XCD-aware tile numbering (tiles per expert % 8 == 0)
-  int super2;   // 1: tilesN and tilesK even -> 2 x 2 supertile order
+  // XCD regions (0 = off): each expert's tilesN x tilesK grid is cut into 8
+  // rectangles of regN x regK tiles, regB of them across the K direction;
+  // rectangle x is walked in bands of `band` rows, column by column
+  int regN, regK, regB, band;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) Stage stages[2];
-  __shared__ int s_start[MXW_MAX_EXPERTS];
-  __shared__ int s_len[MXW_MAX_EXPERTS];
-  __shared__ int s_order[MXW_MAX_EXPERTS];
+  __shared__ __attribute__((aligned(16))) Smem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,48 +224,53 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   // ---- windows from offs (clamped to [0, M], monotone) ----------------------
   if (tid < E) {
     int e = min(max(p.offs[tid], 0), M);
-    int s = tid ? min(max(p.offs[tid - 1], 0), M) : 0;
+    const int s = tid ? min(max(p.offs[tid - 1], 0), M) : 0;
     if (e < s) e = s;
-    s_start[tid] = s;
-    s_len[tid] = e - s;
+    sm.start[tid] = s;
+    sm.len[tid] = e - s;
   }
   __syncthreads();
   // ---- longest-first ranking: lane g counts the experts ahead of it ---------
   if (tid < E) {
-    int mine = s_len[tid], r = 0;
+    const int mine = sm.len[tid];
+    int r = 0;
     for (int u = 0; u < E; ++u) {
-      int l = s_len[u];
+      const int l = sm.len[u];
       r += (l > mine) || (l == mine && u < tid);
     }
-    s_order[r] = tid;
+    sm.order[r] = tid;
   }
   __syncthreads();
 
-  // ---- block -> (expert rank d, tile u) -> (expert g, tile tn, tk) ----------
+  // ---- block -> (expert rank d, tile) -> (expert g, tile tn, tk) -------------
+  // The dispatcher deals block b to XCD b % 8 and each XCD starts its blocks in
+  // order.  With regions, XCD x owns the same rectangle of every expert's tile
+  // grid and works through the experts longest first, so its co-resident
+  // workgroups cover a compact block of one expert's tiles and share their A
+  // and B stripes in that XCD's L2.
   const int T = p.tilesN * p.tilesK;
   const int bid = blockIdx.x;
-  int d, u;
-  if (p.xcd_map) {
-    const int per = T >> 3;          // tiles of one expert dealt to one XCD
+  int d, tn, tk;
+  if (p.regN) {
+    const int per = p.regN * p.regK;  // = T / 8
     const int x = bid & 7, i = bid >> 3;
     d = i / per;
-    u = x * per + (i - d * per);
+    const int v = i - d * per;
+    const int bandsz = p.band * p.regK;
+    const int bnd = v / bandsz, w = v - bnd * bandsz;
+    const int hb = min(p.band, p.regN - bnd * p.band);  // rows in this band
+    const int c = w / hb;
+    tn = (x / p.regB) * p.regN + bnd * p.band + (w - c * hb);
+    tk = (x % p.regB) * p.regK + c;
   } else {
     d = bid / T;
-    u = bid - d * T;
-  }
-  int tn, tk;
-  if (p.super2) {
-    const int sq = u >> 2, q = u & 3, sk = p.tilesK >> 1;
-    tn = 2 * (sq / sk) + (q >> 1);
-    tk = 2 * (sq % sk) + (q & 1);
-  } else {
+    const int u = bid - d * T;
     tn = u / p.tilesK;
     tk = u - tn * p.tilesK;
   }
-  const int g = __builtin_amdgcn_readfirstlane(s_order[d]);
-  const int start = __builtin_amdgcn_readfirstlane(s_start[g]);
-  const int len = __builtin_amdgcn_readfirstlane(s_len[g]);
+  const int g = __builtin_amdgcn_readfirstlane(sm.order[d]);
+  const int start = __builtin_amdgcn_readfirstlane(sm.start[g]);
+  const int len = __builtin_amdgcn_readfirstlane(sm.len[g]);
   const int end = start + len;
   const int n0 = tn * kTile, k0 = tk * kTile;
   uint16_t* outg = p.out + (size_t)g * N * K;
@@ -239,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
     const int chunks = cols / 8;  // 16-byte chunks per row (K % 16 == 0)
     const v4i z = {0, 0, 0, 0};
     for (int i = tid; i < rows * chunks; i += kThreads) {
-      int r = i / chunks, c = i - r * chunks;
+      const int r = i / chunks, c = i - r * chunks;
       *(v4i*)(outg + (size_t)(n0 + r) * K + k0 + 8 * c) = z;
     }
     return;
@@ -247,66 +289,76 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
 
   // ---- buffer resources, rebased to this tile's 256-row bands ----------------
   const int rowsA = min(kTile, N - n0), rowsB = min(kTile, K - k0);
-  const int sbytes = M >> 5;  // scale bytes per row
+  const uint32_t sbytes = (uint32_t)M >> 5;  // scale bytes per row
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (size_t)n0 * M, (uint32_t)rowsA * (uint32_t)M);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + (size_t)k0 * M, (uint32_t)rowsB * (uint32_t)M);
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.sA + (size_t)n0 * sbytes, (uint32_t)rowsA * (uint32_t)sbytes);
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.sB + (size_t)k0 * sbytes, (uint32_t)rowsB * (uint32_t)sbytes);
+  // scale planes are read as whole dwords; rounding the range up to 4 bytes
+  // keeps every dword entirely inside or outside it (bytes past the plane
+  // belong to tokens >= M, which are always masked)
+  const __amdgpu_buffer_rsrc_t rsA =
+      make_rsrc(p.sA + (size_t)n0 * sbytes, ((uint32_t)rowsA * sbytes + 3u) & ~3u);
+  const __amdgpu_buffer_rsrc_t rsB =
+      make_rsrc(p.sB + (size_t)k0 * sbytes, ((uint32_t)rowsB * sbytes + 3u) & ~3u);
 
-  // ---- per-lane load geometry ------------------------------------------------
+  // ---- per-lane DMA geometry -------------------------------------------------
   // Data: wave w fills row groups 8w .. 8w+7 (8 rows x 128 B = 1 KiB each) of
   // both stripes.  Lane i of a group writes LDS bytes [16 i, 16 i + 16) of the
-  // group, i.e. row i / 8, chunk position i % 8, which holds global chunk
+  // group: row i / 8, chunk position i % 8, which holds global chunk
   // (i % 8) ^ swz(row).
-  const int lrow = lane >> 3;                 // row within a group of 8
-  const int cpos = lane & 7;                  // LDS chunk position
-  const int chunk_even = cpos ^ swz(lrow);    // global chunk for an even group
-  const int chunk_odd = cpos ^ swz(lrow + 8); // ... odd group (row bit 3 set)
-  // Scales: thread t loads the dword of tile row t (4 sub-blocks of a step).
-  const uint32_t sc_off = (uint32_t)tid * (uint32_t)sbytes;
-  const bool sc_dword = (sbytes & 3) == 0;
+  const int lrow = lane >> 3;
+  const int ch = (lane & 7) ^ swz(lrow);  // global chunk (row groups are 8-aligned)
+  // Scales: lane l of wave w fetches row 64 w + l: the dword holding its
+  // step's first scale byte and the next one (rows need not be 4-aligned).
+  const uint32_t s_lo = ((uint32_t)(wave * 64 + lane) * sbytes) & ~3u;
 
-  // Relayout destination of thread t's scale bytes: row t -> half t/128,
-  // 16-row tile (t%128)/16 -> word ((t%128)/16)/4, byte ((t%128)/16)%4, lane
-  // (t%16) + 16 * sub-block.
-  const int rh = tid >> 7, rt = (tid & 127) >> 4, rj = tid & 15;
-  const int sc_word = ((rh * 64 + rj) * 2 + (rt >> 2));  // + 32 per sub-block
-  const int sc_byte = rt & 3;
-
-  auto load_scale = [&](const __amdgpu_buffer_rsrc_t& r, int s) -> uint32_t {
-    const uint32_t off = sc_off + (uint32_t)(4 * s);
-    if (sc_dword) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)(off + b), 0, 0) << (8 * b);
-    return v;
-  };
-
-  auto issue_data = [&](Stage& S, int s, uint32_t live) {
-    const int soff = s * kStep;  // token offset of the step (wave-uniform)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int grp = wave * 8 + j;  // row group
+  // One batch = 20 LDS-direct loads per wave: slots 0..15 move the data of
+  // step sdata into stage buf (8 row groups of A and of B; dead sub-blocks are
+  // forced out of range), slots 16..19 the raw scale dwords of step sdata + 1
+  // (A lo, A hi, B lo, B hi) into raw buffer (sdata + 1) % 4.  Slots are
+  // compile-time constants once the callers unroll.
+  auto dma_slot = [&](int i, int buf, int sdata, uint32_t live) {
+    if (i < 16) {
+      const int grp = wave * 8 + (i >> 1), op = i & 1;
       const int row = grp * 8 + lrow;
-      const int ch = (grp & 1) ? chunk_odd : chunk_even;
       const bool ok = (live >> (ch >> 1)) & 1u;
-      const uint32_t base = (uint32_t)row * (uint32_t)M + (uint32_t)(ch * 16);
-      const uint32_t va = ok ? base : kOob;
-      const uint32_t da = (uint32_t)(uintptr_t)(S.a + grp * 1024);
-      const uint32_t db = (uint32_t)(uintptr_t)(S.b + grp * 1024);
-      lds_load16(rA, __builtin_amdgcn_readfirstlane(da), va, (uint32_t)soff);
-      lds_load16(rB, __builtin_amdgcn_readfirstlane(db), va, (uint32_t)soff);
+      const uint32_t va = ok ? (uint32_t)row * (uint32_t)M + (uint32_t)(ch * 16) : kOob;
+      dma16(op ? rB : rA, __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[buf][op][grp * 1024])), va,
+            (uint32_t)(sdata * kStep));
+    } else {
+      const int k = i - 16, sraw = sdata + 1;
+      const uint32_t so = s_lo + 4u * (uint32_t)sraw + 4u * (uint32_t)(k & 1);
+      dma4((k >> 1) ? rsB : rsA,
+           __builtin_amdgcn_readfirstlane(lds_addr(&sm.raw[sraw & 3][k >> 1][k & 1][wave * 64])), so);
     }
   };
-
-  auto write_scales = [&](Stage& S, uint32_t wa, uint32_t wb) {
-    uint8_t* pa = (uint8_t*)S.sa + sc_word * 4 + sc_byte;
-    uint8_t* pb = (uint8_t*)S.sb + sc_word * 4 + sc_byte;
+  auto issue_batch = [&](int buf, int sdata) {
+    const uint32_t live = live_mask(sdata, start, end);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      pa[b * 128] = (uint8_t)(wa >> (8 * b));
-      pb[b * 128] = (uint8_t)(wb >> (8 * b));
+    for (int i = 0; i < kDmaPerBatch; ++i) dma_slot(i, buf, sdata, live);
+  };
+  // raw scales of step sraw alone (prologue)
+  auto dma_raw = [&](int sraw) {
+#pragma unroll
+    for (int i = 16; i < kDmaPerBatch; ++i) dma_slot(i, 0, sraw - 1, 0);
+  };
+
+  // Relayout of thread t's scale row (row t of A and of B) for step s into
+  // words buffer wb: byte b (sub-block b) -> lane (t % 16) + 16 b of half
+  // t / 128, word ((t % 128) / 16) / 4, byte ((t % 128) / 16) % 4.
+  const int rh = tid >> 7, rt = (tid & 127) >> 4, rj = tid & 15;
+  const int wbyte = ((rh * 64 + rj) * 2 + (rt >> 2)) * 4 + (rt & 3);  // + 128 per sub-block
+  const uint32_t tshift = (((uint32_t)tid * sbytes) & 3u) * 8u;
+  auto relayout = [&](int s, int wb) {
+    const int rb = s & 3;
+    const uint32_t bm = byte_mask(live_mask(s, start, end));
+    const uint32_t a = __builtin_amdgcn_alignbit(sm.raw[rb][0][1][tid], sm.raw[rb][0][0][tid], tshift) & bm;
+    const uint32_t b = __builtin_amdgcn_alignbit(sm.raw[rb][1][1][tid], sm.raw[rb][1][0][tid], tshift) & bm;
+    uint8_t* pa = (uint8_t*)sm.words[wb][0] + wbyte;
+    uint8_t* pb = (uint8_t*)sm.words[wb][1] + wbyte;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pa[i * 128] = (uint8_t)(a >> (8 * i));
+      pb[i * 128] = (uint8_t)(b >> (8 * i));
     }
   };
 
@@ -324,69 +376,87 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // One K-step of MFMAs on stage S: the wave's 8 B-fragments (16-row k tiles)
-  // stay in registers while the 8 A-fragments (16-row n tiles) stream through,
-  // one n tile per cluster of 8 MFMAs.
-  auto compute = [&](Stage& S) {
-    const uint32_t* wsb = S.sb + (wk * 64 + lane) * 2;
-    const uint32_t* wsa = S.sa + (wn * 64 + lane) * 2;
-    const int sb0 = (int)wsb[0], sb1 = (int)wsb[1];
-    const int sa0 = (int)wsa[0], sa1 = (int)wsa[1];
-    const uint8_t* bb = S.b + (wk * 128) * kRowBytes;
-    const uint8_t* ba = S.a + (wn * 128) * kRowBytes;
-    v8i fb[8];
+  // ---- the K-loop ----------------------------------------------------------------
+  const int s0 = start / kStep;
+  const int s_end = (end + kStep - 1) / kStep;
+  const int nsteps = s_end - s0;
+
+  // Prologue: raw scales of s0, batch (data s0, scales s0 + 1), relayout of
+  // s0, then batch (data s0 + 1, scales s0 + 2).  Batches past the window are
+  // still issued, with every load out of range (no memory traffic; the stage
+  // they zero is never read again), so that exactly one batch is in flight at
+  // each barrier 1 and the loop body has no branch for the compiler to sink
+  // MFMAs into.
+  dma_raw(s0);
+  issue_batch(0, s0);
+  wait_vm_batch();  // the 4 raw-scale loads of s0 landed
+  __syncthreads();
+  relayout(s0, 0);
+  __syncthreads();  // raw buffer of s0 is free again; words of s0 written
+  issue_batch(1, s0 + 1);
+
+  for (int j = 0; j < nsteps; ++j) {
+    const int s = s0 + j;
+    const int P = j & 1;
+    // barrier 1: this step's data and the next step's raw scales have landed
+    // everywhere (only the batch of step s + 1 may still be in flight); this
+    // step's words were written during the last step.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_batch();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint8_t* ta = sm.data[P][0] + (wn * 128) * kRowBytes;
+    const uint8_t* tb = sm.data[P][1] + (wk * 128) * kRowBytes;
+    const uint32_t* wa = sm.words[P][0] + (wn * 64 + lane) * 2;
+    const uint32_t* wbw = sm.words[P][1] + (wk * 64 + lane) * 2;
+    const int sa0 = (int)wa[0], sa1 = (int)wa[1];
+    const int sb0 = (int)wbw[0], sb1 = (int)wbw[1];
+    // all of this step's fragments, in the order the MFMAs below consume them
+    v8i fa[8], fb[8];
+    fa[0] = frag(ta, frag_lo, frag_hi);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const v4i lo = *(const v4i*)(bb + t * 16 * kRowBytes + frag_lo);
-      const v4i hi = *(const v4i*)(bb + t * 16 * kRowBytes + frag_hi);
-      fb[t] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
+    for (int t = 0; t < 8; ++t) fb[t] = frag(tb + t * 16 * kRowBytes, frag_lo, frag_hi);
+#pragma unroll
+    for (int t = 1; t < 8; ++t) fa[t] = frag(ta + t * 16 * kRowBytes, frag_lo, frag_hi);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint32_t live2 = live_mask(s + 2, start, end);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const v4i lo = *(const v4i*)(ba + nt * 16 * kRowBytes + frag_lo);
-      const v4i hi = *(const v4i*)(ba + nt * 16 * kRowBytes + frag_hi);
-      const v8i fa = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const int saw = nt < 4 ? sa0 : sa1;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
-        const int sbw = kt < 4 ? sb0 : sb1;
-        acc[kt][nt] = mfma_e4m3_sel(kt & 3, nt & 3, fb[kt], fa, acc[kt][nt], sbw, saw);
+        const int m = nt * 8 + kt;
+        acc[kt][nt] = mfma_e4m3_sel(kt & 3, nt & 3, fb[kt], fa[nt], acc[kt][nt], kt < 4 ? sb0 : sb1,
+                                    nt < 4 ? sa0 : sa1);
+        if (m == 15) {
+          // barrier 2: every wave holds this step's fragments and scale words
+          // in registers, so this stage may be refilled (step after next).
+          __builtin_amdgcn_sched_barrier(0);
+          wait_lgkm_all();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (m >= 16 && m < 16 + kDmaPerBatch) {
+          // one refill load between consecutive MFMAs
+          dma_slot(m - 16, P, s + 2, live2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (m == 44) {
+          // the next step's scale words (raw scales of s + 1 landed before
+          // barrier 1; past the window they are all-zero and never read)
+          relayout(s + 1, P ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // ---- the K-loop ----------------------------------------------------------------
-  const int s_lo = start / kStep;
-  const int s_hi = (end + kStep - 1) / kStep;
-  const int nsteps = s_hi - s_lo;
-
-  uint32_t live = live_mask(s_lo, start, end);
-  issue_data(stages[0], s_lo, live);
-  uint32_t scA = load_scale(rsA, s_lo), scB = load_scale(rsB, s_lo);
-
-  for (int j = 0; j < nsteps; ++j) {
-    const int s = s_lo + j;
-    Stage& cur = stages[j & 1];
-    Stage& nxt = stages[(j & 1) ^ 1];
-    const uint32_t bm = byte_mask(live);
-    __builtin_amdgcn_sched_barrier(0);
-    write_scales(cur, scA & bm, scB & bm);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's fills of `cur` landed
-    __syncthreads();                     // all fills + scale words visible; `nxt` free
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < s_hi) {
-      live = live_mask(s + 1, start, end);
-      issue_data(nxt, s + 1, live);
-      scA = load_scale(rsA, s + 1);
-      scB = load_scale(rsB, s + 1);
-    }
-    compute(cur);
   }
+  wait_vm_all();  // no LDS-direct load may outlive the workgroup
 
   // ---- epilogue: bf16 RNE in registers, 8-byte stores -----------------------------
-  const int on = n0 + wn * 128 + fr;        // + 16 nt
-  const int ok = k0 + wk * 128 + 4 * fq;    // + 16 kt
+  const int on = n0 + wn * 128 + fr;      // + 16 nt
+  const int ok = k0 + wk * 128 + 4 * fq;  // + 16 kt
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
 #pragma unroll
@@ -456,9 +526,26 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
   p.K = K;
   p.tilesN = (N + kTile - 1) / kTile;
   p.tilesK = (K + kTile - 1) / kTile;
-  const int T = p.tilesN * p.tilesK;
-  p.xcd_map = (T % 8) == 0;
-  p.super2 = (p.tilesN % 2 == 0) && (p.tilesK % 2 == 0);
+  // XCD regions: split the tile grid a x b = 8 ways into equal rectangles,
+  // the most square split (fewest distinct A + B stripes per rectangle)
+  p.regN = p.regK = p.regB = p.band = 0;
+  int best = 1 << 30;
+  for (int a = 1; a <= 8; a *= 2) {
+    const int b = 8 / a;
+    if (p.tilesN % a || p.tilesK % b) continue;
+    const int rn = p.tilesN / a, rk = p.tilesK / b;
+    if (rn + rk < best) {
+      best = rn + rk;
+      p.regN = rn;
+      p.regK = rk;
+      p.regB = b;
+    }
+  }
+  if (p.regN) {
+    // about 32 co-resident workgroups per XCD: bands of ~32 / regK rows
+    p.band = (32 + p.regK - 1) / p.regK;
+    if (p.band > p.regN) p.band = p.regN;
+  }
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
   return MXW_OK;
