@@ -32,11 +32,17 @@
 //     the buffer range, so the hardware writes zeros (padding that holds NaN
 //     never reaches the MFMA, blog section 5.3), and both operands' scales are
 //     set to 0x00.
-//   * scales: the raw E8M0 bytes of a step (4 sub-blocks per row) also arrive
-//     by LDS-direct loads, one step ahead of the data, and each thread re-lays
-//     its row's 4 bytes into MFMA-ready words (blog sections 5.2 and 5.6):
-//     byte i of a word is 16-row tile i of one K-step, picked by op_sel, so
-//     the MFMA loop reads two dwords per operand per step and unpacks nothing.
+//   * scales: the raw E8M0 bytes arrive by LDS-direct loads and each thread
+//     re-lays its row's 4 bytes of a step into MFMA-ready words (blog
+//     sections 5.2 and 5.6): byte i of a word is 16-row tile i of one K-step,
+//     picked by op_sel, so the MFMA loop reads two dwords per operand per step
+//     and unpacks nothing.  When every row of the scale planes starts 16-byte
+//     aligned (M a multiple of 512) one 16-byte load per row brings four
+//     steps of scales into a double-buffered group area (GROUP = true);
+//     otherwise each step loads its own 4-byte dword per row, three steps
+//     ahead.  A scale dword per row per step would double the number of
+//     L1 -> L2 requests of a step (every lane hits a different row), which
+//     measurably slows the data stream; the grouped form issues 8x fewer.
 //   * contraction: v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3 with
 //     per-32 E8M0 scales, FP32 accumulation (blog section 3).  Operand roles
 //     are swapped (B feeds the instruction's first operand) so that each lane
@@ -75,18 +81,25 @@ constexpr int kThreads = 256;                // 4 wave64
 constexpr int kRowBytes = kStep;             // one staged row = 128 E4M3 codes
 constexpr int kOpBytes = kTile * kRowBytes;  // 32 KiB per operand per stage
 constexpr uint32_t kOob = 0x80000000u;       // a buffer offset past any range used here
-// DMA instructions per wave per batch: 8 A + 8 B row groups, 2 x 2 scale dwords
-constexpr int kDmaPerBatch = 20;
+// DMA instructions per wave per batch of operand data: 8 row groups of A and
+// of B.  Scale loads come on top (see the two scale paths below).
+constexpr int kDataDma = 16;
 // raw buffer descriptor word 3 for gfx9-family: 32-bit data format, no swizzle,
 // range checking on the byte offset
 constexpr int kRsrcWord3 = 0x00020000;
 
-// LDS layout (151 KiB of the 160 KiB per CU).
+// LDS layout (152 KiB of the 160 KiB per CU).
 struct Smem {
   // [stage][0 = A n-rows, 1 = B k-rows]: 256 rows x 128 tokens, chunk-swizzled
   uint8_t data[2][2][kOpBytes];
-  // raw scale dwords [step % 4][op][0 = dword at floor4(addr), 1 = the next][row]
-  uint32_t raw[4][2][2][kTile];
+  // raw E8M0 scale bytes as loaded, 16 KiB, in one of two layouts:
+  //  grouped (scale rows 16-byte aligned): [group % 2][op][row][4 dwords], the
+  //    4 sub-block bytes of 4 consecutive K-steps of a row;
+  //  per step (any row alignment): [step % 4][op][dword at floor4(addr), next][row]
+  uint32_t raw[4096];
+  // destination of the out-of-range scale-slot loads on steps that have no
+  // scale group to fetch (always written with zeros, never read)
+  uint32_t dummy[256];
   // MFMA-ready scale words [buf][op][(half * 64 + lane) * 2 + word]: byte i of
   // word w is 16-row tile 4w + i of that half's 128 rows, for sub-block
   // lane / 16 and row lane % 16
@@ -133,8 +146,9 @@ __device__ __forceinline__ void dma4(const __amdgpu_buffer_rsrc_t& rsrc, uint32_
 
 // counter waits (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the counters not waited on are left at their maxima)
-__device__ __forceinline__ void wait_vm_batch() {
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerBatch & 15) | ((kDmaPerBatch >> 4) << 14));
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -213,6 +227,9 @@ struct Params {
   int regN, regK, regB, band;
 };
 
+// GROUP: scale rows are 16-byte aligned (M % 512 == 0) and scales are loaded
+// 4 K-steps at a time; otherwise step by step.
+template <bool GROUP>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -307,39 +324,42 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   // (i % 8) ^ swz(row).
   const int lrow = lane >> 3;
   const int ch = (lane & 7) ^ swz(lrow);  // global chunk (row groups are 8-aligned)
-  // Scales: lane l of wave w fetches row 64 w + l: the dword holding its
-  // step's first scale byte and the next one (rows need not be 4-aligned).
-  const uint32_t s_lo = ((uint32_t)(wave * 64 + lane) * sbytes) & ~3u;
+  // Scales: lane l of wave w fetches scale row 64 w + l.
+  const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * sbytes;
 
-  // One batch = 20 LDS-direct loads per wave: slots 0..15 move the data of
-  // step sdata into stage buf (8 row groups of A and of B; dead sub-blocks are
-  // forced out of range), slots 16..19 the raw scale dwords of step sdata + 1
-  // (A lo, A hi, B lo, B hi) into raw buffer (sdata + 1) % 4.  Slots are
-  // compile-time constants once the callers unroll.
-  auto dma_slot = [&](int i, int buf, int sdata, uint32_t live) {
-    if (i < 16) {
-      const int grp = wave * 8 + (i >> 1), op = i & 1;
-      const int row = grp * 8 + lrow;
-      const bool ok = (live >> (ch >> 1)) & 1u;
-      const uint32_t va = ok ? (uint32_t)row * (uint32_t)M + (uint32_t)(ch * 16) : kOob;
-      dma16(op ? rB : rA, __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[buf][op][grp * 1024])), va,
-            (uint32_t)(sdata * kStep));
-    } else {
-      const int k = i - 16, sraw = sdata + 1;
-      const uint32_t so = s_lo + 4u * (uint32_t)sraw + 4u * (uint32_t)(k & 1);
-      dma4((k >> 1) ? rsB : rsA,
-           __builtin_amdgcn_readfirstlane(lds_addr(&sm.raw[sraw & 3][k >> 1][k & 1][wave * 64])), so);
-    }
+  // data of step sdata into stage buf, load i of 16 (row group 8w + i/2 of A
+  // for even i, of B for odd i); dead sub-blocks are forced out of range
+  auto dma_data = [&](int i, int buf, int sdata, uint32_t live) {
+    const int grp = wave * 8 + (i >> 1), op = i & 1;
+    const int row = grp * 8 + lrow;
+    const bool ok = (live >> (ch >> 1)) & 1u;
+    const uint32_t va = ok ? (uint32_t)row * (uint32_t)M + (uint32_t)(ch * 16) : kOob;
+    dma16(op ? rB : rA, __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[buf][op][grp * 1024])), va,
+          (uint32_t)(sdata * kStep));
   };
-  auto issue_batch = [&](int buf, int sdata) {
-    const uint32_t live = live_mask(sdata, start, end);
-#pragma unroll
-    for (int i = 0; i < kDmaPerBatch; ++i) dma_slot(i, buf, sdata, live);
+
+  // Scale loads.  A K-step needs 4 bytes of each of 512 rows; fetching them
+  // step by step presents one cache line per row per step to the memory path,
+  // as many requests as all of the step's operand data.  So when scale rows
+  // are 16-byte aligned (M % 512 == 0) each row's 16 bytes of 4 consecutive
+  // K-steps ("group" g = steps 4g .. 4g+3) come in one 16-byte load per lane,
+  // 2 per wave per group, double-buffered by group parity.  Otherwise the
+  // two dwords around each row's 4 bytes are fetched every step (4 loads per
+  // wave per step, 4 buffers by step % 4).
+  // GROUP layout; with real == false the load is out of range (no memory
+  // traffic) and lands in the dummy area, so every step issues the same count
+  auto dma_group = [&](int grp_idx, int op, bool real) {
+    const uint32_t so = real ? srow_off + 16u * (uint32_t)grp_idx : kOob;
+    const uint32_t dst = real ? lds_addr(&sm.raw[(((grp_idx & 1) * 2 + op) * kTile + wave * 64) * 4])
+                              : lds_addr(&sm.dummy[0]);
+    dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), so, 0u);
   };
-  // raw scales of step sraw alone (prologue)
-  auto dma_raw = [&](int sraw) {
-#pragma unroll
-    for (int i = 16; i < kDmaPerBatch; ++i) dma_slot(i, 0, sraw - 1, 0);
+  auto dma_raw = [&](int sraw, int k) {  // per-step layout, k = A lo, A hi, B lo, B hi
+    const uint32_t so = (srow_off & ~3u) + 4u * (uint32_t)sraw + 4u * (uint32_t)(k & 1);
+    dma4((k >> 1) ? rsB : rsA,
+         __builtin_amdgcn_readfirstlane(
+             lds_addr(&sm.raw[(((sraw & 3) * 2 + (k >> 1)) * 2 + (k & 1)) * kTile + wave * 64])),
+         so);
   };
 
   // Relayout of thread t's scale row (row t of A and of B) for step s into
@@ -349,10 +369,21 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   const int wbyte = ((rh * 64 + rj) * 2 + (rt >> 2)) * 4 + (rt & 3);  // + 128 per sub-block
   const uint32_t tshift = (((uint32_t)tid * sbytes) & 3u) * 8u;
   auto relayout = [&](int s, int wb) {
-    const int rb = s & 3;
     const uint32_t bm = byte_mask(live_mask(s, start, end));
-    const uint32_t a = __builtin_amdgcn_alignbit(sm.raw[rb][0][1][tid], sm.raw[rb][0][0][tid], tshift) & bm;
-    const uint32_t b = __builtin_amdgcn_alignbit(sm.raw[rb][1][1][tid], sm.raw[rb][1][0][tid], tshift) & bm;
+    uint32_t a, b;
+    if (GROUP) {
+      const int gb = (s >> 2) & 1, d = s & 3;
+      a = sm.raw[((gb * 2 + 0) * kTile + tid) * 4 + d];
+      b = sm.raw[((gb * 2 + 1) * kTile + tid) * 4 + d];
+    } else {
+      const int rb = s & 3;
+      a = __builtin_amdgcn_alignbit(sm.raw[((rb * 2 + 0) * 2 + 1) * kTile + tid],
+                                    sm.raw[((rb * 2 + 0) * 2 + 0) * kTile + tid], tshift);
+      b = __builtin_amdgcn_alignbit(sm.raw[((rb * 2 + 1) * 2 + 1) * kTile + tid],
+                                    sm.raw[((rb * 2 + 1) * 2 + 0) * kTile + tid], tshift);
+    }
+    a &= bm;
+    b &= bm;
     uint8_t* pa = (uint8_t*)sm.words[wb][0] + wbyte;
     uint8_t* pb = (uint8_t*)sm.words[wb][1] + wbyte;
 #pragma unroll
@@ -380,29 +411,56 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   const int s0 = start / kStep;
   const int s_end = (end + kStep - 1) / kStep;
   const int nsteps = s_end - s0;
-
-  // Prologue: raw scales of s0, batch (data s0, scales s0 + 1), relayout of
-  // s0, then batch (data s0 + 1, scales s0 + 2).  Batches past the window are
-  // still issued, with every load out of range (no memory traffic; the stage
-  // they zero is never read again), so that exactly one batch is in flight at
-  // each barrier 1 and the loop body has no branch for the compiler to sink
-  // MFMAs into.
-  dma_raw(s0);
-  issue_batch(0, s0);
-  wait_vm_batch();  // the 4 raw-scale loads of s0 landed
+  // Loads issued at step x (after its barrier 2): the data of step x + 2, plus
+  //   grouped:  2 scale-slot loads, which fetch group x / 4 + 1 (A, B) when
+  //             x % 4 == 0 and x > s0 and are out-of-range dummies otherwise;
+  //   per step: the raw scales of step x + 3 (4 loads);
+  // so a batch is always kBatch loads (the prologue covers the scales the loop
+  // starts with).
+  constexpr int kBatch = GROUP ? kDataDma + 2 : kDataDma + 4;
+  // Prologue.  Batches past the window are still issued, with every data load
+  // out of range (no memory traffic; the stage they zero is never read again),
+  // so that exactly one batch is in flight at each barrier 1 and the loop body
+  // has no data-dependent branch for the compiler to sink MFMAs into.
+  if (GROUP) {
+    dma_group(s0 >> 2, 0, true);
+    dma_group(s0 >> 2, 1, true);
+    dma_group((s0 >> 2) + 1, 0, true);
+    dma_group((s0 >> 2) + 1, 1, true);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma_raw(s0, k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma_raw(s0 + 1, k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma_raw(s0 + 2, k);
+  }
+  {
+    const uint32_t live = live_mask(s0, start, end);
+#pragma unroll
+    for (int i = 0; i < kDataDma; ++i) dma_data(i, 0, s0, live);
+  }
+  wait_vm<kDataDma>();  // the prologue's scale loads landed
   __syncthreads();
   relayout(s0, 0);
-  __syncthreads();  // raw buffer of s0 is free again; words of s0 written
-  issue_batch(1, s0 + 1);
+  __syncthreads();  // words of s0 written
+  {
+    const uint32_t live = live_mask(s0 + 1, start, end);
+#pragma unroll
+    for (int i = 0; i < kDataDma; ++i) dma_data(i, 1, s0 + 1, live);
+  }
 
   for (int j = 0; j < nsteps; ++j) {
     const int s = s0 + j;
     const int P = j & 1;
-    // barrier 1: this step's data and the next step's raw scales have landed
-    // everywhere (only the batch of step s + 1 may still be in flight); this
-    // step's words were written during the last step.
+    // barrier 1: this step's data (and every scale load issued before it) has
+    // landed everywhere; only the loads issued at step s - 1 may still be in
+    // flight.  This step's words were written during the last step.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_batch();
+    if (j == 0)
+      wait_vm<kDataDma>();
+    else
+      wait_vm<kBatch>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -437,13 +495,25 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (m >= 16 && m < 16 + kDmaPerBatch) {
+        if (m >= 16 && m < 16 + kDataDma) {
           // one refill load between consecutive MFMAs
-          dma_slot(m - 16, P, s + 2, live2);
+          dma_data(m - 16, P, s + 2, live2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (m == 16 + kDataDma) {
+          // this step's scale loads (see batch_size)
+          if (GROUP) {
+            const bool real = (s & 3) == 0 && s > s0;
+            dma_group((s >> 2) + 1, 0, real);
+            dma_group((s >> 2) + 1, 1, real);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dma_raw(s + 3, k);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         if (m == 44) {
-          // the next step's scale words (raw scales of s + 1 landed before
+          // the next step's scale words (their raw bytes landed before
           // barrier 1; past the window they are all-zero and never read)
           relayout(s + 1, P ^ 1);
           __builtin_amdgcn_sched_barrier(0);
@@ -546,7 +616,10 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
     p.band = (32 + p.regK - 1) / p.regK;
     if (p.band > p.regN) p.band = p.regN;
   }
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  if ((M & 511) == 0)
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
   return MXW_OK;
 }
