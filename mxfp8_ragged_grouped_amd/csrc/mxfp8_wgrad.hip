@@ -9,41 +9,45 @@
 // Structure of one launch:
 //   * grid = one 256-thread workgroup (4 wave64) per (expert, 256 x 256 output
 //     tile); a workgroup owns its tile for life, walks its expert's tokens in
-//     128-token K-steps, keeps the tile's 65,536 FP32 sums in accumulator
+//     64-token K-steps, keeps the tile's 65,536 FP32 sums in accumulator
 //     registers and stores once (blog section 4).  No atomics:
 //     bit-reproducible.
 //   * tile scheduler: every workgroup reads offs itself, ranks the experts by
 //     window length with one lane per expert (longest first, ties to the lower
 //     index; blog section 5.4), and numbers tiles so that the workgroups the
 //     dispatcher deals to one XCD (block index mod 8, blog section 3) cover a
-//     compact group of 2 x 2 supertiles of the same expert (blog section 5.5).
-//   * staging: each K-step's operand stripes (256 rows x 128 tokens of A and
-//     of B, 64 KiB) go HBM -> LDS with 16-byte LDS-direct buffer loads into a
-//     ping-pong pair of stages (blog section 4); the 16-byte chunk c of row r
-//     sits at position c ^ (r & 7), which makes the MFMA fragment reads free
-//     of LDS bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT).  Each wave pulls all
-//     of a step's fragments into registers at the top of the step; a
-//     mid-step barrier then frees the stage, which is refilled for the step
-//     after next while this step's MFMAs run.  Up to two steps are in flight
-//     while one computes (the blog's "refill as soon as read", section 4).
-//   * ragged head/tail: a 32-token sub-block of a step is live iff it lies
-//     inside [start, end) (group boundaries are 32-aligned, blog section 1).
-//     Dead sub-blocks are removed twice: their data loads are pointed out of
-//     the buffer range, so the hardware writes zeros (padding that holds NaN
-//     never reaches the MFMA, blog section 5.3), and both operands' scales are
-//     set to 0x00.
+//     compact rectangle of the same expert's tiles (blog section 5.5).
+//   * staging: an LDS stage holds a pair of K-steps (256 rows x 128 tokens of
+//     A and of B, 64 KiB), filled by 16-byte LDS-direct buffer loads, 8 rows x
+//     128 bytes per instruction, so every memory request is one whole cache
+//     line (half-line requests halve the miss bandwidth, measured); two stages
+//     ping-pong (blog section 4).  The 16-byte chunk c of row r sits at
+//     position c ^ (r & 7): the MFMA fragment reads are free of LDS bank
+//     conflicts (8 lanes of a read hit 8 distinct 16-byte bank groups).
+//   * software pipeline: the fragments and scale words of K-step j + 1 are
+//     read from LDS into a second register set while K-step j's 16 MFMAs run,
+//     one read per MFMA, so the MFMAs never wait on LDS and the LDS stays
+//     evenly loaded.  One barrier per K-step; at odd steps it also certifies
+//     that the next pair has landed and that the current pair has been read,
+//     and that pair's stage is refilled with the pair after next, its loads
+//     spread over the step's MFMAs.
+//   * ragged head/tail: a 32-token sub-block is live iff it lies inside
+//     [start, end) (group boundaries are 32-aligned, blog section 1).  Dead
+//     sub-blocks are removed twice: their data loads are pointed out of the
+//     buffer range, so the hardware writes zeros (padding that holds NaN never
+//     reaches the MFMA, blog section 5.3), and both operands' scales are set
+//     to 0x00.
 //   * scales: the raw E8M0 bytes arrive by LDS-direct loads and each thread
-//     re-lays its row's 4 bytes of a step into MFMA-ready words (blog
-//     sections 5.2 and 5.6): byte i of a word is 16-row tile i of one K-step,
-//     picked by op_sel, so the MFMA loop reads two dwords per operand per step
-//     and unpacks nothing.  When every row of the scale planes starts 16-byte
-//     aligned (M a multiple of 512) one 16-byte load per row brings four
-//     steps of scales into a double-buffered group area (GROUP = true);
-//     otherwise each step loads its own 4-byte dword per row, three steps
-//     ahead.  A scale dword per row per step would double the number of
-//     L1 -> L2 requests of a step (every lane hits a different row), which
-//     measurably slows the data stream; the grouped form issues 8x fewer.
-//   * contraction: v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3 with
+//     re-lays its row's 2 bytes of a K-step into MFMA-ready words (blog
+//     sections 5.2 and 5.6): byte i of a word is 32-row block i of the wave's
+//     rows, picked by op_sel, so the MFMA loop reads one dword per operand per
+//     step and unpacks nothing.  When every row of the scale planes starts
+//     16-byte aligned (M a multiple of 512) one 16-byte load per row brings 8
+//     K-steps of scales (GROUP = true); otherwise the two aligned dwords around
+//     a row's 4 bytes of 2 K-steps are loaded.  A scale load per row per step
+//     would double the number of L1 -> L2 requests of a step (every lane hits
+//     a different row), which measurably slows the data stream.
+//   * contraction: v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
 //     per-32 E8M0 scales, FP32 accumulation (blog section 3).  Operand roles
 //     are swapped (B feeds the instruction's first operand) so that each lane
 //     ends with 4 consecutive k of one output row (ROCm/aiter PR 6605,
@@ -51,12 +55,11 @@
 //   * epilogue: FP32 -> bf16 round-to-nearest-even in registers, 8-byte
 //     stores (blog section 5.5).
 //
-// MFMA lane layout used here (16x16x128, FP8 operands): lane l holds row
-// l % 16 and tokens {16(l/16) + p : p < 16} in bytes 0..15 and
-// {64 + 16(l/16) + p} in bytes 16..31 (two runs of 16, 64 apart, blog
-// section 3); the scale word of lane l carries the E8M0 of row l % 16 and
-// 32-token block l / 16; the result's lane l holds rows 4(l/16) .. 4(l/16)+3
-// of column l % 16.
+// MFMA lane layout used here (32x32x64, FP8 operands, checked on gfx950): lane
+// l holds row l % 32 and tokens {16(l/32) + p : p < 16} in bytes 0..15 and
+// {32 + 16(l/32) + p} in bytes 16..31; the scale word of lane l carries the
+// E8M0 of row l % 32 and 32-token block l / 32 (byte chosen by op_sel); the
+// result's lane l register r holds row 8(r/4) + 4(l/32) + r%4 of column l % 32.
 //
 // Every global read in the K-loop is an LDS-direct load issued through asm,
 // and the kernel waits on vmcnt itself: the compiler's wait insertion cannot
@@ -71,44 +74,47 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 256;                   // output tile edge, N and K
-constexpr int kStep = 128;                   // tokens per K-step
+constexpr int kStep = 64;                    // tokens per K-step (two 32-token sub-blocks)
+constexpr int kPair = 2 * kStep;             // tokens per LDS stage (two K-steps)
 constexpr int kThreads = 256;                // 4 wave64
-constexpr int kRowBytes = kStep;             // one staged row = 128 E4M3 codes
+constexpr int kRowBytes = kPair;             // one staged row = 128 E4M3 codes (one cache line)
 constexpr int kOpBytes = kTile * kRowBytes;  // 32 KiB per operand per stage
 constexpr uint32_t kOob = 0x80000000u;       // a buffer offset past any range used here
-// DMA instructions per wave per batch of operand data: 8 row groups of A and
-// of B.  Scale loads come on top (see the two scale paths below).
+// DMA instructions per wave per pair of K-steps for operand data: 8 row groups
+// (8 rows x 128 B = 1 KiB each) of A and 8 of B.
 constexpr int kDataDma = 16;
 // raw buffer descriptor word 3 for gfx9-family: 32-bit data format, no swizzle,
 // range checking on the byte offset
 constexpr int kRsrcWord3 = 0x00020000;
 
-// LDS layout (152 KiB of the 160 KiB per CU).
+// LDS layout (150 KiB of the 160 KiB per CU).
 struct Smem {
   // [stage][0 = A n-rows, 1 = B k-rows]: 256 rows x 128 tokens, chunk-swizzled
   uint8_t data[2][2][kOpBytes];
   // raw E8M0 scale bytes as loaded, 16 KiB, in one of two layouts:
   //  grouped (scale rows 16-byte aligned): [group % 2][op][row][4 dwords], the
-  //    4 sub-block bytes of 4 consecutive K-steps of a row;
-  //  per step (any row alignment): [step % 4][op][dword at floor4(addr), next][row]
+  //    2 sub-block bytes of 8 consecutive K-steps of a row;
+  //  paired (any row alignment): [pair % 4][op][dword][row], the two aligned
+  //    dwords that hold a row's 4 bytes of 2 consecutive K-steps
   uint32_t raw[4096];
   // destination of the out-of-range scale-slot loads on steps that have no
-  // scale group to fetch (always written with zeros, never read)
+  // scale group to fetch (written with zeros, never read)
   uint32_t dummy[256];
-  // MFMA-ready scale words [buf][op][(half * 64 + lane) * 2 + word]: byte i of
-  // word w is 16-row tile 4w + i of that half's 128 rows, for sub-block
-  // lane / 16 and row lane % 16
-  uint32_t words[2][2][256];
+  // MFMA-ready scale words [buf][op][half][lane]: byte i is 32-row block i of
+  // that half's 128 rows, for sub-block lane / 32 and row lane % 32
+  uint32_t words[2][2][2][64];
   int start[MXW_MAX_EXPERTS];
   int len[MXW_MAX_EXPERTS];
   int order[MXW_MAX_EXPERTS];
 };
 
+// 16-byte chunk c of staged row r sits at chunk position c ^ swz(r): 8
+// consecutive rows read at one chunk index then hit distinct LDS banks
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -154,23 +160,27 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 __device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // live-sub-block mask of K-step s for window [start, end): bit b set iff tokens
-// [128 s + 32 b, 128 s + 32 b + 32) lie inside the window.
+// [64 s + 32 b, 64 s + 32 b + 32) lie inside the window.
 __device__ __forceinline__ uint32_t live_mask(int s, int start, int end) {
   uint32_t m = 0;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < 2; ++b) {
     const int t0 = s * kStep + 32 * b;
     m |= (uint32_t)(t0 >= start && t0 + 32 <= end) << b;
   }
   return m;
 }
-
-// byte mask with 0xFF in byte b iff bit b of the live mask is set
-__device__ __forceinline__ uint32_t byte_mask(uint32_t live) {
+// 4-bit live mask of the 128-token pair P from sub-block indices qs, qn
+__device__ __forceinline__ uint32_t live_mask_pair(int P, int qs, int qn) {
   uint32_t m = 0;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) m |= ((live >> b) & 1u) ? (0xFFu << (8 * b)) : 0u;
+  for (int b = 0; b < 4; ++b) m |= (uint32_t)((uint32_t)(4 * P + b - qs) < (uint32_t)qn) << b;
   return m;
+}
+// the same from sub-block indices qs = start / 32, qn = (end - start) / 32
+__device__ __forceinline__ uint32_t live_mask_q(int s, int qs, int qn) {
+  const uint32_t q = (uint32_t)(2 * s - qs);
+  return (uint32_t)(q < (uint32_t)qn) | ((uint32_t)(q + 1u < (uint32_t)qn) << 1);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -181,16 +191,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return u;
 }
 
-// v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 operands (format code 0) and the
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands (format code 0) and the
 // scale byte selectors as template constants.
 template <int OA, int OB>
-__device__ __forceinline__ v4f mfma_e4m3(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+__device__ __forceinline__ v16f mfma_e4m3(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
 }
 
 // same, selectors given as values that are constant after unrolling
-__device__ __forceinline__ v4f mfma_e4m3_sel(int oa, int ob, const v8i& a, const v8i& b, const v4f& c, int sa,
-                                            int sb) {
+__device__ __forceinline__ v16f mfma_e4m3_sel(int oa, int ob, const v8i& a, const v8i& b, const v16f& c, int sa,
+                                             int sb) {
   switch (oa * 4 + ob) {
 #define MXW_SEL(A_, B_) \
   case A_ * 4 + B_:     \
@@ -205,10 +215,10 @@ __device__ __forceinline__ v4f mfma_e4m3_sel(int oa, int ob, const v8i& a, const
   }
 }
 
-// one MFMA operand fragment: the lane's two 16-byte runs of a 16-row tile
-__device__ __forceinline__ v8i frag(const uint8_t* tile, int lo, int hi) {
-  const v4i a = *(const v4i*)(tile + lo);
-  const v4i b = *(const v4i*)(tile + hi);
+// one MFMA operand fragment: the lane's two 16-byte runs of a 32-row block
+__device__ __forceinline__ v8i frag(const uint8_t* blk, int lo, int hi) {
+  const v4i a = *(const v4i*)(blk + lo);
+  const v4i b = *(const v4i*)(blk + hi);
   return (v8i){a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
@@ -228,7 +238,7 @@ struct Params {
 };
 
 // GROUP: scale rows are 16-byte aligned (M % 512 == 0) and scales are loaded
-// 4 K-steps at a time; otherwise step by step.
+// 8 K-steps at a time; otherwise 2 K-steps at a time.
 template <bool GROUP>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
@@ -318,226 +328,272 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       make_rsrc(p.sB + (size_t)k0 * sbytes, ((uint32_t)rowsB * sbytes + 3u) & ~3u);
 
   // ---- per-lane DMA geometry -------------------------------------------------
-  // Data: wave w fills row groups 8w .. 8w+7 (8 rows x 128 B = 1 KiB each) of
-  // both stripes.  Lane i of a group writes LDS bytes [16 i, 16 i + 16) of the
-  // group: row i / 8, chunk position i % 8, which holds global chunk
-  // (i % 8) ^ swz(row).
+  // Data: a stage holds a pair of K-steps (128 tokens, one cache line per row).
+  // Wave w fills row groups 8w .. 8w+7 (8 rows x 128 B = 1 KiB each) of both
+  // stripes.  Lane i of a group writes LDS bytes [16 i, 16 i + 16) of the group:
+  // row i / 8, chunk position i % 8, which holds global chunk (i % 8) ^ swz(row).
   const int lrow = lane >> 3;
-  const int ch = (lane & 7) ^ swz(lrow);  // global chunk (row groups are 8-aligned)
+  const int ch = (lane & 7) ^ swz(lrow);
+  uint32_t vrow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) vrow[q] = (uint32_t)((wave * 8 + q) * 8 + lrow) * (uint32_t)M + (uint32_t)(ch * 16);
   // Scales: lane l of wave w fetches scale row 64 w + l.
   const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * sbytes;
-
-  // data of step sdata into stage buf, load i of 16 (row group 8w + i/2 of A
-  // for even i, of B for odd i); dead sub-blocks are forced out of range
-  auto dma_data = [&](int i, int buf, int sdata, uint32_t live) {
-    const int grp = wave * 8 + (i >> 1), op = i & 1;
-    const int row = grp * 8 + lrow;
-    const bool ok = (live >> (ch >> 1)) & 1u;
-    const uint32_t va = ok ? (uint32_t)row * (uint32_t)M + (uint32_t)(ch * 16) : kOob;
-    dma16(op ? rB : rA, __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[buf][op][grp * 1024])), va,
-          (uint32_t)(sdata * kStep));
+  const int sbl = ch >> 1;  // this lane's 32-token sub-block within a pair
+  const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[0][0][wave * 8 * 1024]));
+  // pair P into stage buf: load i of 16 (row group 8w + i/2 of A for even i,
+  // of B for odd i); dead sub-blocks are forced out of range
+  auto dma_pair = [&](int i, int buf, int P, uint32_t live) {
+    const int q = i >> 1, op = i & 1;
+    const bool ok = (live >> sbl) & 1u;
+    dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + q * 1024), ok ? vrow[q] : kOob,
+          (uint32_t)(P * kPair));
   };
 
-  // Scale loads.  A K-step needs 4 bytes of each of 512 rows; fetching them
+  // Scale loads.  A K-step needs 2 bytes of each of 512 rows; fetching them
   // step by step presents one cache line per row per step to the memory path,
   // as many requests as all of the step's operand data.  So when scale rows
-  // are 16-byte aligned (M % 512 == 0) each row's 16 bytes of 4 consecutive
-  // K-steps ("group" g = steps 4g .. 4g+3) come in one 16-byte load per lane,
-  // 2 per wave per group, double-buffered by group parity.  Otherwise the
-  // two dwords around each row's 4 bytes are fetched every step (4 loads per
-  // wave per step, 4 buffers by step % 4).
-  // GROUP layout; with real == false the load is out of range (no memory
-  // traffic) and lands in the dummy area, so every step issues the same count
-  auto dma_group = [&](int grp_idx, int op, bool real) {
-    const uint32_t so = real ? srow_off + 16u * (uint32_t)grp_idx : kOob;
-    const uint32_t dst = real ? lds_addr(&sm.raw[(((grp_idx & 1) * 2 + op) * kTile + wave * 64) * 4])
-                              : lds_addr(&sm.dummy[0]);
-    dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), so, 0u);
-  };
-  auto dma_raw = [&](int sraw, int k) {  // per-step layout, k = A lo, A hi, B lo, B hi
-    const uint32_t so = (srow_off & ~3u) + 4u * (uint32_t)sraw + 4u * (uint32_t)(k & 1);
-    dma4((k >> 1) ? rsB : rsA,
-         __builtin_amdgcn_readfirstlane(
-             lds_addr(&sm.raw[(((sraw & 3) * 2 + (k >> 1)) * 2 + (k & 1)) * kTile + wave * 64])),
-         so);
+  // are 16-byte aligned (M % 512 == 0) each row's 16 bytes of 8 consecutive
+  // K-steps ("group" G = steps 8G .. 8G+7) come in one 16-byte load per lane,
+  // 2 per wave per group, double-buffered by group parity; group G + 1 is
+  // fetched at step 8G.  Otherwise the two aligned dwords around each row's 4
+  // bytes of 2 consecutive K-steps ("pair" G = steps 2G, 2G+1) are fetched,
+  // 4 loads per wave per pair, into 4 buffers by pair % 4; pair G + 3 is
+  // fetched at step 2G.  Loads with real == false are out of range (no memory
+  // traffic) and land in the dummy area, so every step issues the same count.
+  constexpr int kGroupSteps = GROUP ? 8 : 2;
+  constexpr int kAhead = GROUP ? 1 : 3;
+  constexpr int kScaleDma = GROUP ? 2 : 4;
+  auto dma_scales = [&](int grp_idx, bool real) {
+    if (GROUP) {
+#pragma unroll
+      for (int op = 0; op < 2; ++op) {
+        const uint32_t so = real ? srow_off + 16u * (uint32_t)grp_idx : kOob;
+        const uint32_t dst = real ? lds_addr(&sm.raw[(((grp_idx & 1) * 2 + op) * kTile + wave * 64) * 4])
+                                  : lds_addr(&sm.dummy[0]);
+        dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), so, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // A lo, A hi, B lo, B hi
+        const int op = k >> 1;
+        const uint32_t so = real ? (srow_off & ~3u) + 4u * (uint32_t)grp_idx + 4u * (uint32_t)(k & 1) : kOob;
+        const uint32_t dst = real ? lds_addr(&sm.raw[(((grp_idx & 3) * 2 + op) * 2 + (k & 1)) * kTile + wave * 64])
+                                  : lds_addr(&sm.dummy[0]);
+        dma4(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), so);
+      }
+    }
   };
 
   // Relayout of thread t's scale row (row t of A and of B) for step s into
-  // words buffer wb: byte b (sub-block b) -> lane (t % 16) + 16 b of half
-  // t / 128, word ((t % 128) / 16) / 4, byte ((t % 128) / 16) % 4.
-  const int rh = tid >> 7, rt = (tid & 127) >> 4, rj = tid & 15;
-  const int wbyte = ((rh * 64 + rj) * 2 + (rt >> 2)) * 4 + (rt & 3);  // + 128 per sub-block
+  // words buffer wb: sub-block b -> lane (t % 32) + 32 b of half t / 128,
+  // byte (t % 128) / 32.  Two steps: read the raw dwords (issue), then mask
+  // and write the bytes.
+  const int rh = tid >> 7, ri = (tid >> 5) & 3, rr = tid & 31;
+  const int wbyte = ((rh * 64 + rr) * 4) + ri;  // + 128 per sub-block, + 512 per op, + 1024 per buffer
   const uint32_t tshift = (((uint32_t)tid * sbytes) & 3u) * 8u;
-  auto relayout = [&](int s, int wb) {
-    const uint32_t bm = byte_mask(live_mask(s, start, end));
-    uint32_t a, b;
+  auto raw_read = [&](int s, uint32_t& a, uint32_t& b) {
     if (GROUP) {
-      const int gb = (s >> 2) & 1, d = s & 3;
-      a = sm.raw[((gb * 2 + 0) * kTile + tid) * 4 + d];
-      b = sm.raw[((gb * 2 + 1) * kTile + tid) * 4 + d];
+      const int slot = (s >> 3) & 1, dw = (s & 7) >> 1;
+      a = sm.raw[((slot * 2 + 0) * kTile + tid) * 4 + dw];
+      b = sm.raw[((slot * 2 + 1) * kTile + tid) * 4 + dw];
     } else {
-      const int rb = s & 3;
-      a = __builtin_amdgcn_alignbit(sm.raw[((rb * 2 + 0) * 2 + 1) * kTile + tid],
-                                    sm.raw[((rb * 2 + 0) * 2 + 0) * kTile + tid], tshift);
-      b = __builtin_amdgcn_alignbit(sm.raw[((rb * 2 + 1) * 2 + 1) * kTile + tid],
-                                    sm.raw[((rb * 2 + 1) * 2 + 0) * kTile + tid], tshift);
-    }
-    a &= bm;
-    b &= bm;
-    uint8_t* pa = (uint8_t*)sm.words[wb][0] + wbyte;
-    uint8_t* pb = (uint8_t*)sm.words[wb][1] + wbyte;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pa[i * 128] = (uint8_t)(a >> (8 * i));
-      pb[i * 128] = (uint8_t)(b >> (8 * i));
+      const int slot = (s >> 1) & 3;
+      a = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 0) * 2 + 1) * kTile + tid],
+                                    sm.raw[((slot * 2 + 0) * 2 + 0) * kTile + tid], tshift);
+      b = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 1) * 2 + 1) * kTile + tid],
+                                    sm.raw[((slot * 2 + 1) * 2 + 0) * kTile + tid], tshift);
     }
   };
+  auto raw_write_m = [&](int s, int wb, uint32_t a, uint32_t b, uint32_t live) {
+    const int sh = (s & 1) * 16;
+    uint8_t* base = (uint8_t*)&sm.words[wb][0][0][0] + wbyte;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const bool ok = (live >> sb) & 1u;
+      base[sb * 128] = ok ? (uint8_t)(a >> (sh + 8 * sb)) : (uint8_t)0;
+      base[512 + sb * 128] = ok ? (uint8_t)(b >> (sh + 8 * sb)) : (uint8_t)0;
+    }
+  };
+  auto raw_write = [&](int s, int wb, uint32_t a, uint32_t b) { raw_write_m(s, wb, a, b, live_mask(s, start, end)); };
 
   // ---- MFMA geometry -----------------------------------------------------------
+  // wave (wn, wk) owns A rows 128 wn .. +128 and B rows 128 wk .. +128: 4 x 4
+  // blocks of 32 x 32 outputs.  Fragment of a 32-row block for the first
+  // K-step of a pair: lane l reads row l % 32, chunks l / 32 and l / 32 + 2
+  // (tokens 16 (l / 32) + 0..15 and 32 + 16 (l / 32) + 0..15); for the second
+  // K-step, chunks 4 further on.
   const int wn = wave >> 1, wk = wave & 1;
-  const int fr = lane & 15, fq = lane >> 4;
-  // byte offsets of this lane's two 16-byte runs inside a 16-row tile: chunk
-  // fq (tokens 16 fq ..) and chunk fq + 4 (tokens 64 + 16 fq ..), swizzled
-  const int frag_lo = fr * kRowBytes + ((fq ^ swz(fr)) << 4);
-  const int frag_hi = fr * kRowBytes + (((fq + 4) ^ swz(fr)) << 4);
+  const int fr = lane & 31, fq = lane >> 5;
+  const int frag_lo0 = fr * kRowBytes + ((fq ^ swz(fr)) << 4);
+  const int frag_hi0 = fr * kRowBytes + (((fq + 2) ^ swz(fr)) << 4);
+  const int frag_lo1 = fr * kRowBytes + (((fq + 4) ^ swz(fr)) << 4);
+  const int frag_hi1 = fr * kRowBytes + (((fq + 6) ^ swz(fr)) << 4);
 
-  v4f acc[8][8];
+  v16f acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
 
   // ---- the K-loop ----------------------------------------------------------------
-  const int s0 = start / kStep;
+  // K-step j of the window (tokens [64 (s0 + j), +64)) is half j % 2 of pair
+  // (s0 + j) / 2, which sits in stage (j / 2) % 2.  A pair is DMA'd as whole
+  // 128-byte row segments (one cache line per row, so every memory request
+  // carries a full line).  Step j + 1's fragments and scale words are read into
+  // register set (j + 1) % 2 during step j, so step j's MFMAs never wait on
+  // LDS.  Each step has one barrier (after its first two MFMAs); at odd steps
+  // it also certifies that the next pair has landed and that every wave has
+  // read the current pair, whose stage then takes the pair after next.
+  const int s0 = (start / kPair) * 2;
   const int s_end = (end + kStep - 1) / kStep;
-  const int nsteps = s_end - s0;
-  // Loads issued at step x (after its barrier 2): the data of step x + 2, plus
-  //   grouped:  2 scale-slot loads, which fetch group x / 4 + 1 (A, B) when
-  //             x % 4 == 0 and x > s0 and are out-of-range dummies otherwise;
-  //   per step: the raw scales of step x + 3 (4 loads);
-  // so a batch is always kBatch loads (the prologue covers the scales the loop
-  // starts with).
-  constexpr int kBatch = GROUP ? kDataDma + 2 : kDataDma + 4;
-  // Prologue.  Batches past the window are still issued, with every data load
-  // out of range (no memory traffic; the stage they zero is never read again),
-  // so that exactly one batch is in flight at each barrier 1 and the loop body
-  // has no data-dependent branch for the compiler to sink MFMAs into.
-  if (GROUP) {
-    dma_group(s0 >> 2, 0, true);
-    dma_group(s0 >> 2, 1, true);
-    dma_group((s0 >> 2) + 1, 0, true);
-    dma_group((s0 >> 2) + 1, 1, true);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dma_raw(s0, k);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dma_raw(s0 + 1, k);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dma_raw(s0 + 2, k);
-  }
+  const int nsteps = (s_end - s0 + 3) & ~3;  // a multiple of 4: the loop body is unrolled by 4
+
+  // Every step issues kScaleDma scale-slot loads; odd steps first issue the
+  // 16 loads of the pair after next.  At the barrier of odd step j the pair
+  // issued at step j - 2 must have landed: only the two scale slots issued
+  // since may be in flight.
+  constexpr int kSlot = kScaleDma;
+
+  // Prologue: the scale groups the first steps need, pairs s0/2 and s0/2 + 1,
+  // and one dummy scale slot (so the first odd barrier sees the usual count).
+  const int qs = start >> 5, qn = (end - start) >> 5;
   {
-    const uint32_t live = live_mask(s0, start, end);
+    const int G0 = s0 / kGroupSteps;
 #pragma unroll
-    for (int i = 0; i < kDataDma; ++i) dma_data(i, 0, s0, live);
+    for (int a = 0; a <= kAhead; ++a) dma_scales(G0 + a, true);
+    const int P0 = s0 >> 1;
+    const uint32_t l0 = live_mask_pair(P0, qs, qn), l1 = live_mask_pair(P0 + 1, qs, qn);
+#pragma unroll
+    for (int i = 0; i < kDataDma; ++i) dma_pair(i, 0, P0, l0);
+#pragma unroll
+    for (int i = 0; i < kDataDma; ++i) dma_pair(i, 1, P0 + 1, l1);
+    dma_scales(0, false);
   }
-  wait_vm<kDataDma>();  // the prologue's scale loads landed
+  wait_vm<kDataDma + kSlot>();  // scales and pair s0/2 landed (this wave)
   __syncthreads();
-  relayout(s0, 0);
-  __syncthreads();  // words of s0 written
   {
-    const uint32_t live = live_mask(s0 + 1, start, end);
+    uint32_t a0, b0, a1, b1;
+    raw_read(s0, a0, b0);
+    raw_read(s0 + 1, a1, b1);
+    raw_write(s0, 0, a0, b0);
+    raw_write(s0 + 1, 1, a1, b1);
+  }
+  __syncthreads();
+
+  v8i fa[2][4], fb[2][4];
+  int sa[2], sb[2];
+  {
+    const uint8_t* ta = sm.data[0][0] + (wn * 128) * kRowBytes;
+    const uint8_t* tb = sm.data[0][1] + (wk * 128) * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kDataDma; ++i) dma_data(i, 1, s0 + 1, live);
+    for (int t = 0; t < 4; ++t) fb[0][t] = frag(tb + t * 32 * kRowBytes, frag_lo0, frag_hi0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fa[0][t] = frag(ta + t * 32 * kRowBytes, frag_lo0, frag_hi0);
+    sa[0] = (int)sm.words[0][0][wn][lane];
+    sb[0] = (int)sm.words[0][1][wk][lane];
   }
 
-  for (int j = 0; j < nsteps; ++j) {
-    const int s = s0 + j;
-    const int P = j & 1;
-    // barrier 1: this step's data (and every scale load issued before it) has
-    // landed everywhere; only the loads issued at step s - 1 may still be in
-    // flight.  This step's words were written during the last step.
-    __builtin_amdgcn_sched_barrier(0);
-    if (j == 0)
-      wait_vm<kDataDma>();
-    else
-      wait_vm<kBatch>();
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+  // per-step scalars of the first step; later steps compute theirs one step ahead
+  uint32_t livep = live_mask_pair((s0 >> 1) + 2, qs, qn);  // pair issued at the next odd step
+  uint32_t live2 = live_mask_q(s0 + 2, qs, qn);
+  int sgrp = s0 / kGroupSteps + kAhead;
+  bool sreal = false;  // s0 never issues a real scale load
 
-    const uint8_t* ta = sm.data[P][0] + (wn * 128) * kRowBytes;
-    const uint8_t* tb = sm.data[P][1] + (wk * 128) * kRowBytes;
-    const uint32_t* wa = sm.words[P][0] + (wn * 64 + lane) * 2;
-    const uint32_t* wbw = sm.words[P][1] + (wk * 64 + lane) * 2;
-    const int sa0 = (int)wa[0], sa1 = (int)wa[1];
-    const int sb0 = (int)wbw[0], sb1 = (int)wbw[1];
-    // all of this step's fragments, in the order the MFMAs below consume them
-    v8i fa[8], fb[8];
-    fa[0] = frag(ta, frag_lo, frag_hi);
+#define MXW_DMA(I, U) dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + ((I) >> 1) * 1024), va[(I) >> 1], soffp)
+  for (int jj = 0;; jj += 4) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) fb[t] = frag(tb + t * 16 * kRowBytes, frag_lo, frag_hi);
+    for (int u = 0; u < 4; ++u) {
+      const int j = jj + u;
+      const int s = s0 + j;
+      const int cur = u & 1, nxt = cur ^ 1;
+      const int nst = ((u + 1) >> 1) & 1, nhalf = (u + 1) & 1;  // stage and half of step j + 1
+      const uint8_t* na = sm.data[nst][0] + (wn * 128) * kRowBytes;
+      const uint8_t* nb = sm.data[nst][1] + (wk * 128) * kRowBytes;
+      const int flo = nhalf ? frag_lo1 : frag_lo0, fhi = nhalf ? frag_hi1 : frag_hi0;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm_all();  // this step's fragments and words are in registers
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t ra = 0, rb = 0;
+      uint32_t va[8];
+      uint32_t soffp = 0;
 #pragma unroll
-    for (int t = 1; t < 8; ++t) fa[t] = frag(ta + t * 16 * kRowBytes, frag_lo, frag_hi);
-    __builtin_amdgcn_sched_barrier(0);
-
-    const uint32_t live2 = live_mask(s + 2, start, end);
+      for (int m = 0; m < 16; ++m) {
+        const int i = m >> 2, t = m & 3;  // B block i, A block t
+        acc[i][t] = mfma_e4m3_sel(i, t, fb[cur][i], fa[cur][t], acc[i][t], sb[cur], sa[cur]);
+        if (m == 0 && (u & 1)) {
+          const bool lok = (livep >> sbl) & 1u;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const int m = nt * 8 + kt;
-        acc[kt][nt] = mfma_e4m3_sel(kt & 3, nt & 3, fb[kt], fa[nt], acc[kt][nt], kt < 4 ? sb0 : sb1,
-                                    nt < 4 ? sa0 : sa1);
-        if (m == 15) {
-          // barrier 2: every wave holds this step's fragments and scale words
-          // in registers, so this stage may be refilled (step after next).
+          for (int q = 0; q < 8; ++q) va[q] = lok ? vrow[q] : kOob;
+        }
+        if (m == 1) {
           __builtin_amdgcn_sched_barrier(0);
-          wait_lgkm_all();
+          if (u & 1) wait_vm<2 * kSlot>(); else wait_vm<kDataDma + 2 * kSlot>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (m >= 16 && m < 16 + kDataDma) {
-          // one refill load between consecutive MFMAs
-          dma_data(m - 16, P, s + 2, live2);
-          __builtin_amdgcn_sched_barrier(0);
+        if (m == 2) {
+          int sp = s;
+          asm volatile("" : "+s"(sp));
+          soffp = (uint32_t)(((sp >> 1) + 2) * kPair);
+          raw_read(sp + 2, ra, rb);
         }
-        if (m == 16 + kDataDma) {
-          // this step's scale loads (see batch_size)
-          if (GROUP) {
-            const bool real = (s & 3) == 0 && s > s0;
-            dma_group((s >> 2) + 1, 0, real);
-            dma_group((s >> 2) + 1, 1, real);
-          } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) dma_raw(s + 3, k);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        if (u & 1) {
+          if (m == 2) { MXW_DMA(0, u); MXW_DMA(1, u); }
+          if (m == 3) { MXW_DMA(2, u); MXW_DMA(3, u); }
+          if (m == 4) { MXW_DMA(4, u); MXW_DMA(5, u); }
+          if (m == 5) { MXW_DMA(6, u); MXW_DMA(7, u); }
+          if (m == 6) { MXW_DMA(8, u); MXW_DMA(9, u); }
+          if (m == 7) { MXW_DMA(10, u); MXW_DMA(11, u); }
+          if (m == 8) { MXW_DMA(12, u); MXW_DMA(13, u); }
+          if (m == 9) { MXW_DMA(14, u); MXW_DMA(15, u); }
         }
-        if (m == 44) {
-          // the next step's scale words (their raw bytes landed before
-          // barrier 1; past the window they are all-zero and never read)
-          relayout(s + 1, P ^ 1);
-          __builtin_amdgcn_sched_barrier(0);
+        if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
+        if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
+        if (m == 10) dma_scales(sgrp, sreal);
+        if (m == 11) {
+          sa[nxt] = (int)sm.words[(u + 1) & 1][0][wn][lane];
+          sb[nxt] = (int)sm.words[(u + 1) & 1][1][wk][lane];
         }
+        if (m == 12) raw_write_m(s + 2, u & 1, ra, rb, live2);
+        if (m == 13) {
+          int sp = s;
+          asm volatile("" : "+s"(sp));
+          if (!(u & 1)) livep = live_mask_pair(((sp + 1) >> 1) + 2, qs, qn);
+          live2 = live_mask_q(sp + 3, qs, qn);
+          sreal = ((sp + 1) % kGroupSteps) == 0;
+          sgrp = (sp + 1) / kGroupSteps + kAhead;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (jj + 4 >= nsteps) break;
   }
+#undef MXW_DMA
   wait_vm_all();  // no LDS-direct load may outlive the workgroup
 
   // ---- epilogue: bf16 RNE in registers, 8-byte stores -----------------------------
-  const int on = n0 + wn * 128 + fr;      // + 16 nt
-  const int ok = k0 + wk * 128 + 4 * fq;  // + 16 kt
+  // block (i, t): lane l register r holds k = 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
+  // n = 32 t + l % 32 (within the wave's quarter)
+  const int on = n0 + wn * 128 + fr;      // + 32 t
+  const int ok = k0 + wk * 128 + 4 * fq;  // + 32 i + 8 q
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int n = on + 16 * nt, k = ok + 16 * kt;
-      if (n < N && k < K) {
-        const v4f v = acc[kt][nt];
-        uint2 w;
-        w.x = pack_bf16x2(v.x, v.y);
-        w.y = pack_bf16x2(v.z, v.w);
-        *(uint2*)(outg + (size_t)n * K + k) = w;
+    for (int t = 0; t < 4; ++t) {
+      const int n = on + 32 * t;
+      if (n < N) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = ok + 32 * i + 8 * q;
+          if (k < K) {
+            const v16f& v = acc[i][t];
+            uint2 w;
+            w.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
+            w.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+            *(uint2*)(outg + (size_t)n * K + k) = w;
+          }
+        }
       }
     }
   }
