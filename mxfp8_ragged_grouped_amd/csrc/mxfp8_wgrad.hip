@@ -539,18 +539,17 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
           raw_read(sp + 2, ra, rb);
         }
         if (u & 1) {
+          // one load per MFMA (two at the first two slots): the 4 waves then
+          // present about one 1 KiB load per 16 clocks, the rate at which the
+          // vector memory path of a CU takes them; denser bursts stall issue
+          // and with it the MFMAs queued behind
           if (m == 2) { MXW_DMA(0, u); MXW_DMA(1, u); }
           if (m == 3) { MXW_DMA(2, u); MXW_DMA(3, u); }
-          if (m == 4) { MXW_DMA(4, u); MXW_DMA(5, u); }
-          if (m == 5) { MXW_DMA(6, u); MXW_DMA(7, u); }
-          if (m == 6) { MXW_DMA(8, u); MXW_DMA(9, u); }
-          if (m == 7) { MXW_DMA(10, u); MXW_DMA(11, u); }
-          if (m == 8) { MXW_DMA(12, u); MXW_DMA(13, u); }
-          if (m == 9) { MXW_DMA(14, u); MXW_DMA(15, u); }
+          if (m >= 4) MXW_DMA(m, u);
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
         if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
-        if (m == 10) dma_scales(sgrp, sreal);
+        if (m == 15) dma_scales(sgrp, sreal);  // after the pair's loads (vmcnt order)
         if (m == 11) {
           sa[nxt] = (int)sm.words[(u + 1) & 1][0][wn][lane];
           sb[nxt] = (int)sm.words[(u + 1) & 1][1][wk][lane];
