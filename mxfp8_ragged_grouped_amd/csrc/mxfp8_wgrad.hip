@@ -24,12 +24,12 @@
 //     ping-pong (blog section 4).  The 16-byte chunk c of row r sits at
 //     position c ^ (r & 7): the MFMA fragment reads are free of LDS bank
 //     conflicts (8 lanes of a read hit 8 distinct 16-byte bank groups).
-//   * software pipeline: the fragments and scale words of K-step j + 1 are
-//     read from LDS into a second register set while K-step j's 16 MFMAs run,
-//     one read per MFMA, so the MFMAs never wait on LDS and the LDS stays
-//     evenly loaded.  One barrier per K-step; at odd steps it also certifies
-//     that the next pair has landed and that the current pair has been read,
-//     and that pair's stage is refilled with the pair after next, its loads
+//   * software pipeline: the fragments of K-step j + 1 are read from LDS into
+//     a second register set while K-step j's 16 MFMAs run, one read per MFMA,
+//     so the MFMAs never wait on LDS and the LDS stays evenly loaded.  One
+//     barrier per pair of K-steps, at the odd step: it certifies that the
+//     next pair has landed and that the current pair has been read, and that
+//     pair's stage is then refilled with the pair after next, its loads
 //     spread over the step's MFMAs.
 //   * ragged head/tail: a 32-token sub-block is live iff it lies inside
 //     [start, end) (group boundaries are 32-aligned, blog section 1).  Dead
@@ -37,14 +37,15 @@
 //     buffer range, so the hardware writes zeros (padding that holds NaN never
 //     reaches the MFMA, blog section 5.3), and both operands' scales are set
 //     to 0x00.
-//   * scales: the raw E8M0 bytes arrive by LDS-direct loads and each thread
-//     re-lays its row's 2 bytes of a K-step into MFMA-ready words (blog
-//     sections 5.2 and 5.6): byte i of a word is 32-row block i of the wave's
-//     rows, picked by op_sel, so the MFMA loop reads one dword per operand per
-//     step and unpacks nothing.  When every row of the scale planes starts
-//     16-byte aligned (M a multiple of 512) one 16-byte load per row brings 8
-//     K-steps of scales (GROUP = true); otherwise the two aligned dwords around
-//     a row's 4 bytes of 2 K-steps are loaded.  A scale load per row per step
+//   * scales: the raw E8M0 bytes arrive by LDS-direct loads; once per pair of
+//     K-steps each lane reads, for each of its 32-row blocks, the dword of
+//     its row that holds the pair's 4 bytes (2 K-steps x 2 sub-blocks), shifts
+//     its own sub-block's bytes to bytes 0 and 2, clears dead sub-blocks, and
+//     the MFMA picks byte 0 or 2 with op_sel (blog sections 5.2 and 5.6): no
+//     unpacking and no relayout through LDS.  When every row of the scale
+//     planes starts 16-byte aligned (M a multiple of 512) one 16-byte load per
+//     row brings 8 K-steps of scales (GROUP = true); otherwise the two aligned
+//     dwords around a row's 4 bytes of 2 K-steps are loaded.  A scale load per row per step
 //     would double the number of L1 -> L2 requests of a step (every lane hits
 //     a different row), which measurably slows the data stream.
 //   * contraction: v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
@@ -58,7 +59,7 @@
 // MFMA lane layout used here (32x32x64, FP8 operands, checked on gfx950): lane
 // l holds row l % 32 and tokens {16(l/32) + p : p < 16} in bytes 0..15 and
 // {32 + 16(l/32) + p} in bytes 16..31; the scale word of lane l carries the
-// E8M0 of row l % 32 and 32-token block l / 32 (byte chosen by op_sel); the
+// E8M0 of row l % 32 and 32-token block l / 32 (byte picked by op_sel); the
 // result's lane l register r holds row 8(r/4) + 4(l/32) + r%4 of column l % 32.
 //
 // Every global read in the K-loop is an LDS-direct load issued through asm,
@@ -105,9 +106,6 @@ struct Smem {
   // destination of the out-of-range scale-slot loads on steps that have no
   // scale group to fetch (written with zeros, never read)
   uint32_t dummy[256];
-  // MFMA-ready scale words [buf][op][half][lane]: byte i is 32-row block i of
-  // that half's 128 rows, for sub-block lane / 32 and row lane % 32
-  uint32_t words[2][2][2][64];
   int start[MXW_MAX_EXPERTS];
   int len[MXW_MAX_EXPERTS];
   int order[MXW_MAX_EXPERTS];
@@ -385,38 +383,6 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
     }
   };
 
-  // Relayout of thread t's scale row (row t of A and of B) for step s into
-  // words buffer wb: sub-block b -> lane (t % 32) + 32 b of half t / 128,
-  // byte (t % 128) / 32.  Two steps: read the raw dwords (issue), then mask
-  // and write the bytes.
-  const int rh = tid >> 7, ri = (tid >> 5) & 3, rr = tid & 31;
-  const int wbyte = ((rh * 64 + rr) * 4) + ri;  // + 128 per sub-block, + 512 per op, + 1024 per buffer
-  const uint32_t tshift = (((uint32_t)tid * sbytes) & 3u) * 8u;
-  auto raw_read = [&](int s, uint32_t& a, uint32_t& b) {
-    if (GROUP) {
-      const int slot = (s >> 3) & 1, dw = (s & 7) >> 1;
-      a = sm.raw[((slot * 2 + 0) * kTile + tid) * 4 + dw];
-      b = sm.raw[((slot * 2 + 1) * kTile + tid) * 4 + dw];
-    } else {
-      const int slot = (s >> 1) & 3;
-      a = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 0) * 2 + 1) * kTile + tid],
-                                    sm.raw[((slot * 2 + 0) * 2 + 0) * kTile + tid], tshift);
-      b = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 1) * 2 + 1) * kTile + tid],
-                                    sm.raw[((slot * 2 + 1) * 2 + 0) * kTile + tid], tshift);
-    }
-  };
-  auto raw_write_m = [&](int s, int wb, uint32_t a, uint32_t b, uint32_t live) {
-    const int sh = (s & 1) * 16;
-    uint8_t* base = (uint8_t*)&sm.words[wb][0][0][0] + wbyte;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const bool ok = (live >> sb) & 1u;
-      base[sb * 128] = ok ? (uint8_t)(a >> (sh + 8 * sb)) : (uint8_t)0;
-      base[512 + sb * 128] = ok ? (uint8_t)(b >> (sh + 8 * sb)) : (uint8_t)0;
-    }
-  };
-  auto raw_write = [&](int s, int wb, uint32_t a, uint32_t b) { raw_write_m(s, wb, a, b, live_mask(s, start, end)); };
-
   // ---- MFMA geometry -----------------------------------------------------------
   // wave (wn, wk) owns A rows 128 wn .. +128 and B rows 128 wk .. +128: 4 x 4
   // blocks of 32 x 32 outputs.  Fragment of a 32-row block for the first
@@ -472,17 +438,42 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   }
   wait_vm<kDataDma + kSlot>();  // scales and pair s0/2 landed (this wave)
   __syncthreads();
-  {
-    uint32_t a0, b0, a1, b1;
-    raw_read(s0, a0, b0);
-    raw_read(s0 + 1, a1, b1);
-    raw_write(s0, 0, a0, b0);
-    raw_write(s0 + 1, 1, a1, b1);
-  }
-  __syncthreads();
+
+  // Scale registers.  In lane l the MFMA takes the E8M0 byte of row l % 32 and
+  // 32-token sub-block l / 32 of each 32-row block, from the byte op_sel
+  // picks.  A row's raw dword for a pair of K-steps holds sub-blocks 0, 1 of
+  // the first K-step, then of the second; shifted right by 8 (l / 32) bits,
+  // its byte 0 is this lane's byte of the first K-step and byte 2 that of the
+  // second.  So a lane keeps one dword per 32-row block and operand for a
+  // whole pair, with the bytes of dead sub-blocks cleared.
+  const int msb = lane >> 5;
+  const uint32_t mshift = 8u * (uint32_t)msb;
+  auto load_sregs = [&](int x, uint32_t* ra4, uint32_t* rb4) {  // x: first K-step of the pair
+    const uint32_t pm = (((live_mask_q(x, qs, qn) >> msb) & 1u) ? 0xFFu : 0u) |
+                        (((live_mask_q(x + 1, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
+      uint32_t a, b;
+      if (GROUP) {
+        const int slot = (x >> 3) & 1, dw = (x & 7) >> 1;
+        a = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
+        b = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
+      } else {
+        const int slot = (x >> 1) & 3;
+        a = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 0) * 2 + 1) * kTile + RA],
+                                      sm.raw[((slot * 2 + 0) * 2 + 0) * kTile + RA], (((uint32_t)RA * sbytes) & 3u) * 8u);
+        b = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 1) * 2 + 1) * kTile + RB],
+                                      sm.raw[((slot * 2 + 1) * 2 + 0) * kTile + RB], (((uint32_t)RB * sbytes) & 3u) * 8u);
+      }
+      ra4[i] = (a >> mshift) & pm;
+      rb4[i] = (b >> mshift) & pm;
+    }
+  };
 
   v8i fa[2][4], fb[2][4];
-  int sa[2], sb[2];
+  uint32_t sra[2][4], srb[2][4];  // [pair parity][32-row block]
+  load_sregs(s0, sra[0], srb[0]);
   {
     const uint8_t* ta = sm.data[0][0] + (wn * 128) * kRowBytes;
     const uint8_t* tb = sm.data[0][1] + (wk * 128) * kRowBytes;
@@ -490,13 +481,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
     for (int t = 0; t < 4; ++t) fb[0][t] = frag(tb + t * 32 * kRowBytes, frag_lo0, frag_hi0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) fa[0][t] = frag(ta + t * 32 * kRowBytes, frag_lo0, frag_hi0);
-    sa[0] = (int)sm.words[0][0][wn][lane];
-    sb[0] = (int)sm.words[0][1][wk][lane];
   }
 
   // per-step scalars of the first step; later steps compute theirs one step ahead
   uint32_t livep = live_mask_pair((s0 >> 1) + 2, qs, qn);  // pair issued at the next odd step
-  uint32_t live2 = live_mask_q(s0 + 2, qs, qn);
   int sgrp = s0 / kGroupSteps + kAhead;
   bool sreal = false;  // s0 never issues a real scale load
 
@@ -514,21 +502,21 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
       wait_lgkm_all();  // this step's fragments and words are in registers
       __builtin_amdgcn_sched_barrier(0);
-      uint32_t ra = 0, rb = 0;
       uint32_t va[8];
       uint32_t soffp = 0;
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int i = m >> 2, t = m & 3;  // B block i, A block t
-        acc[i][t] = mfma_e4m3_sel(i, t, fb[cur][i], fa[cur][t], acc[i][t], sb[cur], sa[cur]);
+        acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
+                                  (int)sra[u >> 1][t]);
         if (m == 0 && (u & 1)) {
           const bool lok = (livep >> sbl) & 1u;
 #pragma unroll
           for (int q = 0; q < 8; ++q) va[q] = lok ? vrow[q] : kOob;
         }
-        if (m == 1) {
+        if (m == 1 && (u & 1)) {
           __builtin_amdgcn_sched_barrier(0);
-          if (u & 1) wait_vm<2 * kSlot>(); else wait_vm<kDataDma + 2 * kSlot>();
+          wait_vm<2 * kSlot>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -536,7 +524,6 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
           int sp = s;
           asm volatile("" : "+s"(sp));
           soffp = (uint32_t)(((sp >> 1) + 2) * kPair);
-          raw_read(sp + 2, ra, rb);
         }
         if (u & 1) {
           // one load per MFMA (two at the first two slots): the 4 waves then
@@ -550,16 +537,13 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
         if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
         if (m == 15) dma_scales(sgrp, sreal);  // after the pair's loads (vmcnt order)
-        if (m == 11) {
-          sa[nxt] = (int)sm.words[(u + 1) & 1][0][wn][lane];
-          sb[nxt] = (int)sm.words[(u + 1) & 1][1][wk][lane];
-        }
-        if (m == 12) raw_write_m(s + 2, u & 1, ra, rb, live2);
         if (m == 13) {
           int sp = s;
           asm volatile("" : "+s"(sp));
+          // odd step: the next pair's scale registers (its raw bytes landed
+          // with the pair, certified by this step's barrier)
+          if (u & 1) load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
           if (!(u & 1)) livep = live_mask_pair(((sp + 1) >> 1) + 2, qs, qn);
-          live2 = live_mask_q(sp + 3, qs, qn);
           sreal = ((sp + 1) % kGroupSteps) == 0;
           sgrp = (sp + 1) / kGroupSteps + kAhead;
         }
