@@ -42,7 +42,8 @@ extern "C" {
 #define MXW_ERR_DIM (-2)    /* E, M, N or K outside the supported range */
 #define MXW_ERR_ALIGN (-3)  /* A, B or out not 16-byte aligned */
 #define MXW_ERR_DEVICE (-4) /* current device is not gfx950, or no device */
-#define MXW_ERR_LAUNCH (-5) /* the kernel launch failed (hipGetLastError) */
+#define MXW_ERR_LAUNCH (-5) /* the kernel launch failed (hipGetLastError), or the
+                               column-mode workspace could not be allocated */
 
 /* Supported ranges (checked on the host, no device access). */
 #define MXW_MAX_EXPERTS 256
@@ -52,7 +53,7 @@ extern "C" {
  * mxfp8_wgrad_grouped -- the weight-gradient grouped GEMM above.
  *
  * Arguments (every pointer is caller-owned DEVICE memory on the current HIP
- * device; the library allocates nothing and keeps no state between calls):
+ * device):
  *   A     uint8  [N, M]    E4M3 codes of dY^T, row stride M bytes.
  *   sA    uint8  [N, M/32] E8M0 scales of A, row stride M/32 bytes.
  *   B     uint8  [K, M]    E4M3 codes of X^T, row stride M bytes.
@@ -78,10 +79,22 @@ extern "C" {
  *
  * Effects: enqueues one kernel on `stream` and returns without synchronising.
  * `out` is completely overwritten; an expert with no tokens gets exact +0.0.
- * Inputs are never written.  The result is bitwise reproducible run to run
- * (each output element has exactly one owner and a fixed summation order; no
- * atomics).  The compiled kernel serves every shape: E, M, N, K and offs are
- * runtime arguments.
+ * Inputs are never written.  The result is bitwise reproducible run to run:
+ * for given (E, M, N, K, offs) every output element is summed in a fixed
+ * order, whatever the timing (no atomics on data).
+ *
+ * Scheduling and state: with few output tiles per compute unit and long
+ * experts (mxw_columns() > 0) the launch runs in column mode, one workgroup
+ * per CU, and a region of tiles cut between two columns is summed through
+ * FP32 partial tiles in a device workspace.  The library allocates that
+ * workspace (64 MiB on a 256-CU device, with its flags) with hipMalloc on the
+ * first column-mode call on a device, synchronising the device once, and
+ * keeps it until the process ends.  Column-mode launches on one device must
+ * not overlap in time (different streams would race on the workspace); the
+ * column-mode kernel also expects to have the device's compute units to
+ * itself while it runs (its columns exchange partials, waiting with a
+ * bounded spin: a partial that never arrives turns its tile into NaN rather
+ * than hanging).  Otherwise the call allocates nothing and keeps no state.
  *
  * Returns MXW_OK or a negative MXW_ERR_* code.
  */
@@ -89,12 +102,23 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
                         const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream);
 
 /*
- * mxw_grid_size -- the number of workgroups mxfp8_wgrad_grouped launches for
- * (E, N, K): one per (expert, 256 x 256 output tile), i.e.
- * E * ceil(N/256) * ceil(K/256) (blog section 4: one block per expert per
- * output tile, which owns its tile for life).  Returns 0 for invalid sizes.
+ * mxw_grid_size -- the number of (expert, 256 x 256 output tile) work items
+ * of (E, N, K), E * ceil(N/256) * ceil(K/256) (blog section 4: one block per
+ * expert per output tile).  Outside column mode this is also the number of
+ * workgroups launched.  Returns 0 for invalid sizes.
  */
 int64_t mxw_grid_size(int E, int N, int K);
+
+/*
+ * mxw_columns -- the number of columns mxfp8_wgrad_grouped uses for
+ * (E, M, N, K) on the current device: 0 when it launches one workgroup per
+ * work item, otherwise the column count of column mode (16 workgroups per
+ * column, one per compute unit).  Column mode is chosen when the work items
+ * fill the device at most 4 times over and M >= 8192 * E.  Reads device
+ * properties only; returns MXW_ERR_DIM or MXW_ERR_DEVICE on invalid input or
+ * no gfx950 device.
+ */
+int mxw_columns(int E, int M, int N, int K);
 
 /* mxw_strerror -- a static, human-readable message for a return code. */
 const char* mxw_strerror(int code);

@@ -21,7 +21,8 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "strerror", "version", "library_path", "MxwError"]
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "columns", "strerror", "version", "library_path",
+           "MxwError"]
 
 _lib = None
 
@@ -51,6 +52,8 @@ def _load():
     lib.mxw_strerror.argtypes = [I]
     lib.mxw_version.restype = I
     lib.mxw_version.argtypes = []
+    lib.mxw_columns.restype = I
+    lib.mxw_columns.argtypes = [I, I, I, I]
     _lib = lib
     return lib
 
@@ -65,6 +68,15 @@ def version():
 
 def grid_size(E, N, K):
     return int(_load().mxw_grid_size(int(E), int(N), int(K)))
+
+
+def columns(E, M, N, K):
+    """Columns of a column-mode launch for this shape on the current device
+    (0: one workgroup per tile).  Raises MxwError on a status code."""
+    rc = _load().mxw_columns(int(E), int(M), int(N), int(K))
+    if rc < 0:
+        raise MxwError("mxw_columns failed: %s" % strerror(rc))
+    return rc
 
 
 def mxfp8_wgrad_grouped(A, sA, B, sB, offs, E, M, N, K, out, stream=0):

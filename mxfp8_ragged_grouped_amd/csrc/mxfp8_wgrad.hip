@@ -7,16 +7,26 @@
 // section 1).  A = dY^T [N, M], B = X^T [K, M], token axis contiguous.
 //
 // Structure of one launch:
-//   * grid = one 256-thread workgroup (4 wave64) per (expert, 256 x 256 output
-//     tile); a workgroup owns its tile for life, walks its expert's tokens in
-//     64-token K-steps, keeps the tile's 65,536 FP32 sums in accumulator
-//     registers and stores once (blog section 4).  No atomics:
-//     bit-reproducible.
-//   * tile scheduler: every workgroup reads offs itself, ranks the experts by
-//     window length with one lane per expert (longest first, ties to the lower
-//     index; blog section 5.4), and numbers tiles so that the workgroups the
-//     dispatcher deals to one XCD (block index mod 8, blog section 3) cover a
-//     compact rectangle of the same expert's tiles (blog section 5.5).
+//   * work item = (expert, 256 x 256 output tile), computed by one 256-thread
+//     workgroup (4 wave64) that walks the expert's tokens in 64-token K-steps,
+//     keeps the tile's 65,536 FP32 sums in accumulator registers and stores
+//     once (blog section 4).  No atomics on data: bit-reproducible.
+//   * tile scheduler, two modes:
+//     - one workgroup per work item (many tiles): every workgroup reads offs
+//       itself, ranks the experts by window length with one lane per expert
+//       (longest first, ties to the lower index; blog section 5.4), and
+//       numbers tiles so that the workgroups the dispatcher deals to one XCD
+//       (block index mod 8, blog section 3) cover a compact rectangle of the
+//       same expert's tiles (blog section 5.5);
+//     - column mode (few tiles per CU, long experts): one workgroup per CU;
+//       16 workgroups on one XCD form a column that works through regions of
+//       up to 16 tiles (4 x 4) of one expert, all members on the same tokens
+//       at the same time so that they share the region's A and B stripes in
+//       the XCD's L2.  The sequence of (expert, region) pieces, weighted by
+//       K-steps, is cut into equal spans, one per column (whole tiles pack
+//       unevenly: 1.3x the ideal span at 1.5 tiles per CU).  A region cut
+//       between columns is summed in a fixed order: the later pieces store
+//       FP32 partial tiles and raise a flag, the first piece adds them.
 //   * staging: an LDS stage holds a pair of K-steps (256 rows x 128 tokens of
 //     A and of B, 64 KiB), filled by 16-byte LDS-direct buffer loads, 8 rows x
 //     128 bytes per instruction, so every memory request is one whole cache
@@ -45,16 +55,19 @@
 //     unpacking and no relayout through LDS.  When every row of the scale
 //     planes starts 16-byte aligned (M a multiple of 512) one 16-byte load per
 //     row brings 8 K-steps of scales (GROUP = true); otherwise the two aligned
-//     dwords around a row's 4 bytes of 2 K-steps are loaded.  A scale load per row per step
-//     would double the number of L1 -> L2 requests of a step (every lane hits
-//     a different row), which measurably slows the data stream.
+//     dwords around a row's 4 bytes of 2 K-steps are loaded.  A scale load
+//     per row per step would double the number of L1 -> L2 requests of a
+//     step (every lane hits a different row), which measurably slows the
+//     data stream.
 //   * contraction: v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
 //     per-32 E8M0 scales, FP32 accumulation (blog section 3).  Operand roles
 //     are swapped (B feeds the instruction's first operand) so that each lane
 //     ends with 4 consecutive k of one output row (ROCm/aiter PR 6605,
 //     section 1).
-//   * epilogue: FP32 -> bf16 round-to-nearest-even in registers, 8-byte
-//     stores (blog section 5.5).
+//   * epilogue: FP32 -> bf16 round-to-nearest-even in registers (blog
+//     section 5.5), staged through LDS so that every global store writes
+//     whole 128-byte lines (8-byte stores straight from the MFMA layout touch
+//     32 lines per instruction and took ~19k clocks per tile).
 //
 // MFMA lane layout used here (32x32x64, FP8 operands, checked on gfx950): lane
 // l holds row l % 32 and tokens {16(l/32) + p : p < 16} in bytes 0..15 and
@@ -69,6 +82,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mxfp8_wgrad.h"
 
 namespace {
@@ -78,6 +93,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 256;                   // output tile edge, N and K
 constexpr int kStep = 64;                    // tokens per K-step (two 32-token sub-blocks)
@@ -92,6 +108,19 @@ constexpr int kDataDma = 16;
 // raw buffer descriptor word 3 for gfx9-family: 32-bit data format, no swizzle,
 // range checking on the byte offset
 constexpr int kRsrcWord3 = 0x00020000;
+// cache-policy operand of the buffer builtins: sc1 = device-scope coherence
+constexpr int kSc1 = 16;
+
+// Column mode (see Params): workgroups per column = tiles per region.
+constexpr int kMem = 16;
+// fixed cost of a region piece (prologue and epilogue), in K-steps, charged
+// when the work sequence is cut into columns
+constexpr int kColHov = 3;
+// column mode is used when the (expert, tile) work items fill the chip at
+// most this many times over and the mean expert has at least kColTokens
+// tokens; below that the per-piece costs outweigh the better packing
+constexpr int kColWaves = 4;
+constexpr int kColTokens = 8192;
 
 // LDS layout (150 KiB of the 160 KiB per CU).
 struct Smem {
@@ -109,6 +138,13 @@ struct Smem {
   int start[MXW_MAX_EXPERTS];
   int len[MXW_MAX_EXPERTS];
   int order[MXW_MAX_EXPERTS];
+  // column mode: non-empty experts in index order (expert, loop iterations,
+  // exclusive prefix of region costs), the empty ones, and their counts
+  int ne[MXW_MAX_EXPERTS];
+  int nit[MXW_MAX_EXPERTS];
+  int pre[MXW_MAX_EXPERTS];
+  int ee[MXW_MAX_EXPERTS];
+  int cnt[4];
 };
 
 // 16-byte chunk c of staged row r sits at chunk position c ^ swz(r): 8
@@ -233,84 +269,84 @@ struct Params {
   // rectangles of regN x regK tiles, regB of them across the K direction;
   // rectangle x is walked in bands of `band` rows, column by column
   int regN, regK, regB, band;
+  // column mode (ncol > 0): the grid is ncol columns of kMem workgroups,
+  // each column on one XCD (one workgroup per CU); the (expert, region) work
+  // sequence is cut into ncol equal spans, one per column, and a region cut
+  // between columns is summed through FP32 partial tiles
+  float* part;      // [ncol][kMem][kTile * kTile] partial tiles
+  uint32_t* flags;  // [ncol][kMem] partial-ready flags, 0 between launches
+  int ncol;
+  int regions;  // regions of up to kMem tiles per expert
+  int hov;      // per-region cost, in K-steps, added to the split's weights
 };
 
-// GROUP: scale rows are 16-byte aligned (M % 512 == 0) and scales are loaded
-// 8 K-steps at a time; otherwise 2 K-steps at a time.
-template <bool GROUP>
-__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+// loop iterations (4 K-steps each) of an expert's window [start, start + len)
+__device__ __forceinline__ int window_iters(int start, int len) {
+  const int s0 = (start / kPair) * 2;
+  const int s_end = (start + len + kStep - 1) / kStep;
+  return ((s_end - s0 + 3) & ~3) >> 2;
+}
 
-  const int tid = threadIdx.x;
+// Region r of an expert's tile grid and its member j (0 .. kMem-1): bands of
+// 4 tile rows hold 4 x (kMem / 4) regions; a last band of h < 4 rows holds
+// h x (kMem / h) regions (3 x 5 for h = 3).  A region's tiles share 4 (or h)
+// A stripes and kMem / 4 (or kMem / h) B stripes, which its members stream
+// together through their XCD's L2.  Returns false if member j has no tile.
+__device__ __forceinline__ bool region_tile(int tN, int tK, int r, int j, int& tn, int& tk) {
+  constexpr int wf = kMem / 4;
+  const int full = tN >> 2, rpf = (tK + wf - 1) / wf;
+  int band, c, h, w;
+  if (r < full * rpf) {
+    band = r / rpf;
+    c = r - band * rpf;
+    h = 4;
+    w = wf;
+  } else {
+    band = full;
+    c = r - full * rpf;
+    h = tN - 4 * full;
+    w = kMem / h;
+  }
+  if (j >= h * w) return false;
+  tn = 4 * band + j % h;
+  tk = c * w + j / h;
+  return tk < tK;
+}
+
+// exact +0 over tile (tn, tk) of expert g's output
+__device__ __forceinline__ void zero_tile(const Params& p, int g, int tn, int tk) {
+  const int N = p.N, K = p.K;
+  const int n0 = tn * kTile, k0 = tk * kTile;
+  const int rows = min(kTile, N - n0), cols = min(kTile, K - k0);
+  const int chunks = cols / 8;  // 16-byte chunks per row (K % 16 == 0)
+  const v4i z = {0, 0, 0, 0};
+  uint16_t* o = p.out + (size_t)g * N * K;
+  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
+    const int r = i / chunks, c = i - r * chunks;
+    *(v4i*)(o + (size_t)(n0 + r) * K + k0 + 8 * c) = z;
+  }
+}
+
+// One tile piece: tokens [start, end) of expert g into tile (tn, tk).
+struct Piece {
+  int g, tn, tk, start, end;
+  int role;  // 0: whole tile (bf16 out), 1: hands over an FP32 partial, 2: adds partials
+  int col, member, Q, ra_lin, r_it;  // column mode: position and the region (role 2)
+};
+
+template <bool GROUP, bool COL>
+__device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
+  int tid = threadIdx.x;
+  // opaque per piece: nothing derived from the thread index is hoisted out of
+  // the column loop (it would stay live through the K-loop)
+  if (COL) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int E = p.E, M = p.M, N = p.N, K = p.K;
-
-  // ---- windows from offs (clamped to [0, M], monotone) ----------------------
-  if (tid < E) {
-    int e = min(max(p.offs[tid], 0), M);
-    const int s = tid ? min(max(p.offs[tid - 1], 0), M) : 0;
-    if (e < s) e = s;
-    sm.start[tid] = s;
-    sm.len[tid] = e - s;
-  }
-  __syncthreads();
-  // ---- longest-first ranking: lane g counts the experts ahead of it ---------
-  if (tid < E) {
-    const int mine = sm.len[tid];
-    int r = 0;
-    for (int u = 0; u < E; ++u) {
-      const int l = sm.len[u];
-      r += (l > mine) || (l == mine && u < tid);
-    }
-    sm.order[r] = tid;
-  }
-  __syncthreads();
-
-  // ---- block -> (expert rank d, tile) -> (expert g, tile tn, tk) -------------
-  // The dispatcher deals block b to XCD b % 8 and each XCD starts its blocks in
-  // order.  With regions, XCD x owns the same rectangle of every expert's tile
-  // grid and works through the experts longest first, so its co-resident
-  // workgroups cover a compact block of one expert's tiles and share their A
-  // and B stripes in that XCD's L2.
-  const int T = p.tilesN * p.tilesK;
-  const int bid = blockIdx.x;
-  int d, tn, tk;
-  if (p.regN) {
-    const int per = p.regN * p.regK;  // = T / 8
-    const int x = bid & 7, i = bid >> 3;
-    d = i / per;
-    const int v = i - d * per;
-    const int bandsz = p.band * p.regK;
-    const int bnd = v / bandsz, w = v - bnd * bandsz;
-    const int hb = min(p.band, p.regN - bnd * p.band);  // rows in this band
-    const int c = w / hb;
-    tn = (x / p.regB) * p.regN + bnd * p.band + (w - c * hb);
-    tk = (x % p.regB) * p.regK + c;
-  } else {
-    d = bid / T;
-    const int u = bid - d * T;
-    tn = u / p.tilesK;
-    tk = u - tn * p.tilesK;
-  }
-  const int g = __builtin_amdgcn_readfirstlane(sm.order[d]);
-  const int start = __builtin_amdgcn_readfirstlane(sm.start[g]);
-  const int len = __builtin_amdgcn_readfirstlane(sm.len[g]);
-  const int end = start + len;
-  const int n0 = tn * kTile, k0 = tk * kTile;
+  const int M = p.M, N = p.N, K = p.K;
+  const int g = pc.g, start = pc.start, end = pc.end, role = pc.role;
+  const int col = pc.col, member = pc.member, Q = pc.Q, ra_lin = pc.ra_lin, r_it = pc.r_it;
+  const int n0 = pc.tn * kTile, k0 = pc.tk * kTile;
   uint16_t* outg = p.out + (size_t)g * N * K;
-
-  // ---- empty expert: exact +0 over the tile ----------------------------------
-  if (len == 0) {
-    const int rows = min(kTile, N - n0), cols = min(kTile, K - k0);
-    const int chunks = cols / 8;  // 16-byte chunks per row (K % 16 == 0)
-    const v4i z = {0, 0, 0, 0};
-    for (int i = tid; i < rows * chunks; i += kThreads) {
-      const int r = i / chunks, c = i - r * chunks;
-      *(v4i*)(outg + (size_t)(n0 + r) * K + k0 + 8 * c) = z;
-    }
-    return;
-  }
 
   // ---- buffer resources, rebased to this tile's 256-row bands ----------------
   const int rowsA = min(kTile, N - n0), rowsB = min(kTile, K - k0);
@@ -555,29 +591,311 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
 #undef MXW_DMA
   wait_vm_all();  // no LDS-direct load may outlive the workgroup
 
-  // ---- epilogue: bf16 RNE in registers, 8-byte stores -----------------------------
-  // block (i, t): lane l register r holds k = 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
-  // n = 32 t + l % 32 (within the wave's quarter)
-  const int on = n0 + wn * 128 + fr;      // + 32 t
-  const int ok = k0 + wk * 128 + 4 * fq;  // + 32 i + 8 q
+  // ---- column mode: partial tiles --------------------------------------------
+  // Layout: [column][member][wave][block i][block t][quad q][lane], 16 bytes
+  // each (the accumulator registers as they sit).  A piece that continues a
+  // region (role 1) stores its sums there and raises its flag; the region's
+  // first piece (role 2) waits for the flags of the later columns that hold a
+  // piece of the region and adds their partials, in column order.
+  uint64_t pmask = 0;  // role 2: contributing columns
+  if (COL && role == 2) {
+    for (int cc = col + 1; cc < p.ncol; ++cc) {
+      const int lo = min(max((cc * Q - ra_lin + 2) >> 2, 0), r_it);
+      const int hi = min(max(((cc + 1) * Q - ra_lin + 2) >> 2, 0), r_it);
+      if (lo >= r_it) break;
+      if (lo < hi) pmask |= 1ull << cc;
+    }
+    if (tid == 0) {
+      // bounded wait (seconds): a partial that never comes -- only possible
+      // if the grid is not co-resident -- turns the tile into NaN instead of
+      // a hang
+      int lost = 0;
+      for (uint64_t m = pmask; m; m &= m - 1) {
+        uint32_t* fl = &p.flags[__builtin_ctzll(m) * kMem + member];
+        int spins = 0;
+        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 1u && spins < (1 << 21)) {
+          __builtin_amdgcn_s_sleep(4);
+          ++spins;
+        }
+        if (spins >= (1 << 21)) lost = 1;
+        __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      sm.cnt[3] = lost;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(sm.cnt[3])) pmask = 0;
+  }
+  const bool lost = COL && role == 2 && pmask == 0;
+  // Partial tiles move between XCDs, whose L2s are not coherent with each
+  // other: they are written and read with device-scope (sc1) accesses, which
+  // go to memory rather than a local cache, so the handover needs no L2
+  // writeback or invalidation; the writer's flag follows its stores' vmcnt.
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.part, (uint32_t)(p.ncol * kMem) * (uint32_t)(kTile * kTile * 4));
+  const uint32_t pidx = (uint32_t)(wave * 64 * 64 + lane) * 16u;  // + (((i * 4 + t) * 4 + q) * 64) * 16
+  const uint32_t pmine = (uint32_t)(col * kMem + member) * (uint32_t)(kTile * kTile * 4) + pidx;
+  const uint32_t pbase = (uint32_t)member * (uint32_t)(kTile * kTile * 4) + pidx;  // + cc * 8 tiles
+
+  if (COL && role == 2) {
+    // add the partials, one later column at a time, 16 loads in flight
+    for (uint64_t m = pmask; m; m &= m - 1) {
+      const uint32_t src = pbase + (uint32_t)__builtin_ctzll(m) * (uint32_t)(kMem * kTile * kTile * 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        v4f w[16];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = on + 32 * t;
-      if (n < N) {
+        for (int x = 0; x < 16; ++x)
+          w[x] = __builtin_amdgcn_raw_buffer_load_b128(rP, src + (uint32_t)((i * 16 + x) * 64) * 16u, 0, kSc1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int k = ok + 32 * i + 8 * q;
-          if (k < K) {
-            const v16f& v = acc[i][t];
-            uint2 w;
-            w.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
-            w.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
-            *(uint2*)(outg + (size_t)n * K + k) = w;
-          }
+        for (int x = 0; x < 16; ++x) {
+          const int t = x >> 2, q = x & 3;
+          acc[i][t][4 * q] += w[x].x;
+          acc[i][t][4 * q + 1] += w[x].y;
+          acc[i][t][4 * q + 2] += w[x].z;
+          acc[i][t][4 * q + 3] += w[x].w;
         }
       }
+    }
+  }
+
+  // ---- epilogue ------------------------------------------------------------------
+  // block (i, t): lane l register r holds k = 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
+  // n = 32 t + l % 32 (within the wave's 128 x 128 quarter).
+  if (COL && role == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f v = {acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rP, pmine + (uint32_t)(((i * 4 + t) * 4 + q) * 64) * 16u, 0, kSc1);
+        }
+  } else {
+    // bf16 RNE in registers, then through this wave's 32 KiB of the (now idle)
+    // stage area so that every global store writes whole 128-byte lines: the
+    // quarter is laid out as 128 rows of 256 bytes, 16-byte chunk c of row n
+    // at position c ^ (n % 16) (the 8-byte writes then meet at most 2-way
+    // bank conflicts and the 16-byte reads none).
+    __syncthreads();  // every wave is done with the stages
+    uint8_t* ep = &sm.data[0][0][0] + wave * 32768;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v4f v = {acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
+          if (lost) v = (v4f){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+          const int nl = 32 * t + fr, c = 4 * i + q;
+          uint2 w;
+          w.x = pack_bf16x2(v.x, v.y);
+          w.y = pack_bf16x2(v.z, v.w);
+          *(uint2*)(ep + nl * 256 + ((c ^ (nl & 15)) << 4) + fq * 8) = w;
+        }
+    const int rsub = lane >> 4, cl = lane & 15;
+    const int kk = k0 + wk * 128 + cl * 8;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      const int nl = 4 * x + rsub;
+      const v4i d = *(const v4i*)(ep + nl * 256 + ((cl ^ (nl & 15)) << 4));
+      const int n = n0 + wn * 128 + nl;
+      if (n < N && kk < K) *(v4i*)(outg + (size_t)n * K + kk) = d;
+    }
+  }
+  if (COL && role == 1) {
+    wait_vm_all();  // this wave's partial stores have reached memory
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&p.flags[col * kMem + member], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// GROUP: scale rows are 16-byte aligned (M % 512 == 0) and scales are loaded
+// 8 K-steps at a time; otherwise 2 K-steps at a time.  COL: column mode (see
+// Params); otherwise one workgroup per (expert, tile).
+template <bool GROUP, bool COL>
+__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = p.E, M = p.M;
+  const int T = p.tilesN * p.tilesK;
+  const int bid = blockIdx.x;
+
+  // ---- windows from offs (clamped to [0, M], monotone) ----------------------
+  if (tid < E) {
+    int e = min(max(p.offs[tid], 0), M);
+    const int s = tid ? min(max(p.offs[tid - 1], 0), M) : 0;
+    if (e < s) e = s;
+    sm.start[tid] = s;
+    sm.len[tid] = e - s;
+  }
+  __syncthreads();
+  if (!COL) {
+    // ---- longest-first ranking: lane g counts the experts ahead of it -------
+    if (tid < E) {
+      const int mine = sm.len[tid];
+      int r = 0;
+      for (int u = 0; u < E; ++u) {
+        const int l = sm.len[u];
+        r += (l > mine) || (l == mine && u < tid);
+      }
+      sm.order[r] = tid;
+    }
+  } else if (wave == 0) {
+    // ---- compact lists of non-empty and empty experts (wave scans) ----------
+    int cn = 0, ce = 0, acc_cost = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      const int it = (e < E && sm.len[e] > 0) ? window_iters(sm.start[e], sm.len[e]) : 0;
+      const int cost = it ? 4 * it + p.hov : 0;
+      int sc = cost, sn = it > 0, sz = (e < E && it == 0);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int x = __shfl_up(sc, d), y = __shfl_up(sn, d), z = __shfl_up(sz, d);
+        if (lane >= d) {
+          sc += x;
+          sn += y;
+          sz += z;
+        }
+      }
+      if (it) {
+        sm.ne[cn + sn - 1] = e;
+        sm.nit[cn + sn - 1] = it;
+        sm.pre[cn + sn - 1] = acc_cost + sc - cost;
+      } else if (e < E) {
+        sm.ee[ce + sz - 1] = e;
+      }
+      cn += __shfl(sn, 63);
+      ce += __shfl(sz, 63);
+      acc_cost += __shfl(sc, 63);
+    }
+    if (lane == 0) {
+      sm.cnt[0] = cn;
+      sm.cnt[1] = ce;
+      sm.cnt[2] = acc_cost;
+    }
+  }
+  __syncthreads();
+
+  // ---- column mode: walk state -----------------------------------------------
+  // Block b sits on XCD b % 8 (the dispatcher's round robin); with i = b / 8
+  // its column is (i / kMem, b % 8) -- kMem members i % kMem on one XCD --
+  // numbered from the top so that later columns are dispatched first: a
+  // column's last region may wait for partials of later columns' first
+  // regions, never the reverse.
+  const int col = COL ? p.ncol - 1 - (((bid >> 3) / kMem) * 8 + (bid & 7)) : 0;
+  const int member = (bid >> 3) % kMem;
+  int nne = 0, kx = 0, rx = 0, Q = 0, x0 = 0, x1 = 0;
+  const int Rg = p.regions;
+  if (COL) {
+    // tiles of experts with no tokens: exact +0, dealt round robin
+    const int nemp = __builtin_amdgcn_readfirstlane(sm.cnt[1]);
+    for (int z = bid; z < nemp * T; z += gridDim.x) {
+      const int ez = __builtin_amdgcn_readfirstlane(sm.ee[z / T]);
+      const int tz = z - (z / T) * T;
+      const int tnz = tz / p.tilesK;
+      zero_tile(p, ez, tnz, tz - tnz * p.tilesK);
+    }
+    nne = __builtin_amdgcn_readfirstlane(sm.cnt[0]);
+    const int W = Rg * __builtin_amdgcn_readfirstlane(sm.cnt[2]);
+    Q = (W + p.ncol - 1) / p.ncol;
+    x0 = col * Q;
+    x1 = x0 + Q;
+    // first non-empty expert whose regions reach past x0
+    kx = nne;
+    for (int base = 0; base < nne; base += 64) {
+      const int k = base + lane;
+      const bool hit = k < nne && Rg * (sm.pre[k] + 4 * sm.nit[k] + p.hov) > x0;
+      const uint64_t bal = __ballot(hit);
+      if (bal) {
+        kx = base + (int)__builtin_ctzll(bal);
+        break;
+      }
+    }
+    kx = __builtin_amdgcn_readfirstlane(kx);
+    if (kx < nne) {
+      const int pk = __builtin_amdgcn_readfirstlane(sm.pre[kx]);
+      const int ck = 4 * __builtin_amdgcn_readfirstlane(sm.nit[kx]) + p.hov;
+      rx = x0 > Rg * pk ? (x0 - Rg * pk) / ck : 0;
+    }
+  }
+
+  if constexpr (!COL) {
+    // ---- block -> (expert rank d, tile) -> (expert g, tile tn, tk) -----------
+    // The dispatcher deals block b to XCD b % 8 and each XCD starts its blocks
+    // in order.  With regions, XCD x owns the same rectangle of every expert's
+    // tile grid and works through the experts longest first, so its
+    // co-resident workgroups cover a compact block of one expert's tiles and
+    // share their A and B stripes in that XCD's L2.
+    Piece pc = {};
+    int d;
+    if (p.regN) {
+      const int per = p.regN * p.regK;  // = T / 8
+      const int x = bid & 7, i = bid >> 3;
+      d = i / per;
+      const int v = i - d * per;
+      const int bandsz = p.band * p.regK;
+      const int bnd = v / bandsz, w = v - bnd * bandsz;
+      const int hb = min(p.band, p.regN - bnd * p.band);  // rows in this band
+      const int c = w / hb;
+      pc.tn = (x / p.regB) * p.regN + bnd * p.band + (w - c * hb);
+      pc.tk = (x % p.regB) * p.regK + c;
+    } else {
+      d = bid / T;
+      const int u = bid - d * T;
+      pc.tn = u / p.tilesK;
+      pc.tk = u - pc.tn * p.tilesK;
+    }
+    pc.g = __builtin_amdgcn_readfirstlane(sm.order[d]);
+    pc.start = __builtin_amdgcn_readfirstlane(sm.start[pc.g]);
+    const int len = __builtin_amdgcn_readfirstlane(sm.len[pc.g]);
+    pc.end = pc.start + len;
+    // ---- empty expert: exact +0 over the tile ----------------------------------
+    if (len == 0) {
+      zero_tile(p, pc.g, pc.tn, pc.tk);
+      return;
+    }
+    run_piece<GROUP, false>(p, sm, pc);
+  } else {
+    // ---- column mode: the pieces of this column, in sequence order -------------
+    for (;;) {
+      if (kx >= nne) break;
+      const int it = __builtin_amdgcn_readfirstlane(sm.nit[kx]);
+      const int cost = 4 * it + p.hov;
+      const int a = Rg * __builtin_amdgcn_readfirstlane(sm.pre[kx]) + rx * cost;
+      if (a >= x1) break;
+      // iteration boundary of a sequence position, clamped to [0, it]
+      const int lo = min(max((x0 - a + 2) >> 2, 0), it);
+      const int hi = min(max((x1 - a + 2) >> 2, 0), it);
+      Piece pc;
+      pc.g = __builtin_amdgcn_readfirstlane(sm.ne[kx]);
+      const int rcur = rx;
+      if (++rx == Rg) {
+        rx = 0;
+        ++kx;
+      }
+      if (lo >= hi) continue;
+      if (!region_tile(p.tilesN, p.tilesK, rcur, member, pc.tn, pc.tk)) continue;
+      const int es = __builtin_amdgcn_readfirstlane(sm.start[pc.g]);
+      const int ee = es + __builtin_amdgcn_readfirstlane(sm.len[pc.g]);
+      const int es0 = (es / kPair) * 2;
+      pc.start = max(es, (es0 + 4 * lo) * kStep);
+      pc.end = min(ee, (es0 + 4 * hi) * kStep);
+      pc.role = lo > 0 ? 1 : (hi < it ? 2 : 0);
+      pc.col = col;
+      pc.member = member;
+      pc.Q = Q;
+      pc.ra_lin = a;
+      pc.r_it = it;
+      // the previous piece's stores have completed (vmcnt starts at 0) and its
+      // LDS reads are done in every wave before new loads land
+      wait_vm_all();
+      __syncthreads();
+      run_piece<GROUP, true>(p, sm, pc);
     }
   }
 }
@@ -585,8 +903,47 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
 struct DeviceInfo {
   int checked;
   int ok;
+  int cus;          // compute units
+  float* part;      // column-mode workspace (allocated on first use, kept)
+  uint32_t* flags;
+  int ncol;         // columns the workspace holds
 };
 DeviceInfo g_dev[64];
+std::mutex g_ws_mutex;
+
+// Column-mode workspace of the current device: ncol x 8 FP32 partial tiles
+// and their flags (zeroed once; every reader resets the flag it consumed).
+int get_workspace(int dev, int ncol, float** part, uint32_t** flags) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.part || d.ncol < ncol) {
+    if (d.part) {
+      if (hipDeviceSynchronize() != hipSuccess) return MXW_ERR_LAUNCH;
+      (void)hipFree(d.part);
+      (void)hipFree(d.flags);
+      d.part = nullptr;
+      d.flags = nullptr;
+    }
+    void* pp = nullptr;
+    void* fp = nullptr;
+    if (hipMalloc(&pp, (size_t)ncol * kMem * kTile * kTile * sizeof(float)) != hipSuccess) return MXW_ERR_LAUNCH;
+    if (hipMalloc(&fp, (size_t)ncol * kMem * sizeof(uint32_t)) != hipSuccess) {
+      (void)hipFree(pp);
+      return MXW_ERR_LAUNCH;
+    }
+    if (hipMemset(fp, 0, (size_t)ncol * kMem * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(pp);
+      (void)hipFree(fp);
+      return MXW_ERR_LAUNCH;
+    }
+    d.part = (float*)pp;
+    d.flags = (uint32_t*)fp;
+    d.ncol = ncol;
+  }
+  *part = d.part;
+  *flags = d.flags;
+  return MXW_OK;
+}
 
 int check_device() {
   int dev = -1;
@@ -597,14 +954,45 @@ int check_device() {
   const int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < 64) {
     g_dev[dev].ok = ok;
+    g_dev[dev].cus = prop.multiProcessorCount;
     g_dev[dev].checked = 1;
   }
   return ok ? MXW_OK : MXW_ERR_DEVICE;
 }
 
+// Columns of a column-mode launch (0: one workgroup per work item) and the
+// regions per expert.  Column mode when the work items fill the chip only a
+// few times over (whole tiles then pack unevenly onto the compute units) and
+// experts are long enough to amortise the per-piece costs; it needs whole
+// 8-column groups (one column per XCD each), a flag mask of at most 64
+// columns and a work sequence that fits in int.
+int plan_columns(int E, int M, int N, int K, int cus, int* regions) {
+  const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
+  const int full = tN / 4, h = tN - 4 * full;
+  const int w = h ? kMem / h : 1, wf = kMem / 4;
+  const int R = full * ((tK + wf - 1) / wf) + (h ? (tK + w - 1) / w : 0);
+  *regions = R;
+  const int ncol = (cus / kMem) & ~7;
+  const int64_t items = (int64_t)E * tN * tK;
+  const int64_t wmax = (int64_t)R * (4 * ((int64_t)M / 256 + 2 * E) + (int64_t)E * kColHov);
+  if (ncol >= 8 && ncol <= 64 && items <= (int64_t)kColWaves * cus && (int64_t)M >= (int64_t)kColTokens * E &&
+      wmax < (1LL << 30))
+    return ncol;
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mxw_columns(int E, int M, int N, int K) {
+  if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || N < 16 || K < 16) return MXW_ERR_DIM;
+  const int rc = check_device();
+  if (rc) return rc;
+  int dev = 0, regions = 0;
+  (void)hipGetDevice(&dev);
+  return plan_columns(E, M, N, K, dev < 64 ? g_dev[dev].cus : 0, &regions);
+}
 
 int64_t mxw_grid_size(int E, int N, int K) {
   if (E < 1 || E > MXW_MAX_EXPERTS || N < 16 || K < 16) return 0;
@@ -655,10 +1043,25 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
     p.band = (32 + p.regK - 1) / p.regK;
     if (p.band > p.regN) p.band = p.regN;
   }
-  if ((M & 511) == 0)
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
-  else
-    hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  p.part = nullptr;
+  p.flags = nullptr;
+  p.hov = kColHov;
+  const int ncol = plan_columns(E, M, N, K, dev < 64 ? g_dev[dev].cus : 0, &p.regions);
+  p.ncol = ncol;
+  if (ncol) {
+    rc = get_workspace(dev, ncol, &p.part, &p.flags);
+    if (rc) return rc;
+    if ((M & 511) == 0)
+      hipLaunchKernelGGL((wgrad_kernel<true, true>), dim3((unsigned)(ncol * kMem)), dim3(kThreads), 0, (hipStream_t)stream, p);
+    else
+      hipLaunchKernelGGL((wgrad_kernel<false, true>), dim3((unsigned)(ncol * kMem)), dim3(kThreads), 0, (hipStream_t)stream, p);
+  } else if ((M & 511) == 0) {
+    hipLaunchKernelGGL((wgrad_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  } else {
+    hipLaunchKernelGGL((wgrad_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  }
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
   return MXW_OK;
 }
@@ -675,6 +1078,6 @@ const char* mxw_strerror(int code) {
   }
 }
 
-int mxw_version(void) { return 100; }
+int mxw_version(void) { return 200; }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ def test_library_built():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_strerror", "mxw_version"}
+    assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxw_strerror", "mxw_version"}
     lib = ctypes.CDLL(mxw.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -93,3 +93,14 @@ def test_python_face_validates_shapes():
         mxw.wgrad(A, sA, B, sB, offs)          # CPU tensors are refused: no host fallback
     with pytest.raises(TypeError):
         mxw.wgrad(A, sA, B, sB, offs.to(torch.int64))
+
+
+def test_columns_host_checks():
+    """mxw_columns rejects invalid sizes on the host, before any device query."""
+    lib = ctypes.CDLL(mxw.library_path())
+    lib.mxw_columns.restype = ctypes.c_int
+    lib.mxw_columns.argtypes = [ctypes.c_int] * 4
+    assert lib.mxw_columns(0, 8192, 256, 256) == -2
+    assert lib.mxw_columns(257, 8192, 256, 256) == -2
+    assert lib.mxw_columns(4, -32, 256, 256) == -2
+    assert lib.mxw_columns(4, 8192, 8, 256) == -2

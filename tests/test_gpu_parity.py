@@ -103,6 +103,39 @@ def test_ragged_shapes(case):
     full_compare(cfg, "ragged case %d" % case)
 
 
+COLUMN_CASES = [
+    # E, N, K, M, sizes: long experts on few tiles -> column mode, with regions
+    # cut across many columns (several partial tiles per region)
+    (1, 272, 528, 8192, [8192]),                   # one region spread over every column
+    (2, 512, 768, 16416, [8992, 7392]),            # M % 512 != 0 (dword scale path), padding
+    (3, 1040, 272, 24576, [12000, 0, 9600]),       # empty expert, partial tiles, 4-row and 1-row bands
+    (8, 1408, 2048, 65536, [12000, 4000, 9600, 0, 11200, 8000, 6400, 14336]),  # 16B shape
+]
+
+
+@pytest.mark.parametrize("case", range(len(COLUMN_CASES)))
+def test_column_mode_cases(case):
+    """Column mode (one workgroup per CU, regions split between columns and
+    summed through FP32 partials), whole output, plus bitwise repeat."""
+    E, N, K, M, sizes = COLUMN_CASES[case]
+    assert mxw.columns(E, M, N, K) > 0, "case does not select column mode"
+    cfg = W.make_random(E, N, K, M, sizes, seed=700 + case, device=DEV)
+    out, bits, ref, stats = full_compare(cfg, "column case %d" % case)
+    print("column case %d max_rel %.3e" % (case, stats["max_rel"]))
+    again = bf16_bits(run_gpu(cfg))
+    np.testing.assert_array_equal(again, bits)
+
+
+def test_mode_selection():
+    """The shapes the benchmark and parity cases rely on pick the mode the
+    design expects: column mode for the 16B shape at 24k tokens/expert, one
+    workgroup per tile for 1k tokens/expert and for the 671B shapes."""
+    assert mxw.columns(8, 196608, 1408, 2048) > 0
+    assert mxw.columns(8, 8192, 1408, 2048) == 0
+    assert mxw.columns(32, 262144, 4096, 7168) == 0
+    assert mxw.columns(32, 262144, 7168, 2048) == 0
+
+
 def test_16b_1k_full():
     """The 16B expert shape at 1,024 tokens/expert, whole output."""
     cfg = W.make_config("16b_1k", device=DEV)
