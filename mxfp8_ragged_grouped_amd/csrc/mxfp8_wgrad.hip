@@ -122,19 +122,18 @@ constexpr int kColHov = 3;
 constexpr int kColWaves = 4;
 constexpr int kColTokens = 8192;
 
-// LDS layout (150 KiB of the 160 KiB per CU).
+// LDS layout (159 KiB of the 160 KiB per CU).
 struct Smem {
   // [stage][0 = A n-rows, 1 = B k-rows]: 256 rows x 128 tokens, chunk-swizzled
   uint8_t data[2][2][kOpBytes];
-  // raw E8M0 scale bytes as loaded, 16 KiB, in one of two layouts:
-  //  grouped (scale rows 16-byte aligned): [group % 2][op][row][4 dwords], the
+  // raw E8M0 scale bytes as loaded, 24 KiB, in one of two layouts:
+  //  grouped (scale rows 16-byte aligned): [group % 3][op][row][4 dwords], the
   //    2 sub-block bytes of 8 consecutive K-steps of a row;
   //  paired (any row alignment): [pair % 4][op][dword][row], the two aligned
-  //    dwords that hold a row's 4 bytes of 2 consecutive K-steps
-  uint32_t raw[4096];
-  // destination of the out-of-range scale-slot loads on steps that have no
-  // scale group to fetch (written with zeros, never read)
-  uint32_t dummy[256];
+  //    dwords that hold a row's 4 bytes of 2 consecutive K-steps (16 KiB),
+  //    then 1 KiB taking the out-of-range scale-slot loads of steps that
+  //    have no scale pair to fetch (written with zeros, never read)
+  uint32_t raw[6144];
   int start[MXW_MAX_EXPERTS];
   int len[MXW_MAX_EXPERTS];
   int order[MXW_MAX_EXPERTS];
@@ -388,32 +387,33 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // step by step presents one cache line per row per step to the memory path,
   // as many requests as all of the step's operand data.  So when scale rows
   // are 16-byte aligned (M % 512 == 0) each row's 16 bytes of 8 consecutive
-  // K-steps ("group" G = steps 8G .. 8G+7) come in one 16-byte load per lane,
-  // 2 per wave per group, double-buffered by group parity; group G + 1 is
-  // fetched at step 8G.  Otherwise the two aligned dwords around each row's 4
-  // bytes of 2 consecutive K-steps ("pair" G = steps 2G, 2G+1) are fetched,
-  // 4 loads per wave per pair, into 4 buffers by pair % 4; pair G + 3 is
-  // fetched at step 2G.  Loads with real == false are out of range (no memory
-  // traffic) and land in the dummy area, so every step issues the same count.
+  // K-steps ("group" G = steps 8G .. 8G+7) come in one 16-byte load per lane
+  // and operand, into 3 buffers by G % 3: one load per loop iteration (4
+  // K-steps), operand k % 2 of group (s0 + 4 (k - k % 2)) / 8 + 2 in
+  // iteration k, so no step carries a load with nothing to fetch.  Otherwise
+  // the two aligned dwords around each row's 4 bytes of 2 consecutive K-steps
+  // ("pair" G = steps 2G, 2G+1) are fetched, 4 loads per wave per pair, into
+  // 4 buffers by pair % 4; pair G + 3 is fetched at step 2G, and loads with
+  // real == false are out of range (no memory traffic, but address-unit
+  // time) so that every step issues the same count.
   constexpr int kGroupSteps = GROUP ? 8 : 2;
   constexpr int kAhead = GROUP ? 1 : 3;
   constexpr int kScaleDma = GROUP ? 2 : 4;
+  // grouped: one operand's 16 bytes of group g for this lane's row, into
+  // slot g % 3 (groups past the row's end read other rows' bytes or nothing;
+  // they only reach steps past M, whose sub-blocks are all dead)
+  auto dma_scale_grp = [&](int g, int op) {
+    const uint32_t dst = lds_addr(&sm.raw[(((g % 3) * 2 + op) * kTile + wave * 64) * 4]);
+    dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), srow_off + 16u * (uint32_t)g, 0u);
+  };
   auto dma_scales = [&](int grp_idx, bool real) {
-    if (GROUP) {
-#pragma unroll
-      for (int op = 0; op < 2; ++op) {
-        const uint32_t so = real ? srow_off + 16u * (uint32_t)grp_idx : kOob;
-        const uint32_t dst = real ? lds_addr(&sm.raw[(((grp_idx & 1) * 2 + op) * kTile + wave * 64) * 4])
-                                  : lds_addr(&sm.dummy[0]);
-        dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), so, 0u);
-      }
-    } else {
+    {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {  // A lo, A hi, B lo, B hi
         const int op = k >> 1;
         const uint32_t so = real ? (srow_off & ~3u) + 4u * (uint32_t)grp_idx + 4u * (uint32_t)(k & 1) : kOob;
         const uint32_t dst = real ? lds_addr(&sm.raw[(((grp_idx & 3) * 2 + op) * 2 + (k & 1)) * kTile + wave * 64])
-                                  : lds_addr(&sm.dummy[0]);
+                                  : lds_addr(&sm.raw[4096]);
         dma4(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), so);
       }
     }
@@ -451,28 +451,37 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   const int s_end = (end + kStep - 1) / kStep;
   const int nsteps = (s_end - s0 + 3) & ~3;  // a multiple of 4: the loop body is unrolled by 4
 
-  // Every step issues kScaleDma scale-slot loads; odd steps first issue the
-  // 16 loads of the pair after next.  At the barrier of odd step j the pair
-  // issued at step j - 2 must have landed: only the two scale slots issued
-  // since may be in flight.
+  // Odd steps issue the 16 loads of the pair after next, then the scale
+  // loads (paired: kScaleDma per step; grouped: one per 4-step iteration, at
+  // its first step).  At the barrier of odd step j the pair issued at step
+  // j - 2 must have landed: only the scale loads issued since may be in
+  // flight.
   constexpr int kSlot = kScaleDma;
 
   // Prologue: the scale groups the first steps need, pairs s0/2 and s0/2 + 1,
-  // and one dummy scale slot (so the first odd barrier sees the usual count).
+  // and (paired) one dummy scale slot so the first odd barrier sees the usual
+  // count.
   const int qs = start >> 5, qn = (end - start) >> 5;
   {
     const int G0 = s0 / kGroupSteps;
+    if (GROUP) {
+      // groups G0 and G0 + 1; the loop fetches group G + 2 for both operands
+      // during the two iterations that start in group G
 #pragma unroll
-    for (int a = 0; a <= kAhead; ++a) dma_scales(G0 + a, true);
+      for (int a = 0; a < 4; ++a) dma_scale_grp(G0 + (a >> 1), a & 1);
+    } else {
+#pragma unroll
+      for (int a = 0; a <= kAhead; ++a) dma_scales(G0 + a, true);
+    }
     const int P0 = s0 >> 1;
     const uint32_t l0 = live_mask_pair(P0, qs, qn), l1 = live_mask_pair(P0 + 1, qs, qn);
 #pragma unroll
     for (int i = 0; i < kDataDma; ++i) dma_pair(i, 0, P0, l0);
 #pragma unroll
     for (int i = 0; i < kDataDma; ++i) dma_pair(i, 1, P0 + 1, l1);
-    dma_scales(0, false);
+    if (!GROUP) dma_scales(0, false);
   }
-  wait_vm<kDataDma + kSlot>();  // scales and pair s0/2 landed (this wave)
+  wait_vm<GROUP ? kDataDma : kDataDma + kSlot>();  // scales and pair s0/2 landed (this wave)
   __syncthreads();
 
   // Scale registers.  In lane l the MFMA takes the E8M0 byte of row l % 32 and
@@ -492,7 +501,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
       uint32_t a, b;
       if (GROUP) {
-        const int slot = (x >> 3) & 1, dw = (x & 7) >> 1;
+        const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
         a = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
         b = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
       } else {
@@ -552,7 +561,11 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         }
         if (m == 1 && (u & 1)) {
           __builtin_amdgcn_sched_barrier(0);
-          wait_vm<2 * kSlot>();
+          // grouped: only the scale load of u = 0 follows the pair's loads
+          // before the barrier of u = 1, none before that of u = 3
+          if (!GROUP) wait_vm<2 * kSlot>();
+          else if (u == 1) wait_vm<1>();
+          else wait_vm<0>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -572,7 +585,15 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
         if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
-        if (m == 15) dma_scales(sgrp, sreal);  // after the pair's loads (vmcnt order)
+        if (m == 15) {  // after the step's data loads (vmcnt order)
+          if (!GROUP) {
+            dma_scales(sgrp, sreal);
+          } else if (u == 0) {
+            // iteration k fetches operand k % 2 of group (s0 + 4 (k - k % 2)) / 8 + 2
+            const int kk = jj >> 2;
+            dma_scale_grp(((s0 + 4 * (kk & ~1)) >> 3) + 2, kk & 1);
+          }
+        }
         if (m == 13) {
           int sp = s;
           asm volatile("" : "+s"(sp));
