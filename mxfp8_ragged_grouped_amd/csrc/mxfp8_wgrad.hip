@@ -32,8 +32,8 @@
 //     128 bytes per instruction, so every memory request is one whole cache
 //     line (half-line requests halve the miss bandwidth, measured); two stages
 //     ping-pong (blog section 4).  The 16-byte chunk c of row r sits at
-//     position c ^ (r & 7): the MFMA fragment reads are free of LDS bank
-//     conflicts (8 lanes of a read hit 8 distinct 16-byte bank groups).
+//     position c ^ ((r / 2) % 8): the MFMA fragment reads, served 16 lanes
+//     (256 bytes of banks) at a time, are free of LDS bank conflicts.
 //   * software pipeline: the fragments of K-step j + 1 are read from LDS into
 //     a second register set while K-step j's 16 MFMAs run, one read per MFMA,
 //     so the MFMAs never wait on LDS and the LDS stays evenly loaded.  One
@@ -146,9 +146,13 @@ struct Smem {
   int cnt[4];
 };
 
-// 16-byte chunk c of staged row r sits at chunk position c ^ swz(r): 8
-// consecutive rows read at one chunk index then hit distinct LDS banks
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// 16-byte chunk c of staged row r sits at chunk position c ^ swz(r).  A
+// ds_read_b128 is served 16 lanes (256 bytes of banks) at a time; a fragment
+// read's 16 lanes take rows r .. r+15 at one chunk index, and with 128-byte
+// rows two rows share a 256-byte bank line, so swz must differ across the 8
+// rows of each parity: (r / 2) % 8 (r % 8 left rows r and r + 8 on the same
+// banks, measured with SQ_LDS_BANK_CONFLICT)
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -366,19 +370,20 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // stripes.  Lane i of a group writes LDS bytes [16 i, 16 i + 16) of the group:
   // row i / 8, chunk position i % 8, which holds global chunk (i % 8) ^ swz(row).
   const int lrow = lane >> 3;
-  const int ch = (lane & 7) ^ swz(lrow);
+  // swz of the wave's rows depends on lrow and the parity of the row group q
+  const int ch_e = (lane & 7) ^ swz(lrow), ch_o = (lane & 7) ^ swz(8 + lrow);
   uint32_t vrow[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) vrow[q] = (uint32_t)((wave * 8 + q) * 8 + lrow) * (uint32_t)M + (uint32_t)(ch * 16);
+  for (int q = 0; q < 8; ++q) vrow[q] = (uint32_t)((wave * 8 + q) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
   // Scales: lane l of wave w fetches scale row 64 w + l.
   const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * sbytes;
-  const int sbl = ch >> 1;  // this lane's 32-token sub-block within a pair
+  const int sbl_e = ch_e >> 1, sbl_o = ch_o >> 1;  // this lane's 32-token sub-block within a pair
   const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[0][0][wave * 8 * 1024]));
   // pair P into stage buf: load i of 16 (row group 8w + i/2 of A for even i,
   // of B for odd i); dead sub-blocks are forced out of range
   auto dma_pair = [&](int i, int buf, int P, uint32_t live) {
     const int q = i >> 1, op = i & 1;
-    const bool ok = (live >> sbl) & 1u;
+    const bool ok = (live >> ((q & 1) ? sbl_o : sbl_e)) & 1u;
     dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + q * 1024), ok ? vrow[q] : kOob,
           (uint32_t)(P * kPair));
   };
@@ -555,9 +560,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
                                   (int)sra[u >> 1][t]);
         if (m == 0 && (u & 1)) {
-          const bool lok = (livep >> sbl) & 1u;
+          const bool lok_e = (livep >> sbl_e) & 1u, lok_o = (livep >> sbl_o) & 1u;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) va[q] = lok ? vrow[q] : kOob;
+          for (int q = 0; q < 8; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? vrow[q] : kOob;
         }
         if (m == 1 && (u & 1)) {
           __builtin_amdgcn_sched_barrier(0);
@@ -697,8 +702,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     // bf16 RNE in registers, then through this wave's 32 KiB of the (now idle)
     // stage area so that every global store writes whole 128-byte lines: the
     // quarter is laid out as 128 rows of 256 bytes, 16-byte chunk c of row n
-    // at position c ^ (n % 16) (the 8-byte writes then meet at most 2-way
-    // bank conflicts and the 16-byte reads none).
+    // at position c ^ (n % 16), its two 8-byte halves swapped when n / 16 is
+    // odd.  The 8-byte writes of 32 lanes (rows n .. n+31, one half each) and
+    // the 16-byte reads of 16 lanes then all hit distinct banks.
     __syncthreads();  // every wave is done with the stages
     uint8_t* ep = &sm.data[0][0][0] + wave * 32768;
 #pragma unroll
@@ -713,14 +719,15 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           uint2 w;
           w.x = pack_bf16x2(v.x, v.y);
           w.y = pack_bf16x2(v.z, v.w);
-          *(uint2*)(ep + nl * 256 + ((c ^ (nl & 15)) << 4) + fq * 8) = w;
+          *(uint2*)(ep + nl * 256 + ((c ^ (nl & 15)) << 4) + ((fq ^ (nl >> 4)) & 1) * 8) = w;
         }
     const int rsub = lane >> 4, cl = lane & 15;
     const int kk = k0 + wk * 128 + cl * 8;
 #pragma unroll
     for (int x = 0; x < 32; ++x) {
       const int nl = 4 * x + rsub;
-      const v4i d = *(const v4i*)(ep + nl * 256 + ((cl ^ (nl & 15)) << 4));
+      v4i d = *(const v4i*)(ep + nl * 256 + ((cl ^ (nl & 15)) << 4));
+      if ((nl >> 4) & 1) d = (v4i){d.z, d.w, d.x, d.y};  // (x / 4) % 2: a constant after unrolling
       const int n = n0 + wn * 128 + nl;
       if (n < N && kk < K) *(v4i*)(outg + (size_t)n * K + kk) = d;
     }
