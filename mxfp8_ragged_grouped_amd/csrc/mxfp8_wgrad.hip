@@ -521,8 +521,30 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     }
   };
 
+  // grouped: the raw dwords are read a few MFMAs before they are shifted and
+  // masked, so the wave does not wait on the LDS between two MFMAs
+  auto read_raw = [&](int x, uint32_t* a4, uint32_t* b4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
+      const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
+      a4[i] = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
+      b4[i] = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
+    }
+  };
+  auto finish_sregs = [&](int x, const uint32_t* a4, const uint32_t* b4, uint32_t* ra4, uint32_t* rb4) {
+    const uint32_t pm = (((live_mask_q(x, qs, qn) >> msb) & 1u) ? 0xFFu : 0u) |
+                        (((live_mask_q(x + 1, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra4[i] = (a4[i] >> mshift) & pm;
+      rb4[i] = (b4[i] >> mshift) & pm;
+    }
+  };
+
   v8i fa[2][4], fb[2][4];
   uint32_t sra[2][4], srb[2][4];  // [pair parity][32-row block]
+  uint32_t rawa[4], rawb[4];
   load_sregs(s0, sra[0], srb[0]);
   {
     const uint8_t* ta = sm.data[0][0] + (wn * 128) * kRowBytes;
@@ -590,6 +612,11 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
         if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
+        if (GROUP && (u & 1) && m == 10) {
+          int sq = s;
+          asm volatile("" : "+s"(sq));
+          read_raw(sq + 1, rawa, rawb);
+        }
         if (m == 15) {  // after the step's data loads (vmcnt order)
           if (!GROUP) {
             dma_scales(sgrp, sreal);
@@ -604,7 +631,10 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           asm volatile("" : "+s"(sp));
           // odd step: the next pair's scale registers (its raw bytes landed
           // with the pair, certified by this step's barrier)
-          if (u & 1) load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
+          if (u & 1) {
+            if (GROUP) finish_sregs(sp + 1, rawa, rawb, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
+            else load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
+          }
           if (!(u & 1)) livep = live_mask_pair(((sp + 1) >> 1) + 2, qs, qn);
           sreal = ((sp + 1) % kGroupSteps) == 0;
           sgrp = (sp + 1) / kGroupSteps + kAhead;
