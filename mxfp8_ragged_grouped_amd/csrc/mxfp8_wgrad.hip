@@ -753,13 +753,25 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         }
     const int rsub = lane >> 4, cl = lane & 15;
     const int kk = k0 + wk * 128 + cl * 8;
+    // 8 reads in flight before their stores (one read, wait, store at a time
+    // left the wave waiting on the LDS 32 times)
 #pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      const int nl = 4 * x + rsub;
-      v4i d = *(const v4i*)(ep + nl * 256 + ((cl ^ (nl & 15)) << 4));
-      if ((nl >> 4) & 1) d = (v4i){d.z, d.w, d.x, d.y};  // (x / 4) % 2: a constant after unrolling
-      const int n = n0 + wn * 128 + nl;
-      if (n < N && kk < K) *(v4i*)(outg + (size_t)n * K + kk) = d;
+    for (int x0 = 0; x0 < 32; x0 += 8) {
+      v4i d[8];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int nl = 4 * (x0 + x) + rsub;
+        d[x] = *(const v4i*)(ep + nl * 256 + ((cl ^ (nl & 15)) << 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int nl = 4 * (x0 + x) + rsub;
+        if ((nl >> 4) & 1) d[x] = (v4i){d[x].z, d[x].w, d[x].x, d[x].y};  // a constant after unrolling
+        const int n = n0 + wn * 128 + nl;
+        if (n < N && kk < K) *(v4i*)(outg + (size_t)n * K + kk) = d[x];
+      }
     }
   }
   if (COL && role == 1) {
