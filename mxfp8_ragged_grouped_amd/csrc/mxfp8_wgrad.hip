@@ -372,9 +372,24 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   const int lrow = lane >> 3;
   // swz of the wave's rows depends on lrow and the parity of the row group q
   const int ch_e = (lane & 7) ^ swz(lrow), ch_o = (lane & 7) ^ swz(8 + lrow);
-  uint32_t vrow[8];
+  // Column mode: the lane's offset for each row group q in a register.  One
+  // workgroup per tile: the offset in group 0 of q's parity, plus q * 8 M
+  // bytes as a scalar (soffset), and the row groups go out in a rotated
+  // order: the tiles that share an A (B) stripe issue its groups rotated by
+  // different even amounts, so each tile's first loads of a pair are the
+  // likely misses, with the most lead, and its last ones mostly hit lines
+  // another tile requested earlier.  (Column mode's in-step tiles lost with
+  // the rotation, and its extra scalar state spilled.)
+  uint32_t vrow[COL ? 8 : 1];
+  if constexpr (COL) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) vrow[q] = (uint32_t)((wave * 8 + q) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
+    for (int q = 0; q < 8; ++q)
+      vrow[q] = (uint32_t)((wave * 8 + q) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
+  }
+  const uint32_t vr_e = (uint32_t)(wave * 64 + lrow) * (uint32_t)M + (uint32_t)(ch_e * 16);
+  const uint32_t vr_o = (uint32_t)(wave * 64 + lrow) * (uint32_t)M + (uint32_t)(ch_o * 16);
+  const uint32_t M8 = 8u * (uint32_t)M;
+  const int rotA = COL ? 0 : 2 * ((pc.tk + pc.tn) & 3), rotB = COL ? 0 : 2 * ((pc.tn + 2 * pc.tk) & 3);
   // Scales: lane l of wave w fetches scale row 64 w + l.
   const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * sbytes;
   const int sbl_e = ch_e >> 1, sbl_o = ch_o >> 1;  // this lane's 32-token sub-block within a pair
@@ -382,10 +397,16 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // pair P into stage buf: load i of 16 (row group 8w + i/2 of A for even i,
   // of B for odd i); dead sub-blocks are forced out of range
   auto dma_pair = [&](int i, int buf, int P, uint32_t live) {
-    const int q = i >> 1, op = i & 1;
-    const bool ok = (live >> ((q & 1) ? sbl_o : sbl_e)) & 1u;
-    dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + q * 1024), ok ? vrow[q] : kOob,
-          (uint32_t)(P * kPair));
+    const int qi = i >> 1, op = i & 1;
+    const bool ok = (live >> ((qi & 1) ? sbl_o : sbl_e)) & 1u;
+    if constexpr (COL) {
+      dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + qi * 1024), ok ? vrow[qi] : kOob,
+            (uint32_t)(P * kPair));
+    } else {
+      const int q = (qi + (op ? rotB : rotA)) & 7;  // same parity as qi
+      dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + q * 1024), ok ? ((qi & 1) ? vr_o : vr_e) : kOob,
+            (uint32_t)(P * kPair) + (uint32_t)q * M8);
+    }
   };
 
   // Scale loads.  A K-step needs 2 bytes of each of 512 rows; fetching them
@@ -560,7 +581,17 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   int sgrp = s0 / kGroupSteps + kAhead;
   bool sreal = false;  // s0 never issues a real scale load
 
-#define MXW_DMA(I, U) dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + ((I) >> 1) * 1024), va[(I) >> 1], soffp)
+#define MXW_DMA(I, U)                                                                                          \
+  do {                                                                                                         \
+    if constexpr (COL) {                                                                                       \
+      dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + ((I) >> 1) * 1024), \
+            va[(I) >> 1], soffp);                                                                              \
+    } else {                                                                                                   \
+      const int q_ = (((I) >> 1) + (((I) & 1) ? rotB : rotA)) & 7;                                             \
+      dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + q_ * 1024),     \
+            va[((I) >> 1) & 1], soffp + (uint32_t)q_ * M8);                                                    \
+    }                                                                                                          \
+  } while (0)
   for (int jj = 0;; jj += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -584,7 +615,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         if (m == 0 && (u & 1)) {
           const bool lok_e = (livep >> sbl_e) & 1u, lok_o = (livep >> sbl_o) & 1u;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? vrow[q] : kOob;
+          for (int q = 0; q < 8; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? (COL ? vrow[COL ? q : 0] : ((q & 1) ? vr_o : vr_e)) : kOob;
         }
         if (m == 1 && (u & 1)) {
           __builtin_amdgcn_sched_barrier(0);
