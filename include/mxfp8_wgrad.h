@@ -85,16 +85,16 @@ extern "C" {
  *
  * Scheduling and state: with few output tiles per compute unit and long
  * experts (mxw_columns() > 0) the launch runs in column mode, one workgroup
- * per CU, and a region of tiles cut between two columns is summed through
- * FP32 partial tiles in a device workspace.  The library allocates that
- * workspace (64 MiB on a 256-CU device, with its flags) with hipMalloc on the
- * first column-mode call on a device, synchronising the device once, and
- * keeps it until the process ends.  Column-mode launches on one device must
- * not overlap in time (different streams would race on the workspace); the
- * column-mode kernel also expects to have the device's compute units to
- * itself while it runs (its columns exchange partials, waiting with a
- * bounded spin: a partial that never arrives turns its tile into NaN rather
- * than hanging).  Otherwise the call allocates nothing and keeps no state.
+ * per CU, and a region of tiles cut between columns is summed through FP32
+ * partial tiles in a device workspace plus one arrival counter per region:
+ * the last piece of a region to finish adds the others' partials, so no
+ * workgroup ever waits for another and the kernel needs no co-residency.
+ * The library allocates that workspace (128 MiB on a 256-CU device) with
+ * hipMalloc on the first column-mode call on a device, synchronising the
+ * device once, and keeps it until the process ends; every launch leaves the
+ * counters at zero.  Column-mode launches on one device must not overlap in
+ * time (launches on different streams would race on the workspace).
+ * Otherwise the call allocates nothing and keeps no state.
  *
  * Returns MXW_OK or a negative MXW_ERR_* code.
  */

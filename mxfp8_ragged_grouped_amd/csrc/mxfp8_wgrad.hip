@@ -25,8 +25,9 @@
 //       the XCD's L2.  The sequence of (expert, region) pieces, weighted by
 //       K-steps, is cut into equal spans, one per column (whole tiles pack
 //       unevenly: 1.3x the ideal span at 1.5 tiles per CU).  A region cut
-//       between columns is summed in a fixed order: the later pieces store
-//       FP32 partial tiles and raise a flag, the first piece adds them.
+//       between columns is summed in a fixed order: its pieces count
+//       themselves in on a counter and the last to finish adds the others'
+//       FP32 partial tiles (no workgroup waits for another).
 //   * staging: an LDS stage holds a pair of K-steps (256 rows x 128 tokens of
 //     A and of B, 64 KiB), filled by 16-byte LDS-direct buffer loads, 8 rows x
 //     128 bytes per instruction, so every memory request is one whole cache
@@ -276,8 +277,8 @@ struct Params {
   // each column on one XCD (one workgroup per CU); the (expert, region) work
   // sequence is cut into ncol equal spans, one per column, and a region cut
   // between columns is summed through FP32 partial tiles
-  float* part;      // [ncol][kMem][kTile * kTile] partial tiles
-  uint32_t* flags;  // [ncol][kMem] partial-ready flags, 0 between launches
+  float* part;      // [ncol][2][kMem][kTile * kTile] partial tiles (a column's first / last piece)
+  uint32_t* flags;  // [ncol][kMem] arrival counters of cut regions, 0 between launches
   int ncol;
   int regions;  // regions of up to kMem tiles per expert
   int hov;      // per-region cost, in K-steps, added to the split's weights
@@ -678,54 +679,63 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #undef MXW_DMA
   wait_vm_all();  // no LDS-direct load may outlive the workgroup
 
-  // ---- column mode: partial tiles --------------------------------------------
-  // Layout: [column][member][wave][block i][block t][quad q][lane], 16 bytes
-  // each (the accumulator registers as they sit).  A piece that continues a
-  // region (role 1) stores its sums there and raises its flag; the region's
-  // first piece (role 2) waits for the flags of the later columns that hold a
-  // piece of the region and adds their partials, in column order.
-  uint64_t pmask = 0;  // role 2: contributing columns
-  if (COL && role == 2) {
-    for (int cc = col + 1; cc < p.ncol; ++cc) {
+  // ---- column mode: regions cut between columns ------------------------------
+  // Such a region has one piece in each column that holds part of it (column
+  // order = token order).  When its K-loop is done, every piece counts itself
+  // in on the region's counter (a device-scope atomic); the last one to arrive
+  // finishes the region.  With two pieces it adds the other piece's FP32
+  // partial tile to its own sums -- IEEE addition is commutative, so the bits
+  // do not depend on which piece arrives last; with more, every piece stores
+  // its partial and the last one adds them all, in column order, from zero.
+  // No workgroup ever waits for another.  Partial tiles move between XCDs,
+  // whose L2s are not coherent with each other: they are written and read
+  // with device-scope (sc1) accesses, which go to memory rather than a local
+  // cache, and a piece counts itself in only after its stores have completed.
+  // Layout of a slot: [wave][block i][block t][quad q][lane], 16 bytes each
+  // (the accumulator registers as they sit); slot [column][0 / 1][member]
+  // holds the column's first / last piece (a region's first piece is the last
+  // piece of its column, its other pieces are first pieces).
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.part, (uint32_t)(p.ncol * 2 * kMem) * (uint32_t)(kTile * kTile * 4));
+  const uint32_t pidx = (uint32_t)(wave * 64 * 64 + lane) * 16u;  // + (((i * 4 + t) * 4 + q) * 64) * 16
+  bool finish = true;  // this piece writes the bf16 result
+  if (COL && role != 0) {
+    uint64_t pmask = 0;  // columns holding a piece of this region
+    for (int cc = 0; cc < p.ncol; ++cc) {
       const int lo = min(max((cc * Q - ra_lin + 2) >> 2, 0), r_it);
       const int hi = min(max(((cc + 1) * Q - ra_lin + 2) >> 2, 0), r_it);
       if (lo >= r_it) break;
       if (lo < hi) pmask |= 1ull << cc;
     }
-    if (tid == 0) {
-      // bounded wait (seconds): a partial that never comes -- only possible
-      // if the grid is not co-resident -- turns the tile into NaN instead of
-      // a hang
-      int lost = 0;
-      for (uint64_t m = pmask; m; m &= m - 1) {
-        uint32_t* fl = &p.flags[__builtin_ctzll(m) * kMem + member];
-        int spins = 0;
-        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 1u && spins < (1 << 21)) {
-          __builtin_amdgcn_s_sleep(4);
-          ++spins;
-        }
-        if (spins >= (1 << 21)) lost = 1;
-        __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      sm.cnt[3] = lost;
-    }
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(sm.cnt[3])) pmask = 0;
-  }
-  const bool lost = COL && role == 2 && pmask == 0;
-  // Partial tiles move between XCDs, whose L2s are not coherent with each
-  // other: they are written and read with device-scope (sc1) accesses, which
-  // go to memory rather than a local cache, so the handover needs no L2
-  // writeback or invalidation; the writer's flag follows its stores' vmcnt.
-  const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.part, (uint32_t)(p.ncol * kMem) * (uint32_t)(kTile * kTile * 4));
-  const uint32_t pidx = (uint32_t)(wave * 64 * 64 + lane) * 16u;  // + (((i * 4 + t) * 4 + q) * 64) * 16
-  const uint32_t pmine = (uint32_t)(col * kMem + member) * (uint32_t)(kTile * kTile * 4) + pidx;
-  const uint32_t pbase = (uint32_t)member * (uint32_t)(kTile * kTile * 4) + pidx;  // + cc * 8 tiles
-
-  if (COL && role == 2) {
-    // add the partials, one later column at a time, 16 loads in flight
-    for (uint64_t m = pmask; m; m &= m - 1) {
-      const uint32_t src = pbase + (uint32_t)__builtin_ctzll(m) * (uint32_t)(kMem * kTile * kTile * 4);
+    pmask |= 1ull << col;  // never empty, whatever the arithmetic above says
+    const int c0 = __builtin_ctzll(pmask), np = __builtin_popcountll(pmask);
+    uint32_t* ctr = &p.flags[c0 * kMem + member];
+    auto slot = [&](int cc) {
+      return (uint32_t)((cc * 2 + (cc == c0 ? 1 : 0)) * kMem + member) * (uint32_t)(kTile * kTile * 4) + pidx;
+    };
+    auto store_mine = [&]() {
+      const uint32_t dst = slot(col);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v4f v = {acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rP, dst + (uint32_t)(((i * 4 + t) * 4 + q) * 64) * 16u, 0, kSc1);
+          }
+      wait_vm_all();  // this wave's partial has reached memory
+    };
+    // tid 0 performs op on the counter; every thread gets its result
+    auto counter = [&](bool add) {
+      __syncthreads();
+      if (tid == 0)
+        sm.cnt[3] = add ? (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : (int)__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      return __builtin_amdgcn_readfirstlane(sm.cnt[3]);
+    };
+    // acc (+)= the partial in slot src, 16 loads in flight
+    auto add_partial = [&](uint32_t src, auto add) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v4f w[16];
@@ -737,29 +747,36 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int t = x >> 2, q = x & 3;
-          acc[i][t][4 * q] += w[x].x;
-          acc[i][t][4 * q + 1] += w[x].y;
-          acc[i][t][4 * q + 2] += w[x].z;
-          acc[i][t][4 * q + 3] += w[x].w;
+          acc[i][t][4 * q] = add ? acc[i][t][4 * q] + w[x].x : w[x].x;
+          acc[i][t][4 * q + 1] = add ? acc[i][t][4 * q + 1] + w[x].y : w[x].y;
+          acc[i][t][4 * q + 2] = add ? acc[i][t][4 * q + 2] + w[x].z : w[x].z;
+          acc[i][t][4 * q + 3] = add ? acc[i][t][4 * q + 3] + w[x].w : w[x].w;
         }
       }
+    };
+    // two pieces: if the other one is done already, finish without storing
+    if (np == 2 && counter(false) != 0) {
+      finish = true;
+    } else {
+      store_mine();
+      finish = counter(true) == np - 1;
     }
+    if (finish) {
+      uint64_t todo = pmask & ~(1ull << col);  // two pieces: mine + the other's
+      if (np != 2) {                            // more: all, in column order
+        add_partial(slot(c0), std::false_type{});
+        todo = pmask & (pmask - 1);
+      }
+      for (uint64_t m = todo; m; m &= m - 1) add_partial(slot(__builtin_ctzll(m)), std::true_type{});
+    }
+    // the finisher leaves the counter at 0 for the next launch
+    if (finish && tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue ------------------------------------------------------------------
   // block (i, t): lane l register r holds k = 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
   // n = 32 t + l % 32 (within the wave's 128 x 128 quarter).
-  if (COL && role == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4f v = {acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(v, rP, pmine + (uint32_t)(((i * 4 + t) * 4 + q) * 64) * 16u, 0, kSc1);
-        }
-  } else {
+  if (finish) {
     // bf16 RNE in registers, then through this wave's 32 KiB of the (now idle)
     // stage area so that every global store writes whole 128-byte lines: the
     // quarter is laid out as 128 rows of 256 bytes, 16-byte chunk c of row n
@@ -775,7 +792,6 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v4f v = {acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
-          if (lost) v = (v4f){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
           const int nl = 32 * t + fr, c = 4 * i + q;
           uint2 w;
           w.x = pack_bf16x2(v.x, v.y);
@@ -804,11 +820,6 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         if (n < N && kk < K) *(v4i*)(outg + (size_t)n * K + kk) = d[x];
       }
     }
-  }
-  if (COL && role == 1) {
-    wait_vm_all();  // this wave's partial stores have reached memory
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(&p.flags[col * kMem + member], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1012,8 +1023,9 @@ struct DeviceInfo {
 DeviceInfo g_dev[64];
 std::mutex g_ws_mutex;
 
-// Column-mode workspace of the current device: ncol x 8 FP32 partial tiles
-// and their flags (zeroed once; every reader resets the flag it consumed).
+// Column-mode workspace of the current device: ncol x 2 x kMem FP32 partial
+// tiles and ncol x kMem arrival counters (zeroed once; the piece that
+// finishes a region resets its counter).
 int get_workspace(int dev, int ncol, float** part, uint32_t** flags) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   DeviceInfo& d = g_dev[dev];
@@ -1027,7 +1039,7 @@ int get_workspace(int dev, int ncol, float** part, uint32_t** flags) {
     }
     void* pp = nullptr;
     void* fp = nullptr;
-    if (hipMalloc(&pp, (size_t)ncol * kMem * kTile * kTile * sizeof(float)) != hipSuccess) return MXW_ERR_LAUNCH;
+    if (hipMalloc(&pp, (size_t)ncol * 2 * kMem * kTile * kTile * sizeof(float)) != hipSuccess) return MXW_ERR_LAUNCH;
     if (hipMalloc(&fp, (size_t)ncol * kMem * sizeof(uint32_t)) != hipSuccess) {
       (void)hipFree(pp);
       return MXW_ERR_LAUNCH;
@@ -1065,7 +1077,7 @@ int check_device() {
 // regions per expert.  Column mode when the work items fill the chip only a
 // few times over (whole tiles then pack unevenly onto the compute units) and
 // experts are long enough to amortise the per-piece costs; it needs whole
-// 8-column groups (one column per XCD each), a flag mask of at most 64
+// 8-column groups (one column per XCD each), a column mask of at most 64
 // columns and a work sequence that fits in int.
 int plan_columns(int E, int M, int N, int K, int cus, int* regions) {
   const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
