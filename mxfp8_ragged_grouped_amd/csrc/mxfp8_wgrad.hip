@@ -106,6 +106,8 @@ constexpr uint32_t kOob = 0x80000000u;       // a buffer offset past any range u
 // DMA instructions per wave per pair of K-steps for operand data: 8 row groups
 // (8 rows x 128 B = 1 KiB each) of A and 8 of B.
 constexpr int kDataDma = 16;
+// column mode: L2 prefetch loads per wave per even K-step
+constexpr int kPrefetch = 4;
 // raw buffer descriptor word 3 for gfx9-family: 32-bit data format, no swizzle,
 // range checking on the byte offset
 constexpr int kRsrcWord3 = 0x00020000;
@@ -145,6 +147,7 @@ struct Smem {
   int pre[MXW_MAX_EXPERTS];
   int ee[MXW_MAX_EXPERTS];
   int cnt[4];
+  uint32_t pfd[64];  // landing place of the L2 prefetch loads (never read)
 };
 
 // 16-byte chunk c of staged row r sits at chunk position c ^ swz(r).  A
@@ -188,6 +191,17 @@ __device__ __forceinline__ void dma4(const __amdgpu_buffer_rsrc_t& rsrc, uint32_
 }
 #pragma clang diagnostic pop
 
+// the same for 4 bytes per lane (lane l's dword lands at lds + 4 l), with a
+// scalar offset added after the range check
+__device__ __forceinline__ void dma4s(const __amdgpu_buffer_rsrc_t& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
 // counter waits (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the counters not waited on are left at their maxima)
 template <int N>
@@ -334,8 +348,8 @@ __device__ __forceinline__ void zero_tile(const Params& p, int g, int tn, int tk
 // One tile piece: tokens [start, end) of expert g into tile (tn, tk).
 struct Piece {
   int g, tn, tk, start, end;
-  int role;  // 0: whole tile (bf16 out), 1: hands over an FP32 partial, 2: adds partials
-  int col, member, Q, ra_lin, r_it;  // column mode: position and the region (role 2)
+  int role;  // 0: whole tile; 1, 2: a piece of a region cut between columns (2: its first)
+  int col, member, Q, ra_lin, r_it;  // column mode: position, column quota, the region's place and length
 };
 
 template <bool GROUP, bool COL>
@@ -373,41 +387,48 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   const int lrow = lane >> 3;
   // swz of the wave's rows depends on lrow and the parity of the row group q
   const int ch_e = (lane & 7) ^ swz(lrow), ch_o = (lane & 7) ^ swz(8 + lrow);
-  // Column mode: the lane's offset for each row group q in a register.  One
-  // workgroup per tile: the offset in group 0 of q's parity, plus q * 8 M
-  // bytes as a scalar (soffset), and the row groups go out in a rotated
-  // order: the tiles that share an A (B) stripe issue its groups rotated by
-  // different even amounts, so each tile's first loads of a pair are the
-  // likely misses, with the most lead, and its last ones mostly hit lines
-  // another tile requested earlier.  (Column mode's in-step tiles lost with
-  // the rotation, and its extra scalar state spilled.)
-  uint32_t vrow[COL ? 8 : 1];
-  if constexpr (COL) {
+  // The lane's offset for each of the wave's 8 row groups, in a register (so
+  // the descriptor's range check sees the row: rows past the operand's end
+  // read nothing).  One workgroup per tile: the row groups go out in a
+  // rotated order, load q taking group (q + rot) % 8: the tiles that share an
+  // A (B) stripe rotate by different even amounts, so each tile's first loads
+  // of a pair are the likely misses, with the most lead, and its last ones
+  // mostly hit lines another tile requested earlier.  (Column mode's in-step
+  // tiles lose with the rotation.)
+  const int rot = COL ? 0 : 2 * ((pc.tk + pc.tn) & 3);
+  uint32_t vrow[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      vrow[q] = (uint32_t)((wave * 8 + q) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
-  }
-  const uint32_t vr_e = (uint32_t)(wave * 64 + lrow) * (uint32_t)M + (uint32_t)(ch_e * 16);
-  const uint32_t vr_o = (uint32_t)(wave * 64 + lrow) * (uint32_t)M + (uint32_t)(ch_o * 16);
-  const uint32_t M8 = 8u * (uint32_t)M;
-  const int rotA = COL ? 0 : 2 * ((pc.tk + pc.tn) & 3), rotB = COL ? 0 : 2 * ((pc.tn + 2 * pc.tk) & 3);
+  for (int q = 0; q < 8; ++q)
+    vrow[q] = (uint32_t)((wave * 8 + ((q + rot) & 7)) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
   // Scales: lane l of wave w fetches scale row 64 w + l.
   const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * sbytes;
   const int sbl_e = ch_e >> 1, sbl_o = ch_o >> 1;  // this lane's 32-token sub-block within a pair
   const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[0][0][wave * 8 * 1024]));
+  // Column mode L2 prefetch.  The tiles of a region that share an A (B) stripe
+  // run in step and would all wait out the same misses; instead, at each even
+  // step every tile touches its share of the stripe lines of the pair after
+  // the one the next odd step loads (one dword per line, 8 lines per
+  // instruction), so that pair's loads mostly hit in L2.  Sharer i of a stripe with
+  // S sharers takes row groups i and i + S (if < 8) of every wave's 8, of A
+  // and of B: two instructions per operand per wave.
+  int pfa = 8, pfb = 8, pfsa = 8, pfsb = 8;
+  if constexpr (COL) {
+    const int full = p.tilesN >> 2, band = pc.tn >> 2;
+    const int rh = band < full ? 4 : p.tilesN - 4 * full;  // region height (tiles along N)
+    pfa = __builtin_amdgcn_readfirstlane(member / rh);      // index among the A stripe's sharers
+    pfb = __builtin_amdgcn_readfirstlane(member % rh);      // among the B stripe's
+    pfsa = __builtin_amdgcn_readfirstlane(kMem / rh);       // A stripe sharers = region width
+    pfsb = __builtin_amdgcn_readfirstlane(rh);
+  }
+  const uint32_t pfdst = __builtin_amdgcn_readfirstlane(lds_addr(&sm.pfd[0]));
   // pair P into stage buf: load i of 16 (row group 8w + i/2 of A for even i,
   // of B for odd i); dead sub-blocks are forced out of range
   auto dma_pair = [&](int i, int buf, int P, uint32_t live) {
     const int qi = i >> 1, op = i & 1;
     const bool ok = (live >> ((qi & 1) ? sbl_o : sbl_e)) & 1u;
-    if constexpr (COL) {
-      dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + qi * 1024), ok ? vrow[qi] : kOob,
-            (uint32_t)(P * kPair));
-    } else {
-      const int q = (qi + (op ? rotB : rotA)) & 7;  // same parity as qi
-      dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + q * 1024), ok ? ((qi & 1) ? vr_o : vr_e) : kOob,
-            (uint32_t)(P * kPair) + (uint32_t)q * M8);
-    }
+    const int q = (qi + rot) & 7;  // same parity as qi
+    dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kOpBytes + q * 1024), ok ? vrow[qi] : kOob,
+          (uint32_t)(P * kPair));
   };
 
   // Scale loads.  A K-step needs 2 bytes of each of 512 rows; fetching them
@@ -582,16 +603,11 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   int sgrp = s0 / kGroupSteps + kAhead;
   bool sreal = false;  // s0 never issues a real scale load
 
-#define MXW_DMA(I, U)                                                                                          \
-  do {                                                                                                         \
-    if constexpr (COL) {                                                                                       \
-      dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + ((I) >> 1) * 1024), \
-            va[(I) >> 1], soffp);                                                                              \
-    } else {                                                                                                   \
-      const int q_ = (((I) >> 1) + (((I) & 1) ? rotB : rotA)) & 7;                                             \
-      dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + q_ * 1024),     \
-            va[((I) >> 1) & 1], soffp + (uint32_t)q_ * M8);                                                    \
-    }                                                                                                          \
+#define MXW_DMA(I, U)                                                                                        \
+  do {                                                                                                       \
+    const int q_ = (((I) >> 1) + rot) & 7;                                                                   \
+    dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + q_ * 1024), \
+          va[(I) >> 1], soffp);                                                                              \
   } while (0)
   for (int jj = 0;; jj += 4) {
 #pragma unroll
@@ -616,15 +632,16 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         if (m == 0 && (u & 1)) {
           const bool lok_e = (livep >> sbl_e) & 1u, lok_o = (livep >> sbl_o) & 1u;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? (COL ? vrow[COL ? q : 0] : ((q & 1) ? vr_o : vr_e)) : kOob;
+          for (int q = 0; q < 8; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? vrow[q] : kOob;
         }
         if (m == 1 && (u & 1)) {
           __builtin_amdgcn_sched_barrier(0);
           // grouped: only the scale load of u = 0 follows the pair's loads
-          // before the barrier of u = 1, none before that of u = 3
-          if (!GROUP) wait_vm<2 * kSlot>();
-          else if (u == 1) wait_vm<1>();
-          else wait_vm<0>();
+          // before the barrier of u = 1, none before that of u = 3; column
+          // mode: plus the previous step's kPrefetch prefetches
+          if (!GROUP) wait_vm<2 * kSlot + (COL ? kPrefetch : 0)>();
+          else if (u == 1) wait_vm<1 + (COL ? kPrefetch : 0)>();
+          else wait_vm<COL ? kPrefetch : 0>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -641,6 +658,21 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           if (m == 2) { MXW_DMA(0, u); MXW_DMA(1, u); }
           if (m == 3) { MXW_DMA(2, u); MXW_DMA(3, u); }
           if (m >= 4) MXW_DMA(m, u);
+        }
+        if (COL && !(u & 1) && (m == 4 || m == 6 || m == 8 || m == 10)) {
+          // prefetch slot k: row group pfa + k pfsa of A (k = 0, 1), pfb + (k - 2) pfsb
+          // of B (k = 2, 3), of pair s / 2 + 3; always issued (an unused slot
+          // is out of range) so the load count per step is fixed
+          int sq = s;
+          asm volatile("" : "+s"(sq));
+          const int pp = (sq >> 1) + 3;
+          const int k = (m - 4) >> 1;
+          const int q = k < 2 ? pfa + (k & 1) * pfsa : pfb + (k & 1) * pfsb;
+          const bool ok = 2 * pp < s0 + nsteps && q < 8 && (pp + 1) * kPair <= M;
+          // the row group goes into the range-checked (VGPR) offset, the
+          // token offset (inside the row) into the scalar one
+          const uint32_t rq = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)q * 8u * (uint32_t)M : kOob);
+          dma4s(k < 2 ? rA : rB, pfdst, vrow[0] + rq, __builtin_amdgcn_readfirstlane(ok ? (uint32_t)(pp * kPair) : 0u));
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
         if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
