@@ -492,23 +492,31 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // 128-byte row segments (one cache line per row, so every memory request
   // carries a full line).  Step j + 1's fragments and scale words are read into
   // register set (j + 1) % 2 during step j, so step j's MFMAs never wait on
-  // LDS.  Each step has one barrier (after its first two MFMAs); at odd steps
-  // it also certifies that the next pair has landed and that every wave has
-  // read the current pair, whose stage then takes the pair after next.
+  // LDS.  Odd steps have one barrier (after their first two MFMAs): it
+  // certifies that the next pair has landed and that every wave has read the
+  // current pair, whose stage then takes the pair after next (loaded during
+  // this step and the next).
   const int s0 = (start / kPair) * 2;
   const int s_end = (end + kStep - 1) / kStep;
   const int nsteps = (s_end - s0 + 3) & ~3;  // a multiple of 4: the loop body is unrolled by 4
 
-  // Odd steps issue the 16 loads of the pair after next, then the scale
-  // loads (paired: kScaleDma per step; grouped: one per 4-step iteration, at
-  // its first step).  At the barrier of odd step j the pair issued at step
-  // j - 2 must have landed: only the scale loads issued since may be in
-  // flight.
+  // The 16 loads of a pair go out in two parts: kOddLoads at the odd step
+  // whose barrier freed its stage (two steps ahead of its use), the rest in
+  // the first MFMA slots of the next (even) step.  Spreading them keeps the
+  // address unit below its full rate (one 1 KiB load per ~16 clk per CU,
+  // that is one per MFMA from each of the 4 waves), so load issue does not
+  // hold up the MFMAs, while the even step's part still lands well before
+  // the next odd barrier.  Then the scale loads (paired: kScaleDma per step;
+  // grouped: one per 4-step iteration, at its first step) and, in column
+  // mode, the even step's prefetches.  At the barrier of odd step j the pair
+  // issued at steps j - 2 and j - 1 must have landed: only the loads issued
+  // after step j - 1's data loads may still be in flight.
   constexpr int kSlot = kScaleDma;
+  constexpr int kOddLoads = 10;
 
-  // Prologue: the scale groups the first steps need, pairs s0/2 and s0/2 + 1,
-  // and (paired) one dummy scale slot so the first odd barrier sees the usual
-  // count.
+  // Prologue: the scale groups the first steps need, pair s0/2, the odd-step
+  // part of pair s0/2 + 1 (the first step issues the rest), and (paired) one
+  // dummy scale slot.
   const int qs = start >> 5, qn = (end - start) >> 5;
   {
     const int G0 = s0 / kGroupSteps;
@@ -526,10 +534,10 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #pragma unroll
     for (int i = 0; i < kDataDma; ++i) dma_pair(i, 0, P0, l0);
 #pragma unroll
-    for (int i = 0; i < kDataDma; ++i) dma_pair(i, 1, P0 + 1, l1);
+    for (int i = 0; i < kOddLoads; ++i) dma_pair(i, 1, P0 + 1, l1);
     if (!GROUP) dma_scales(0, false);
   }
-  wait_vm<GROUP ? kDataDma : kDataDma + kSlot>();  // scales and pair s0/2 landed (this wave)
+  wait_vm<GROUP ? kOddLoads : kOddLoads + kSlot>();  // scales and pair s0/2 landed (this wave)
   __syncthreads();
 
   // Scale registers.  In lane l the MFMA takes the E8M0 byte of row l % 32 and
@@ -600,15 +608,30 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 
   // per-step scalars of the first step; later steps compute theirs one step ahead
   uint32_t livep = live_mask_pair((s0 >> 1) + 2, qs, qn);  // pair issued at the next odd step
+  // per row group: the lane's load offset in the pair being issued, or out of
+  // range for a dead sub-block (set at odd steps, used again by the next
+  // even step; the first even step issues the rest of pair s0/2 + 1)
+  uint32_t va[8];
+  {
+    const uint32_t l1 = live_mask_pair((s0 >> 1) + 1, qs, qn);
+    const bool lok_e = (l1 >> sbl_e) & 1u, lok_o = (l1 >> sbl_o) & 1u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? vrow[q] : kOob;
+  }
   int sgrp = s0 / kGroupSteps + kAhead;
   bool sreal = false;  // s0 never issues a real scale load
 
-#define MXW_DMA(I, U)                                                                                        \
-  do {                                                                                                       \
-    const int q_ = (((I) >> 1) + rot) & 7;                                                                   \
-    dma16(((I) & 1) ? rB : rA, dbase + (uint32_t)((((U) >> 1) * 2 + ((I) & 1)) * kOpBytes + q_ * 1024), \
-          va[(I) >> 1], soffp);                                                                              \
-  } while (0)
+// load D of a pair's 16 (operand D % 2, row group D / 2): odd step U issues
+// the pair after next into stage U / 2, even step U the same pair into stage
+// (U / 2 + 1) % 2
+#define MXW_DMA_ODD(D, U)                                                                                    \
+  dma16(((D) & 1) ? rB : rA,                                                                                 \
+        dbase + (uint32_t)((((U) >> 1) * 2 + ((D) & 1)) * kOpBytes + (((((D) >> 1) + rot) & 7) * 1024)), \
+        va[(D) >> 1], soffp)
+#define MXW_DMA_EVEN(D, U)                                                                                         \
+  dma16(((D) & 1) ? rB : rA,                                                                                       \
+        dbase + (uint32_t)((((((U) >> 1) + 1) & 1) * 2 + ((D) & 1)) * kOpBytes + (((((D) >> 1) + rot) & 7) * 1024)), \
+        va[(D) >> 1], soffb)
   for (int jj = 0;; jj += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -622,8 +645,13 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       __builtin_amdgcn_sched_barrier(0);
       wait_lgkm_all();  // this step's fragments and words are in registers
       __builtin_amdgcn_sched_barrier(0);
-      uint32_t va[8];
-      uint32_t soffp = 0;
+      uint32_t soffp = 0;  // odd step: token offset of the pair after next
+      uint32_t soffb = 0;  // even step: of the next pair
+      if (!(u & 1)) {
+        int sb = s;
+        asm volatile("" : "+s"(sb));
+        soffb = (uint32_t)(((sb >> 1) + 1) * kPair);
+      }
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int i = m >> 2, t = m & 3;  // B block i, A block t
@@ -636,10 +664,10 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         }
         if (m == 1 && (u & 1)) {
           __builtin_amdgcn_sched_barrier(0);
-          // grouped: only the scale load of u = 0 follows the pair's loads
-          // before the barrier of u = 1, none before that of u = 3; column
-          // mode: plus the previous step's kPrefetch prefetches
-          if (!GROUP) wait_vm<2 * kSlot + (COL ? kPrefetch : 0)>();
+          // after the previous (even) step's data loads: its scale loads
+          // (paired: kSlot; grouped: one at u = 0) and, in column mode, its
+          // kPrefetch prefetches
+          if (!GROUP) wait_vm<kSlot + (COL ? kPrefetch : 0)>();
           else if (u == 1) wait_vm<1 + (COL ? kPrefetch : 0)>();
           else wait_vm<COL ? kPrefetch : 0>();
           __builtin_amdgcn_s_barrier();
@@ -650,23 +678,23 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           asm volatile("" : "+s"(sp));
           soffp = (uint32_t)(((sp >> 1) + 2) * kPair);
         }
-        if (u & 1) {
-          // one load per MFMA (two at the first two slots): the 4 waves then
-          // present about one 1 KiB load per 16 clocks, the rate at which the
-          // vector memory path of a CU takes them; denser bursts stall issue
-          // and with it the MFMAs queued behind
-          if (m == 2) { MXW_DMA(0, u); MXW_DMA(1, u); }
-          if (m == 3) { MXW_DMA(2, u); MXW_DMA(3, u); }
-          if (m >= 4) MXW_DMA(m, u);
+        {
+          // odd step: loads 0 .. 9 after the MFMAs m = 2, 3, 5, 6, 8, 9, 11, 12,
+          // 14, 15; even step: loads 10 .. 15 after m = 0 .. 5
+          constexpr int odd_load[16] = {-1, -1, 0, 1, -1, 2, 3, -1, 4, 5, -1, 6, 7, -1, 8, 9};
+          constexpr int even_load[16] = {10, 11, 12, 13, 14, 15, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+          static_assert(odd_load[15] == kOddLoads - 1 && even_load[0] == kOddLoads, "load split");
+          if ((u & 1) && odd_load[m] >= 0) MXW_DMA_ODD(odd_load[m], u);
+          if (!(u & 1) && even_load[m] >= 0) MXW_DMA_EVEN(even_load[m], u);
         }
-        if (COL && !(u & 1) && (m == 4 || m == 6 || m == 8 || m == 10)) {
+        if (COL && !(u & 1) && m >= 8 && m < 12) {
           // prefetch slot k: row group pfa + k pfsa of A (k = 0, 1), pfb + (k - 2) pfsb
           // of B (k = 2, 3), of pair s / 2 + 3; always issued (an unused slot
           // is out of range) so the load count per step is fixed
           int sq = s;
           asm volatile("" : "+s"(sq));
           const int pp = (sq >> 1) + 3;
-          const int k = (m - 4) >> 1;
+          const int k = m - 8;
           const int q = k < 2 ? pfa + (k & 1) * pfsa : pfb + (k & 1) * pfsb;
           const bool ok = 2 * pp < s0 + nsteps && q < 8 && (pp + 1) * kPair <= M;
           // the row group goes into the range-checked (VGPR) offset, the
@@ -708,7 +736,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     }
     if (jj + 4 >= nsteps) break;
   }
-#undef MXW_DMA
+#undef MXW_DMA_ODD
+#undef MXW_DMA_EVEN
   wait_vm_all();  // no LDS-direct load may outlive the workgroup
 
   // ---- column mode: regions cut between columns ------------------------------
