@@ -17,6 +17,12 @@ Grouped GEMM on MI355X", section 1; ROCm blog "Group-GEMM in XLA", section
     dW[g][n][k] = sum_{m in [start_g, end_g)} e4m3(A[n][m]) 2^(sA[n][m/32]-127)
                                              * e4m3(B[k][m]) 2^(sB[k][m/32]-127)
 
+It also holds the row-ragged grouped GEMM of the same layer (forward and data
+gradient; blog section 1, XLA blog "non-contracting" ragged dot):
+
+    out[m][n] = sum_{c < C} e4m3(X[m][c]) 2^(sX[m][c/32]-127)
+                          * e4m3(W[g][n][c]) 2^(sW[g][n][c/32]-127),  m in [start_g, end_g)
+
 Pins (all in ``tests/test_oracle_*.py``): every E4M3 and E8M0 code against the
 format definition; a hand-computed two-expert case; exact rational brute force
 on tiny random problems; the invariants (empty expert, scale-exponent doubling,
@@ -70,6 +76,9 @@ def _load():
     lib.mxw_oracle_decode_plane.argtypes = [P, P, I, I64, I64, P]
     lib.mxw_oracle_wgrad_f64.argtypes = [P, P, P, P, P, I, I64, I, I, P]
     lib.mxw_oracle_wgrad_points.argtypes = [P, P, P, P, P, I, I64, I, I, P, P, P, I64, P]
+    lib.mxw_oracle_rows_contract_f64.argtypes = [P, P, P, P, I, I64, I, I, P]
+    lib.mxw_oracle_rows_f64.argtypes = [P, P, P, P, P, I, I64, I, I, P]
+    lib.mxw_oracle_rows_points.argtypes = [P, P, P, P, P, I, I64, I, I, P, P, I64, P]
     lib.mxw_oracle_bf16_rne.restype = ctypes.c_uint16
     lib.mxw_oracle_bf16_rne.argtypes = [ctypes.c_double]
     lib.mxw_oracle_to_bf16.argtypes = [P, I64, P]
@@ -177,6 +186,62 @@ def wgrad_points(A, sA, B, sB, offs, g, n, k):
     out = np.empty(g.shape[0], np.float64)
     _check(_load().mxw_oracle_wgrad_points(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(offs), offs.shape[0], M, N, K,
                                            _ptr(g), _ptr(n), _ptr(k), g.shape[0], _ptr(out)))
+    return out
+
+
+def rows_contract_f64(Xd, Wd, start, end):
+    """Row-ragged core on decoded fp64 operands Xd [M, C], Wd [E, Nw, C] ->
+    [M, Nw]; rows outside every window are NaN."""
+    Xd = np.ascontiguousarray(Xd, dtype=np.float64)
+    Wd = np.ascontiguousarray(Wd, dtype=np.float64)
+    start = np.ascontiguousarray(start, dtype=np.int64)
+    end = np.ascontiguousarray(end, dtype=np.int64)
+    M, C = Xd.shape
+    E, Nw, C2 = Wd.shape
+    if C2 != C or start.shape != (E,) or end.shape != (E,):
+        raise ValueError("shape mismatch")
+    out = np.full((M, Nw), np.nan)
+    _check(_load().mxw_oracle_rows_contract_f64(_ptr(Xd), _ptr(Wd), _ptr(start), _ptr(end), E, M, C, Nw, _ptr(out)))
+    return out
+
+
+def rows_f64(X, sX, W, sW, offs):
+    """Row-ragged grouped GEMM of MXFP8 operands X [M, C] (scales [M, C/32])
+    and W [E, Nw, C] (scales [E, Nw, C/32]) -> fp64 [M, Nw]; rows past
+    offs[E-1] are NaN (not part of any expert)."""
+    X = _u8(X)
+    M, C = X.shape
+    W = _u8(W)
+    E, Nw, C2 = W.shape
+    if C2 != C:
+        raise ValueError("X and W disagree on C")
+    sX = _u8(sX, (M, C // 32))
+    sW = _u8(sW, (E, Nw, C // 32))
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    if offs.shape != (E,):
+        raise ValueError("offs must have one entry per expert")
+    out = np.full((M, Nw), np.nan)
+    _check(_load().mxw_oracle_rows_f64(_ptr(X), _ptr(sX), _ptr(W), _ptr(sW), _ptr(offs), E, M, C, Nw, _ptr(out)))
+    return out
+
+
+def rows_points(X, sX, W, sW, offs, m, n):
+    """out[m[i], n[i]] of the row-ragged GEMM in fp64, straight from the
+    definition (NaN for a row past the last expert)."""
+    X = _u8(X)
+    M, C = X.shape
+    W = _u8(W)
+    E, Nw, _ = W.shape
+    sX = _u8(sX, (M, C // 32))
+    sW = _u8(sW, (E, Nw, C // 32))
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    m = np.ascontiguousarray(m, dtype=np.int64)
+    n = np.ascontiguousarray(n, dtype=np.int32)
+    if m.shape != n.shape or m.ndim != 1:
+        raise ValueError("point index arrays must be 1-D and of equal length")
+    out = np.empty(m.shape[0], np.float64)
+    _check(_load().mxw_oracle_rows_points(_ptr(X), _ptr(sX), _ptr(W), _ptr(sW), _ptr(offs), E, M, C, Nw, _ptr(m),
+                                          _ptr(n), m.shape[0], _ptr(out)))
     return out
 
 

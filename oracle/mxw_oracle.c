@@ -222,6 +222,126 @@ int mxw_oracle_wgrad_points(const uint8_t* A, const uint8_t* sA, const uint8_t* 
 }
 
 /*
+ * Row-ragged grouped GEMM: the forward and data-gradient GEMMs of the same
+ * MoE layer (blog section 1: the weight gradient is one of three grouped
+ * GEMMs per expert layer, the other two keep the contraction over the fixed
+ * hidden dimension and carry the raggedness in their rows; XLA blog, the
+ * "non-contracting" ragged dot and its forward / data-gradient classes).
+ * For every expert g, every row m in [start_g, end_g) and every n < Nw:
+ *
+ *   out[m][n] = sum over c in [0, C) of
+ *               dec(X[m][c], sX[m][c/32]) * dec(W[g][n][c], sW[g][n][c/32])
+ *
+ * X is [M, C] and W is [E, Nw, C], both contraction-contiguous (MXFP8
+ * carries its 32-element blocks along the contraction axis, so both operands
+ * are stored with it innermost), scale planes sX [M, C/32] and sW
+ * [E, Nw, C/32].  offs[g] is the cumulative END of expert g's rows; rows
+ * past offs[E-1] belong to no expert and are not written.  This first level
+ * works on already-decoded fp64 operands Xd [M, C] and Wd [E, Nw, C]
+ * (ascending c; no alignment requirement, so the XLA blog's decimal example
+ * can be fed to it directly).
+ */
+int mxw_oracle_rows_contract_f64(const double* Xd, const double* Wd, const int64_t* start, const int64_t* end,
+                                 int E, int64_t M, int C, int Nw, double* out) {
+  if (!Xd || !Wd || !start || !end || !out) return MXWO_ERR_NULL;
+  if (E < 1 || M < 0 || C < 1 || Nw < 1) return MXWO_ERR_DIM;
+  for (int g = 0; g < E; ++g)
+    if (start[g] < 0 || end[g] < start[g] || end[g] > M || (g > 0 && start[g] != end[g - 1])) return MXWO_ERR_OFFS;
+  for (int g = 0; g < E; ++g) {
+    const double* wg = Wd + (int64_t)g * Nw * C;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t m = start[g]; m < end[g]; ++m) {
+      const double* xrow = Xd + m * C;
+      double* orow = out + m * Nw;
+      for (int n = 0; n < Nw; ++n) {
+        const double* wrow = wg + (int64_t)n * C;
+        double acc = 0.0;
+        for (int c = 0; c < C; ++c) acc += xrow[c] * wrow[c];
+        orow[n] = acc;
+      }
+    }
+  }
+  return MXWO_OK;
+}
+
+/* The full row-ragged GEMM from MXFP8 operands: validate, decode, contract.
+ * out is fp64 [M, Nw]; rows past offs[E-1] are left as the caller set them. */
+int mxw_oracle_rows_f64(const uint8_t* X, const uint8_t* sX, const uint8_t* W, const uint8_t* sW,
+                        const int32_t* offs, int E, int64_t M, int C, int Nw, double* out) {
+  if (!X || !sX || !W || !sW || !offs || !out) return MXWO_ERR_NULL;
+  if (E < 1 || M < 0 || C < 32 || (C % 32) != 0 || Nw < 1) return MXWO_ERR_DIM;
+  int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  int64_t* end = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  double* Xd = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * (size_t)C);
+  double* Wd = (double*)malloc(sizeof(double) * (size_t)E * (size_t)Nw * (size_t)C);
+  int rc = MXWO_OK;
+  if (!start || !end || !Xd || !Wd) {
+    rc = MXWO_ERR_NOMEM;
+    goto done;
+  }
+  rc = mxw_oracle_windows(offs, E, M, 1, start, end);
+  if (rc) goto done;
+  /* rows past the last expert are decoded as zeros (never read as values) */
+  rc = mxw_oracle_decode_plane(X, sX, (int)end[E - 1], C, C, Xd);
+  if (rc) goto done;
+  rc = mxw_oracle_decode_plane(W, sW, E * Nw, C, C, Wd);
+  if (rc) goto done;
+  rc = mxw_oracle_rows_contract_f64(Xd, Wd, start, end, E, M, C, Nw, out);
+done:
+  free(start);
+  free(end);
+  free(Xd);
+  free(Wd);
+  return rc;
+}
+
+/* Selected outputs of the row-ragged GEMM, each straight from the
+ * definition: (pm[i], pn[i]) -> out[i]; a row past offs[E-1] gives NaN. */
+int mxw_oracle_rows_points(const uint8_t* X, const uint8_t* sX, const uint8_t* W, const uint8_t* sW,
+                           const int32_t* offs, int E, int64_t M, int C, int Nw, const int64_t* pm,
+                           const int32_t* pn, int64_t npts, double* out) {
+  if (!X || !sX || !W || !sW || !offs || !pm || !pn || !out) return MXWO_ERR_NULL;
+  if (E < 1 || M < 0 || C < 32 || (C % 32) != 0 || Nw < 1 || npts < 0) return MXWO_ERR_DIM;
+  int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  int64_t* end = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  if (!start || !end) {
+    free(start);
+    free(end);
+    return MXWO_ERR_NOMEM;
+  }
+  int rc = mxw_oracle_windows(offs, E, M, 1, start, end);
+  for (int64_t i = 0; rc == MXWO_OK && i < npts; ++i)
+    if (pm[i] < 0 || pm[i] >= M || pn[i] < 0 || pn[i] >= Nw) rc = MXWO_ERR_DIM;
+  if (rc == MXWO_OK) {
+    const int64_t nb = C / 32;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < npts; ++i) {
+      int g = -1;
+      for (int h = 0; h < E; ++h)
+        if (start[h] <= pm[i] && pm[i] < end[h]) g = h;
+      if (g < 0) {
+        out[i] = NAN;
+        continue;
+      }
+      const uint8_t* xrow = X + pm[i] * C;
+      const uint8_t* sxrow = sX + pm[i] * nb;
+      const uint8_t* wrow = W + ((int64_t)g * Nw + pn[i]) * C;
+      const uint8_t* swrow = sW + ((int64_t)g * Nw + pn[i]) * nb;
+      double acc = 0.0;
+      for (int c = 0; c < C; ++c) {
+        double a = mxw_oracle_e4m3(xrow[c]) * mxw_oracle_e8m0(sxrow[c / 32]);
+        double b = mxw_oracle_e4m3(wrow[c]) * mxw_oracle_e8m0(swrow[c / 32]);
+        acc += a * b;
+      }
+      out[i] = acc;
+    }
+  }
+  free(start);
+  free(end);
+  return rc;
+}
+
+/*
  * Round a binary64 value to bfloat16 (1 sign, 8 exponent, 7 mantissa bits),
  * round-to-nearest, ties-to-even, in one step from the exact fp64 value
  * (no intermediate fp32).  The blog's epilogue narrows to bf16 with
