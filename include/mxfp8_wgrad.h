@@ -39,7 +39,7 @@ extern "C" {
 /* Return codes. */
 #define MXW_OK 0
 #define MXW_ERR_NULL (-1)   /* a required pointer is NULL */
-#define MXW_ERR_DIM (-2)    /* E, M, N or K outside the supported range */
+#define MXW_ERR_DIM (-2)    /* a size outside the supported range */
 #define MXW_ERR_ALIGN (-3)  /* A, B or out not 16-byte aligned */
 #define MXW_ERR_DEVICE (-4) /* current device is not gfx950, or no device */
 #define MXW_ERR_LAUNCH (-5) /* the kernel launch failed (hipGetLastError), or the
@@ -48,6 +48,7 @@ extern "C" {
 /* Supported ranges (checked on the host, no device access). */
 #define MXW_MAX_EXPERTS 256
 #define MXW_MAX_TOKENS (8 * 1024 * 1024)
+#define MXW_MAX_ROWS (8 * 1024 * 1024)
 
 /*
  * mxfp8_wgrad_grouped -- the weight-gradient grouped GEMM above.
@@ -119,6 +120,65 @@ int64_t mxw_grid_size(int E, int N, int K);
  * no gfx950 device.
  */
 int mxw_columns(int E, int M, int N, int K);
+
+/*
+ * mxfp8_grouped_fwd -- the row-ragged MXFP8 grouped GEMM: the forward and
+ * data-gradient GEMMs of the same MoE layer.  (Blog section 1: the weight
+ * gradient is one of three grouped GEMMs per expert layer; the other two keep
+ * the contraction over the fixed hidden dimension and carry the raggedness
+ * in their rows.  XLA blog: the "non-contracting" ragged dot and its forward
+ * and data-gradient classes.)  For every expert g, every row m in
+ * [start_g, end_g) (start_0 = 0, start_g = offs[g-1], end_g = offs[g]) and
+ * every n < N:
+ *
+ *   out[m][n] = sum over c in [0, C) of
+ *               e4m3(A[m][c]) 2^(sA[m][c/32] - 127) * e4m3(B[g][n][c]) 2^(sB[g][n][c/32] - 127)
+ *
+ * accumulated in FP32 and rounded to bf16 (round to nearest even).  Forward:
+ * A = the routed tokens' activations (C = the layer's input width), B = the
+ * expert weights.  Data gradient: A = the output gradient, B = the weights
+ * quantized along their other axis.  MXFP8 puts its 32-element blocks along
+ * the contraction axis, so both operands are stored with C innermost.
+ *
+ * Arguments (caller-owned DEVICE memory on the current HIP device):
+ *   A     uint8  [R, C]       E4M3 codes, row stride C bytes.
+ *   sA    uint8  [R, C/32]    E8M0 scales of A.
+ *   B     uint8  [E, N, C]    E4M3 codes of each expert's [N, C] operand.
+ *   sB    uint8  [E, N, C/32] E8M0 scales of B.
+ *   offs  int32  [E]          cumulative end of each expert's run of rows.
+ *   E     1 <= E <= MXW_MAX_EXPERTS.
+ *   R     rows of A and out, 0 <= R <= MXW_MAX_ROWS.
+ *   C     contraction length, 32 <= C <= 65536, C % 32 == 0.
+ *   N     output columns, 16 <= N <= 65536, N % 16 == 0.
+ *   out   bf16 bit patterns [R, N], row-major.
+ *   stream  a hipStream_t (NULL = the default stream), passed as void*.
+ *
+ * Host-checked preconditions return an error code and launch nothing:
+ * non-NULL pointers; A, B and out 16-byte aligned; the ranges above; a
+ * gfx950 device.  Device-data preconditions (never read on the host): offs
+ * non-decreasing and offs[E-1] <= R; row boundaries need no alignment.
+ * Rows in [offs[E-1], R) belong to no expert: they are neither read as
+ * values nor written.  Malformed offs give unspecified values but no
+ * out-of-bounds access (windows are clamped to [0, R], loads range-checked,
+ * stores confined to the clamped windows).
+ *
+ * Effects: enqueues one kernel on `stream`; allocates nothing, keeps no
+ * state, never writes its inputs.  Each output element is one workgroup's
+ * fixed-order sum: bitwise reproducible run to run.
+ *
+ * Returns MXW_OK or a negative MXW_ERR_* code.
+ */
+int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                      const int32_t* offs, int E, int R, int C, int N, uint16_t* out, void* stream);
+
+/*
+ * mxw_fwd_grid_size -- the workgroups mxfp8_grouped_fwd launches for
+ * (E, R, N): (R / 256 + E) * ceil(N / 256) work items at most (each expert
+ * adds at most one partial 256-row tile), rounded up to a multiple of 8.
+ * Workgroups past the actual number of work items exit at once.  Returns 0
+ * for invalid sizes.
+ */
+int64_t mxw_fwd_grid_size(int E, int R, int N);
 
 /* mxw_strerror -- a static, human-readable message for a return code. */
 const char* mxw_strerror(int code);

@@ -1,6 +1,7 @@
-"""MI355X-native MXFP8 ragged weight-gradient grouped GEMM.
+"""MI355X-native MXFP8 ragged grouped GEMMs.
 
     out = wgrad(A, sA, B, sB, offs)        # bf16 [E, N, K]
+    out = fwd(A, sA, B, sB, offs)          # bf16 [R, N]
 
 computes, for every expert g (blog "Ragged MXFP8 Weight Gradients: A FlyDSL
 Grouped GEMM on MI355X", section 1),
@@ -8,7 +9,13 @@ Grouped GEMM on MI355X", section 1),
     dW[g] = dY[g]^T X[g]   over expert g's tokens [offs[g-1], offs[g])
 
 from MXFP8 operands A = dY^T [N, M] and B = X^T [K, M] (E4M3 codes, token axis
-contiguous) with E8M0 scale planes sA [N, M/32] and sB [K, M/32].  Everything
+contiguous) with E8M0 scale planes sA [N, M/32] and sB [K, M/32]; and the
+row-ragged GEMM of the same layer (forward and data gradient):
+
+    out[m] = A[m] B[g]^T   for the rows m of expert g, contraction over C
+
+from A [R, C] and B [E, N, C] (contraction innermost, 32-element E8M0 blocks
+along it).  Everything
 runs in the HIP library ``lib/libmxfp8_wgrad.so`` (C ABI in
 ``include/mxfp8_wgrad.h``); this module only checks tensor metadata and passes
 device pointers and the current stream.  There is no fallback: if the library
@@ -21,8 +28,8 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "columns", "strerror", "version", "library_path",
-           "MxwError"]
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "columns", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
+           "strerror", "version", "library_path", "MxwError"]
 
 _lib = None
 
@@ -54,6 +61,10 @@ def _load():
     lib.mxw_version.argtypes = []
     lib.mxw_columns.restype = I
     lib.mxw_columns.argtypes = [I, I, I, I]
+    lib.mxfp8_grouped_fwd.restype = I
+    lib.mxfp8_grouped_fwd.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
+    lib.mxw_fwd_grid_size.restype = ctypes.c_int64
+    lib.mxw_fwd_grid_size.argtypes = [I, I, I]
     _lib = lib
     return lib
 
@@ -133,4 +144,58 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None):
                                  E, M, N, K, out.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise MxwError("mxfp8_wgrad_grouped failed (%d): %s" % (rc, strerror(rc)))
+    return out
+
+
+def fwd_grid_size(E, R, N):
+    return int(_load().mxw_fwd_grid_size(int(E), int(R), int(N)))
+
+
+def mxfp8_grouped_fwd(A, sA, B, sB, offs, E, R, C, N, out, stream=0):
+    """Raw C-ABI call on device addresses (ints).  Returns the status code."""
+    lib = _load()
+    return lib.mxfp8_grouped_fwd(A, sA, B, sB, offs, int(E), int(R), int(C), int(N), out, stream)
+
+
+def fwd(A, sA, B, sB, offs, out=None, stream=None):
+    """Row-ragged grouped GEMM, bf16 [R, N]: out[m] = A[m] . B[g]^T for the
+    rows m of expert g (forward: A = activations, B = weights; data gradient:
+    A = output gradient, B = the weights quantized along the other axis).
+
+    A: [R, C] uint8/float8_e4m3fn, sA: [R, C/32] uint8, B: [E, N, C],
+    sB: [E, N, C/32], offs: [E] int32 cumulative row ends, all contiguous on
+    one GPU.  Rows past offs[E-1] are not written (a new `out` leaves them
+    uninitialised).  Runs on `stream` (default: the current stream) and does
+    not synchronise.
+    """
+    A = _as_u8(A, "A")
+    B = _as_u8(B, "B")
+    sA = _as_u8(sA, "sA")
+    sB = _as_u8(sB, "sB")
+    if A.dim() != 2 or sA.dim() != 2 or B.dim() != 3 or sB.dim() != 3 or offs.dim() != 1:
+        raise ValueError("A, sA must be 2-D, B, sB 3-D and offs 1-D")
+    R, C = A.shape
+    E, N, C2 = B.shape
+    if C2 != C or sA.shape != (R, C // 32) or sB.shape != (E, N, C // 32) or offs.shape[0] != E:
+        raise ValueError("shape mismatch: A %s sA %s B %s sB %s offs %s" % (
+            tuple(A.shape), tuple(sA.shape), tuple(B.shape), tuple(sB.shape), tuple(offs.shape)))
+    if offs.dtype != torch.int32:
+        raise TypeError("offs must be int32")
+    dev = A.device
+    for name, t in (("A", A), ("sA", sA), ("B", B), ("sB", sB), ("offs", offs)):
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("%s must be on the same GPU as A" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (R, N) or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bf16 [R, N] tensor on the same device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = mxfp8_grouped_fwd(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
+                               E, R, C, N, out.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise MxwError("mxfp8_grouped_fwd failed (%d): %s" % (rc, strerror(rc)))
     return out

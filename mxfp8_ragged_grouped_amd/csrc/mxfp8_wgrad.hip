@@ -281,7 +281,10 @@ struct Params {
   const uint8_t* sB;
   const int32_t* offs;
   uint16_t* out;
+  // weight gradient: A [N, M], B [K, M], out [E, N, K] (contraction M);
+  // row-ragged GEMM: A [R, M], B [E, N, M], out [R, N] (contraction M, K unused)
   int E, M, N, K;
+  int R;  // row-ragged GEMM: rows of A and out
   int tilesN, tilesK;
   // XCD regions (0 = off): each expert's tilesN x tilesK grid is cut into 8
   // rectangles of regN x regK tiles, regB of them across the K direction;
@@ -345,14 +348,19 @@ __device__ __forceinline__ void zero_tile(const Params& p, int g, int tn, int tk
   }
 }
 
-// One tile piece: tokens [start, end) of expert g into tile (tn, tk).
+// One tile piece: contraction [start, end) of expert g into tile (tn, tk).
+// Row-ragged GEMM: tile (tn = row tile, tk = column tile) of rows
+// [ar0, ar0 + ra) of A, all of expert g.
 struct Piece {
   int g, tn, tk, start, end;
   int role;  // 0: whole tile; 1, 2: a piece of a region cut between columns (2: its first)
   int col, member, Q, ra_lin, r_it;  // column mode: position, column quota, the region's place and length
+  int ar0, ra;                       // row-ragged GEMM: first row of A and rows in the tile
 };
 
-template <bool GROUP, bool COL>
+// ROWS: the row-ragged GEMM (out rows = A rows of one expert, out columns =
+// that expert's B rows); otherwise the weight gradient.
+template <bool GROUP, bool COL, bool ROWS>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
   int tid = threadIdx.x;
   // opaque per piece: nothing derived from the thread index is hoisted out of
@@ -363,21 +371,40 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   const int M = p.M, N = p.N, K = p.K;
   const int g = pc.g, start = pc.start, end = pc.end, role = pc.role;
   const int col = pc.col, member = pc.member, Q = pc.Q, ra_lin = pc.ra_lin, r_it = pc.r_it;
-  const int n0 = pc.tn * kTile, k0 = pc.tk * kTile;
-  uint16_t* outg = p.out + (size_t)g * N * K;
+  // the tile: rows [arow, arow + rowsA) of A, [brow, brow + rowsB) of B, and
+  // its place in out (row stride ldo)
+  size_t arow, brow;
+  int rowsA, rowsB, ldo;
+  uint16_t* otile;
+  if constexpr (ROWS) {
+    const int c0 = pc.tk * kTile;
+    arow = (size_t)pc.ar0;
+    rowsA = pc.ra;
+    brow = (size_t)g * N + c0;
+    rowsB = min(kTile, N - c0);
+    ldo = N;
+    otile = p.out + arow * N + c0;
+  } else {
+    const int n0 = pc.tn * kTile, k0 = pc.tk * kTile;
+    arow = (size_t)n0;
+    rowsA = min(kTile, N - n0);
+    brow = (size_t)k0;
+    rowsB = min(kTile, K - k0);
+    ldo = K;
+    otile = p.out + (size_t)g * N * K + (size_t)n0 * K + k0;
+  }
 
   // ---- buffer resources, rebased to this tile's 256-row bands ----------------
-  const int rowsA = min(kTile, N - n0), rowsB = min(kTile, K - k0);
   const uint32_t sbytes = (uint32_t)M >> 5;  // scale bytes per row
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (size_t)n0 * M, (uint32_t)rowsA * (uint32_t)M);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + (size_t)k0 * M, (uint32_t)rowsB * (uint32_t)M);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + arow * M, (uint32_t)rowsA * (uint32_t)M);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + brow * M, (uint32_t)rowsB * (uint32_t)M);
   // scale planes are read as whole dwords; rounding the range up to 4 bytes
   // keeps every dword entirely inside or outside it (bytes past the plane
   // belong to tokens >= M, which are always masked)
   const __amdgpu_buffer_rsrc_t rsA =
-      make_rsrc(p.sA + (size_t)n0 * sbytes, ((uint32_t)rowsA * sbytes + 3u) & ~3u);
+      make_rsrc(p.sA + arow * sbytes, ((uint32_t)rowsA * sbytes + 3u) & ~3u);
   const __amdgpu_buffer_rsrc_t rsB =
-      make_rsrc(p.sB + (size_t)k0 * sbytes, ((uint32_t)rowsB * sbytes + 3u) & ~3u);
+      make_rsrc(p.sB + brow * sbytes, ((uint32_t)rowsB * sbytes + 3u) & ~3u);
 
   // ---- per-lane DMA geometry -------------------------------------------------
   // Data: a stage holds a pair of K-steps (128 tokens, one cache line per row).
@@ -860,7 +887,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           *(uint2*)(ep + nl * 256 + ((c ^ (nl & 15)) << 4) + ((fq ^ (nl >> 4)) & 1) * 8) = w;
         }
     const int rsub = lane >> 4, cl = lane & 15;
-    const int kk = k0 + wk * 128 + cl * 8;
+    const int kk = wk * 128 + cl * 8;  // within the tile
     // 8 reads in flight before their stores (one read, wait, store at a time
     // left the wave waiting on the LDS 32 times)
 #pragma unroll
@@ -877,8 +904,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       for (int x = 0; x < 8; ++x) {
         const int nl = 4 * (x0 + x) + rsub;
         if ((nl >> 4) & 1) d[x] = (v4i){d[x].z, d[x].w, d[x].x, d[x].y};  // a constant after unrolling
-        const int n = n0 + wn * 128 + nl;
-        if (n < N && kk < K) *(v4i*)(outg + (size_t)n * K + kk) = d[x];
+        const int n = wn * 128 + nl;
+        if (n < rowsA && kk < rowsB) *(v4i*)(otile + (size_t)n * ldo + kk) = d[x];
       }
     }
   }
@@ -1032,7 +1059,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       zero_tile(p, pc.g, pc.tn, pc.tk);
       return;
     }
-    run_piece<GROUP, false>(p, sm, pc);
+    run_piece<GROUP, false, false>(p, sm, pc);
   } else {
     // ---- column mode: the pieces of this column, in sequence order -------------
     for (;;) {
@@ -1068,9 +1095,78 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       // LDS reads are done in every wave before new loads land
       wait_vm_all();
       __syncthreads();
-      run_piece<GROUP, true>(p, sm, pc);
+      run_piece<GROUP, true, false>(p, sm, pc);
     }
   }
+}
+
+// Row-ragged grouped GEMM (the forward and data-gradient GEMMs of the layer):
+// out[m][n] = sum_c A[m][c] B[g][n][c] for the rows m of expert g.  Expert
+// g's rows [start_g, end_g) are cut into 256-row tiles (the last one
+// partial), never crossing into another expert; work item t = (row tile,
+// column tile) in expert order, column tile fastest.  XCD x (blocks x,
+// x + 8, ...) takes a contiguous range of work items, so the column tiles of
+// a row tile (sharing its A rows) and the row tiles of an expert (sharing its
+// B) meet in one L2.  The grid is sized on the host for the most row tiles
+// any offs can give (R / 256 + E); blocks past the actual count exit.
+template <bool GROUP>
+__global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int E = p.E, R = p.R;
+  const int bid = blockIdx.x;
+  // ---- row windows from offs (clamped to [0, R], monotone) and the exclusive
+  // prefix of their row-tile counts (wave 0 scan) ------------------------------
+  if (tid < E) {
+    int e = min(max(p.offs[tid], 0), R);
+    const int st = tid ? min(max(p.offs[tid - 1], 0), R) : 0;
+    if (e < st) e = st;
+    sm.start[tid] = st;
+    sm.len[tid] = e - st;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int carry = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      const int nt = e < E ? (sm.len[e] + kTile - 1) / kTile : 0;
+      int sc = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int x = __shfl_up(sc, d);
+        if (lane >= d) sc += x;
+      }
+      if (e < E) sm.pre[e] = carry + sc - nt;
+      carry += __shfl(sc, 63);
+    }
+    if (lane == 0) sm.cnt[0] = carry;
+  }
+  __syncthreads();
+  const int tiles = __builtin_amdgcn_readfirstlane(sm.cnt[0]) * p.tilesN;
+  const int per = (tiles + 7) >> 3;  // work items per XCD
+  const int t = (bid & 7) * per + (bid >> 3);
+  if ((bid >> 3) >= per || t >= tiles) return;
+  const int mt = t / p.tilesN, nt = t - mt * p.tilesN;
+  // the expert whose row tiles hold mt: the last non-empty one starting at or before it
+  int g = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const bool hit = e < E && sm.len[e] > 0 && sm.pre[e] <= mt;
+    const uint64_t bal = __ballot(hit);
+    if (bal) g = base + 63 - (int)__builtin_clzll(bal);
+  }
+  g = __builtin_amdgcn_readfirstlane(g);
+  Piece pc = {};
+  pc.g = g;
+  pc.tn = mt;
+  pc.tk = nt;
+  pc.start = 0;
+  pc.end = p.M;
+  pc.ar0 = __builtin_amdgcn_readfirstlane(sm.start[g]) + (mt - __builtin_amdgcn_readfirstlane(sm.pre[g])) * kTile;
+  pc.ra = min(kTile, __builtin_amdgcn_readfirstlane(sm.start[g]) + __builtin_amdgcn_readfirstlane(sm.len[g]) - pc.ar0);
+  __syncthreads();  // the scan's LDS words are not reused below, but keep the waves together
+  run_piece<GROUP, false, true>(p, sm, pc);
 }
 
 struct DeviceInfo {
@@ -1240,11 +1336,50 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
   return MXW_OK;
 }
 
+int64_t mxw_fwd_grid_size(int E, int R, int N) {
+  if (E < 1 || E > MXW_MAX_EXPERTS || R < 0 || R > MXW_MAX_ROWS || N < 16) return 0;
+  const int64_t items = ((int64_t)R / kTile + E) * ((N + kTile - 1) / kTile);
+  return ((items + 7) / 8) * 8;
+}
+
+int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                      const int32_t* offs, int E, int R, int C, int N, uint16_t* out, void* stream) {
+  if (!A || !sA || !B || !sB || !offs || !out) return MXW_ERR_NULL;
+  if (E < 1 || E > MXW_MAX_EXPERTS || R < 0 || R > MXW_MAX_ROWS || C < 32 || (C & 31) || C > 65536 || N < 16 ||
+      (N & 15) || N > 65536)
+    return MXW_ERR_DIM;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
+  const int64_t grid = mxw_fwd_grid_size(E, R, N);
+  if (grid <= 0 || grid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
+  int rc = check_device();
+  if (rc) return rc;
+  Params p = {};
+  p.A = A;
+  p.sA = sA;
+  p.B = B;
+  p.sB = sB;
+  p.offs = offs;
+  p.out = out;
+  p.E = E;
+  p.M = C;  // the contraction length (and row stride of A and B)
+  p.N = N;
+  p.K = 0;
+  p.R = R;
+  p.tilesN = (N + kTile - 1) / kTile;
+  p.tilesK = 0;
+  if ((C & 511) == 0)
+    hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
+  return MXW_OK;
+}
+
 const char* mxw_strerror(int code) {
   switch (code) {
     case MXW_OK: return "ok";
     case MXW_ERR_NULL: return "a required pointer is NULL";
-    case MXW_ERR_DIM: return "E, M, N or K outside the supported range";
+    case MXW_ERR_DIM: return "a size (E, M, N, K, R or C) outside the supported range";
     case MXW_ERR_ALIGN: return "A, B or out is not 16-byte aligned";
     case MXW_ERR_DEVICE: return "the current device is not gfx950 (or no device)";
     case MXW_ERR_LAUNCH: return "kernel launch failed";
@@ -1252,6 +1387,6 @@ const char* mxw_strerror(int code) {
   }
 }
 
-int mxw_version(void) { return 200; }
+int mxw_version(void) { return 300; }
 
 }  // extern "C"

@@ -30,7 +30,8 @@ def test_library_built():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxw_strerror", "mxw_version"}
+    assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
+                          "mxw_fwd_grid_size", "mxw_strerror", "mxw_version"}
     lib = ctypes.CDLL(mxw.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -104,3 +105,47 @@ def test_columns_host_checks():
     assert lib.mxw_columns(257, 8192, 256, 256) == -2
     assert lib.mxw_columns(4, -32, 256, 256) == -2
     assert lib.mxw_columns(4, 8192, 8, 256) == -2
+
+
+def test_fwd_grid_size():
+    # (R / 256 + E) row tiles at most, times the column tiles, rounded up to 8
+    assert mxw.fwd_grid_size(4, 512, 128) == 8          # (2 + 4) * 1 -> 8
+    assert mxw.fwd_grid_size(8, 196608, 1408) == (768 + 8) * 6
+    assert mxw.fwd_grid_size(32, 262144, 7168) == (1024 + 32) * 28
+    assert mxw.fwd_grid_size(1, 0, 256) == 8
+    assert mxw.fwd_grid_size(0, 512, 128) == 0
+    assert mxw.fwd_grid_size(4, -1, 128) == 0
+    assert mxw.fwd_grid_size(4, 512, 8) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, P, P, P, P, 4, 512, 256, 128, P), -1),            # NULL A
+    ((P, P, P, 0, P, 4, 512, 256, 128, P), -1),            # NULL sB
+    ((P, P, P, P, P, 0, 512, 256, 128, P), -2),            # E = 0
+    ((P, P, P, P, P, 257, 512, 256, 128, P), -2),          # E too large
+    ((P, P, P, P, P, 4, -1, 256, 128, P), -2),             # R < 0
+    ((P, P, P, P, P, 4, 512, 48, 128, P), -2),             # C % 32 != 0
+    ((P, P, P, P, P, 4, 512, 0, 128, P), -2),              # C = 0
+    ((P, P, P, P, P, 4, 512, 256, 120, P), -2),            # N % 16 != 0
+    ((P, P, P, P, P, 4, 512, 256, 131072, P), -2),         # N too large
+    ((P, P, P + 8, P, P, 4, 512, 256, 128, P), -3),        # B misaligned
+    ((P, P, P, P, P, 4, 512, 256, 128, P + 2), -3),        # out misaligned
+])
+def test_fwd_host_argument_checks(args, code):
+    assert mxw.mxfp8_grouped_fwd(*args) == code
+
+
+def test_fwd_python_face_validates_shapes():
+    import torch
+    A = torch.zeros((512, 256), dtype=torch.uint8)
+    sA = torch.zeros((512, 8), dtype=torch.uint8)
+    B = torch.zeros((4, 128, 256), dtype=torch.uint8)
+    sB = torch.zeros((4, 128, 7), dtype=torch.uint8)
+    offs = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mxw.fwd(A, sA, B, sB, offs)            # sB has the wrong shape
+    sB = torch.zeros((4, 128, 8), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mxw.fwd(A, sA, B, sB, offs[:3])        # one offs entry per expert
+    with pytest.raises(ValueError):
+        mxw.fwd(A, sA, B, sB, offs)            # CPU tensors are refused: no host fallback

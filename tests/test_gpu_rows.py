@@ -1,0 +1,150 @@
+"""GPU parity of the row-ragged grouped GEMM (forward / data gradient) against
+the CPU oracle (needs an MI355X).
+
+Each case NaN-poisons the output, runs the C-ABI library through the Python
+binding, and compares every row that belongs to an expert with the oracle to
+the same tolerance as the weight gradient; rows past the last expert must keep
+their poison (they are never written).  Small cases cover the whole output;
+the full-size workloads (the benchmark's launch configuration) are checked on
+seeded sample points plus the edges of partial tiles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_ragged_grouped_amd as mxw
+import oracle
+import workloads as W
+from helpers import BF16_NAN, bf16_bits, check_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print("[gpu-case] " + msg, flush=True)
+
+
+def run_rows(cfg):
+    out = torch.empty((cfg["R"], cfg["N"]), dtype=torch.bfloat16, device=cfg["A"].device)
+    out.view(torch.int16).fill_(BF16_NAN)
+    mxw.fwd(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    torch.cuda.synchronize()
+    return bf16_bits(out)
+
+
+def host_rows(cfg):
+    return tuple(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs"))
+
+
+def full_compare_rows(cfg, what):
+    say("%s: launch E=%d R=%d C=%d N=%d" % (what, cfg["E"], cfg["R"], cfg["C"], cfg["N"]))
+    bits = run_rows(cfg)
+    ref = oracle.rows_f64(*host_rows(cfg))
+    used = int(np.asarray(cfg["sizes"]).sum())
+    stats = check_close(bits[:used], ref[:used], what=what)
+    assert (bits[used:] == BF16_NAN).all(), "%s: a row past the last expert was written" % what
+    return bits, ref, stats
+
+
+ROWS_CASES = [
+    # E, R, C, N, sizes (sum <= R; rows after them are padding)
+    (3, 700, 256, 272, [300, 0, 290]),          # unaligned row boundaries, empty expert, partial N tile, padding
+    (1, 16, 32, 16, [16]),                      # the smallest problem
+    (4, 1100, 160, 512, [1, 255, 257, 513]),    # C % 128 != 0 (paired scale path), 1-row and tile-straddling experts
+    (2, 600, 512, 256, [512, 88]),              # C % 512 == 0 (grouped scale path)
+    (5, 1024, 1408, 336, [200, 0, 0, 600, 224]),  # the 16B down-projection width as C
+    (6, 520, 2048, 1408, [100, 32, 0, 200, 96, 64]),  # 16B gate/up widths
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROWS_CASES)))
+def test_rows_ragged_shapes(case):
+    E, R, C, N, sizes = ROWS_CASES[case]
+    cfg = W.make_rows(E, R, C, N, sizes, seed=800 + case, device=DEV)
+    bits, ref, stats = full_compare_rows(cfg, "rows case %d" % case)
+    print("rows case %d max_rel %.3e" % (case, stats["max_rel"]))
+
+
+def test_rows_bitwise_repeat():
+    cfg = W.make_rows(4, 1100, 160, 512, [1, 255, 257, 513], seed=810, device=DEV)
+    say("rows repeat: launch twice")
+    a = run_rows(cfg)
+    b = run_rows(cfg)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rows_exact_regime_bitwise():
+    """Codes in {0, +-.5, +-1, +-1.5, +-2} and scale bytes 126..128 keep every
+    partial sum exact in FP32: the bf16 output equals the oracle rounded once."""
+    rng = np.random.default_rng(820)
+    E, R, C, N = 3, 600, 512, 272
+    codes = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x3C, 0xBC, 0x40, 0xC0], np.uint8)
+    A = rng.choice(codes, (R, C))
+    B = rng.choice(codes, (E, N, C))
+    sA = rng.integers(126, 129, (R, C // 32)).astype(np.uint8)
+    sB = rng.integers(126, 129, (E, N, C // 32)).astype(np.uint8)
+    sizes = np.array([257, 0, 300])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    cfg = dict(E=E, R=R, C=C, N=N, A=t(A), sA=t(sA), B=t(B), sB=t(sB),
+               offs=t(np.cumsum(sizes).astype(np.int32)), sizes=sizes)
+    say("rows exact regime: launch")
+    bits = run_rows(cfg)
+    ref = oracle.rows_f64(A, sA, B, sB, np.cumsum(sizes).astype(np.int32))
+    used = int(sizes.sum())
+    np.testing.assert_array_equal(bits[:used], oracle.to_bf16_bits(ref[:used]))
+
+
+def test_rows_padding_garbage_ignored():
+    cfg = W.make_rows(3, 700, 256, 272, [300, 0, 290], seed=830, device=DEV)
+    say("rows padding garbage: two launches")
+    base = run_rows(cfg)
+    used = int(np.asarray(cfg["sizes"]).sum())
+    cfg["A"][used:] = 0x7F   # NaN codes
+    cfg["sA"][used:] = 0xFF  # NaN scales
+    np.testing.assert_array_equal(run_rows(cfg), base)
+
+
+def test_rows_all_experts_empty():
+    cfg = W.make_rows(4, 256, 256, 256, [0, 0, 0, 0], seed=840, device=DEV)
+    say("rows all empty: launch")
+    assert (run_rows(cfg) == BF16_NAN).all()
+
+
+def sample_rows(cfg, n_rand=2048, seed=0):
+    """Seeded (row, column) points: random rows of every expert plus the first
+    and last rows of every expert and of every 256-row tile, against the edge
+    columns of the last partial column tile."""
+    rng = np.random.default_rng(seed)
+    offs = cfg["offs"].cpu().numpy().astype(np.int64)
+    starts = np.concatenate([[0], offs[:-1]])
+    N = cfg["N"]
+    rows, cols = [], []
+    edge_cols = sorted({0, 1, 7, 8, 127, 128, 255, N - 1, N - 8, N - 129, (N // 256) * 256 % N})
+    edge_cols = [c for c in edge_cols if 0 <= c < N]
+    for s, e in zip(starts, offs):
+        if e <= s:
+            continue
+        r = rng.integers(s, e, n_rand // len(offs))
+        rows += r.tolist()
+        cols += rng.integers(0, N, r.shape[0]).tolist()
+        for t0 in range(int(s), int(e), 256):
+            for rr in {t0, min(t0 + 255, int(e) - 1)}:
+                rows += [rr] * len(edge_cols)
+                cols += edge_cols
+    return np.array(rows, np.int64), np.array(cols, np.int32)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["16b_fwd", "16b_fwd_down"])
+def test_rows_full_size_sampled(name):
+    cfg = W.make_rows_config(name, device=DEV)
+    say("%s: launch R=%d C=%d N=%d (sampled check)" % (name, cfg["R"], cfg["C"], cfg["N"]))
+    bits = run_rows(cfg)
+    m, n = sample_rows(cfg, seed=5)
+    ref = oracle.rows_points(*host_rows(cfg), m, n)
+    used = int(np.asarray(cfg["sizes"]).sum())
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    check_close(bits[m, n], ref, rms=rms, what=name)
+    assert (bits[used:] == BF16_NAN).all()

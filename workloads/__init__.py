@@ -304,3 +304,56 @@ def algorithmic_bytes(cfg):
     mu = float(np.asarray(cfg["sizes"]).sum())
     N, K, E = cfg["N"], cfg["K"], cfg["E"]
     return mu * (N + K) * (1.0 + 1.0 / 32.0) + 2.0 * E * N * K + 4.0 * E
+
+
+# --------------------------------------------------------------------------
+# Row-ragged grouped GEMM (forward / data gradient of the same layer)
+# --------------------------------------------------------------------------
+# (base routing, C = contraction, N = output columns): the forward gate/up
+# GEMM of a workload contracts over its K (hidden) and produces N columns,
+# the forward down GEMM contracts over N and produces K.
+ROWS_CONFIGS = {
+    "16b_fwd": dict(base="16b_24k", C="K", N="N"),
+    "16b_fwd_down": dict(base="16b_24k", C="N", N="K"),
+    "16b_1k_fwd": dict(base="16b_1k", C="K", N="N"),
+    "671b_fwd": dict(base="671b_gateup", C="K", N="N"),
+}
+
+
+def make_rows(E, R, C, N, sizes, seed, device="cpu", mode="normal", std=(1.0, 1.0)):
+    """A row-ragged problem: A [R, C] and B [E, N, C] quantised along C,
+    offs from `sizes` (any row counts, sum <= R)."""
+    sizes = np.asarray(sizes, np.int64)
+    if sizes.shape != (E,) or sizes.sum() > R:
+        raise ValueError("sizes must be [E] with sum <= R")
+    A, sA = make_operand(R, C, mode, std[0], seed, device)
+    B, sB = make_operand(E * N, C, mode, std[1], seed + 1, device)
+    return dict(name="custom_rows", E=E, R=R, C=C, N=N, A=A, sA=sA, B=B.reshape(E, N, C),
+                sB=sB.reshape(E, N, C // 32), offs=torch.from_numpy(offs_from_sizes(sizes)).to(device),
+                sizes=sizes, value_seed=seed)
+
+
+def make_rows_config(name, device="cpu", seed=None):
+    """A named row-ragged workload: the routing of its base workload, rows =
+    that workload's tokens."""
+    rc = ROWS_CONFIGS[name]
+    c = CONFIGS[rc["base"]]
+    sizes, rseed = routing_sizes(rc["base"])
+    vseed = 1000 * c["cid"] + 777 if seed is None else int(seed)
+    mode, std = ("wide", (1.0, 1.0)) if c["values"] == "wide" else ("normal", c["values"])
+    cfg = make_rows(c["E"], c["M"], c[rc["C"]], c[rc["N"]], sizes, vseed, device, mode, std)
+    cfg.update(name=name, routing_seed=rseed)
+    return cfg
+
+
+def rows_useful_flops(cfg):
+    """2 * rows_used * C * N (rows past the last expert excluded)."""
+    return 2.0 * float(np.asarray(cfg["sizes"]).sum()) * cfg["C"] * cfg["N"]
+
+
+def rows_algorithmic_bytes(cfg):
+    """Each routed row's C codes + C/32 scales read once, each expert's
+    [N, C] operand + scales read once, the bf16 rows written once, offs."""
+    mu = float(np.asarray(cfg["sizes"]).sum())
+    C, N, E = cfg["C"], cfg["N"], cfg["E"]
+    return mu * C * (1.0 + 1.0 / 32.0) + E * N * C * (1.0 + 1.0 / 32.0) + 2.0 * mu * N + 4.0 * E
