@@ -17,6 +17,11 @@ HBM traffic measured by rocprofv3 counters (when the committed counter
 summary matches this kernel source), and the CPU oracle timed on the host
 cores on a bounded sample of the same workload.
 
+The row-ragged grouped GEMM of the same layer (forward / data gradient,
+mxfp8_grouped_fwd) is measured the same way with --workload 16b_fwd,
+16b_fwd_down, 16b_1k_fwd or 671b_fwd (rows = the base workload's routed
+tokens; useful work 2 * rows * C * N).
+
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
     --copy-calibration   run a plain 1 GiB device copy (counter calibration)
@@ -99,6 +104,85 @@ def cpu_baseline(cfg, A, sA, B, sB, offs, budget_s=25.0):
                                                 cfg["N"], cfg["K"], int(used), dt)}
 
 
+def cpu_baseline_rows(cfg, A, sA, B, sB, offs, budget_s=20.0):
+    """Time the oracle on seeded sample points of the row-ragged GEMM (each a
+    full C-term dot product); a 2,000-point probe sizes the sample to about
+    budget_s."""
+    import oracle
+
+    used = int(np.sum(cfg["sizes"]))
+    rng = np.random.default_rng(11)
+
+    def run(npts):
+        m = rng.integers(0, used, npts)
+        n = rng.integers(0, cfg["N"], npts).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.rows_points(A, sA, B, sB, offs, m, n)
+        return time.perf_counter() - t0
+
+    t_probe = run(2000)
+    npts = int(max(2000, min(4_000_000, 2000 * budget_s / max(t_probe, 1e-6))))
+    dt = run(npts)
+    return {"value": 2.0 * cfg["C"] * npts / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "%s: %d seeded (row, column) outputs of %d x %d, each a %d-term fp64 dot "
+                                        "product, %.1f s" % (cfg["name"], npts, used, cfg["N"], cfg["C"], dt)}
+
+
+def bench_rows(args):
+    import torch
+
+    import mxfp8_ragged_grouped_amd as mxw
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.make_rows_config(args.workload, device=dev)
+    E, R, C, N = cfg["E"], cfg["R"], cfg["C"], cfg["N"]
+    out = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mxw.fwd(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=stream)
+
+    ms, wall = time_steps(step, args, stream)
+    tflops = W.rows_useful_flops(cfg) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "MXFP8 row-ragged grouped GEMM TFLOP/s (2·rows·C·N), forward / data gradient",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8(e4m3,e8m0/32)->fp32acc->bf16",
+        "data": "synthetic (seeded routing of the base workload, N(0,1) values, MXFP8-quantised along C)",
+        "config": {"workload": args.workload, "E": E, "R": R, "C": C, "N": N,
+                   "rows_used": int(np.sum(cfg["sizes"])), "routing_seed": cfg["routing_seed"],
+                   "value_seed": cfg["value_seed"], "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": None},
+        "hbm_gbps_algorithmic": round(W.rows_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_rows(cfg, *(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
+    print(json.dumps(res))
+
+
+def time_steps(step, args, stream):
+    """W untimed steps, then K timed ones between HIP events on `stream`."""
+    import torch
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +208,10 @@ def main():
     import mxfp8_ragged_grouped_amd as mxw
     import workloads as W
 
+    if args.workload in W.ROWS_CONFIGS:
+        bench_rows(args)
+        return
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = W.make_config(args.workload, device=dev)
@@ -134,19 +222,7 @@ def main():
     def step():
         mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / args.steps
+    ms, wall = time_steps(step, args, stream)
 
     flops = W.useful_flops(cfg)
     tflops = flops / (ms * 1e-3) / 1e12
