@@ -23,6 +23,10 @@ gradient; blog section 1, XLA blog "non-contracting" ragged dot):
     out[m][n] = sum_{c < C} e4m3(X[m][c]) 2^(sX[m][c/32]-127)
                           * e4m3(W[g][n][c]) 2^(sW[g][n][c/32]-127),  m in [start_g, end_g)
 
+and the token-axis MXFP8 quantiser that produces the weight gradient's operands
+(scale byte clamp(floor(log2 amax) - 8 + 127, 0, 254), E4M3 round-to-nearest-even
+with saturation, transposed to token-contiguous).
+
 Pins (all in ``tests/test_oracle_*.py``): every E4M3 and E8M0 code against the
 format definition; a hand-computed two-expert case; exact rational brute force
 on tiny random problems; the invariants (empty expert, scale-exponent doubling,
@@ -79,6 +83,7 @@ def _load():
     lib.mxw_oracle_rows_contract_f64.argtypes = [P, P, P, P, I, I64, I, I, P]
     lib.mxw_oracle_rows_f64.argtypes = [P, P, P, P, P, I, I64, I, I, P]
     lib.mxw_oracle_rows_points.argtypes = [P, P, P, P, P, I, I64, I, I, P, P, I64, P]
+    lib.mxw_oracle_quantize_tokens.argtypes = [P, I64, I, I64, P, P]
     lib.mxw_oracle_bf16_rne.restype = ctypes.c_uint16
     lib.mxw_oracle_bf16_rne.argtypes = [ctypes.c_double]
     lib.mxw_oracle_to_bf16.argtypes = [P, I64, P]
@@ -243,6 +248,19 @@ def rows_points(X, sX, W, sW, offs, m, n):
     _check(_load().mxw_oracle_rows_points(_ptr(X), _ptr(sX), _ptr(W), _ptr(sW), _ptr(offs), E, M, C, Nw, _ptr(m),
                                           _ptr(n), m.shape[0], _ptr(out)))
     return out
+
+
+def quantize_tokens(x_bits, used=None):
+    """Token-axis MXFP8 quantiser: bf16 bit patterns x [M, H] (uint16) ->
+    (codes q [H, M], scales s [H, M/32]); tokens at or past `used` (default
+    M) give code 0 and count as 0 in their block's amax."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, H = x_bits.shape
+    used = M if used is None else int(used)
+    q = np.empty((H, M), np.uint8)
+    s = np.empty((H, M // 32), np.uint8)
+    _check(_load().mxw_oracle_quantize_tokens(_ptr(x_bits), M, H, used, _ptr(q), _ptr(s)))
+    return q, s
 
 
 def to_bf16_bits(x):

@@ -342,6 +342,84 @@ int mxw_oracle_rows_points(const uint8_t* X, const uint8_t* sX, const uint8_t* W
 }
 
 /*
+ * Token-axis MXFP8 quantiser (the step that produces the weight gradient's
+ * operands; blog section 1: both operands are quantised along the token
+ * axis, token-contiguous, one E8M0 scale per 32 tokens; the blog excludes
+ * this step from its timing, section 7).  From bf16 x [M, H] (tokens x
+ * hidden, hidden contiguous) to codes q [H, M] and scales s [H, M/32]:
+ *
+ *   amax   = max |x[m][h]| over the block's 32 tokens (tokens at or past
+ *            `used` count as 0: they belong to no expert)
+ *   s      = clamp(floor(log2 amax) - 8 + 127, 0, 254), and 127 when amax = 0
+ *            (8 = floor(log2 448), the largest E4M3 power of two)
+ *   q[h][m] = E4M3FN(x[m][h] / 2^(s - 127)), round to nearest, ties to the
+ *            even code, saturated to +-448; 0 for a token at or past `used`
+ *
+ * (OCP MX definition of the shared scale; the reading and its basis are in
+ * the notes: scale exponent = floor(log2 amax) - emax of the element type,
+ * saturating conversion.)  floor(log2) is taken exactly from frexp.  The
+ * rounding is done on the exact binary64 value by searching the E4M3 grid.
+ */
+static unsigned mxwo_e4m3_rne(double y) {
+  /* nearest of the 127 non-negative finite codes 0x00..0x7E to |y|; ties to
+   * the even code (the one whose mantissa LSB is 0) */
+  double a = fabs(y);
+  unsigned best = 0;
+  double bd = a;
+  for (unsigned c = 1; c <= 0x7E; ++c) {
+    double d = fabs(mxw_oracle_e4m3(c) - a);
+    if (d < bd || (d == bd && (c & 1u) == 0 && (best & 1u) != 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  if (a > 448.0) best = 0x7E; /* saturate */
+  if (best != 0 && y < 0) best |= 0x80u;
+  return best;
+}
+
+int mxw_oracle_quantize_tokens(const uint16_t* x, int64_t M, int H, int64_t used, uint8_t* q, uint8_t* s) {
+  if (!x || !q || !s) return MXWO_ERR_NULL;
+  if (M < 0 || (M % 32) != 0 || H < 1 || used < 0 || used > M) return MXWO_ERR_DIM;
+  const int64_t nb = M / 32;
+#pragma omp parallel for schedule(static)
+  for (int h = 0; h < H; ++h) {
+    for (int64_t b = 0; b < nb; ++b) {
+      double v[32];
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const int64_t m = b * 32 + i;
+        double xv = 0.0;
+        if (m < used) {
+          uint32_t bits = (uint32_t)x[m * H + h] << 16;
+          float f;
+          memcpy(&f, &bits, 4);
+          xv = (double)f;
+        }
+        v[i] = xv;
+        if (fabs(xv) > amax) amax = fabs(xv);
+      }
+      int sb;
+      if (amax == 0.0) {
+        sb = 127;
+      } else {
+        int e2;
+        frexp(amax, &e2); /* amax = f 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+        sb = (e2 - 1) - 8 + 127;
+        if (sb < 0) sb = 0;
+        if (sb > 254) sb = 254;
+      }
+      s[(int64_t)h * nb + b] = (uint8_t)sb;
+      for (int i = 0; i < 32; ++i) {
+        const int64_t m = b * 32 + i;
+        q[(int64_t)h * M + m] = m < used ? (uint8_t)mxwo_e4m3_rne(ldexp(v[i], 127 - sb)) : 0;
+      }
+    }
+  }
+  return MXWO_OK;
+}
+
+/*
  * Round a binary64 value to bfloat16 (1 sign, 8 exponent, 7 mantissa bits),
  * round-to-nearest, ties-to-even, in one step from the exact fp64 value
  * (no intermediate fp32).  The blog's epilogue narrows to bf16 with
