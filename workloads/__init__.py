@@ -192,6 +192,14 @@ def mx_scale_bytes(amax):
     return b.to(torch.uint8)
 
 
+def pow2(k):
+    """2**k as float64, exactly, for integer tensors k in [-1022, 1023]: built
+    from the exponent field.  (torch.ldexp and torch.pow(2, k) round on some
+    devices: on the GPU they are not exact for integer k.)"""
+    k = k.to(torch.int64)
+    return ((k + 1023) << 52).view(torch.float64)
+
+
 def e4m3_encode_rne(y):
     """Encode float64 values (already within +-448) to OCP E4M3FN codes,
     round-half-even.  Returns uint8 codes."""
@@ -199,14 +207,14 @@ def e4m3_encode_rne(y):
     _, ex = torch.frexp(a)
     fl = ex.to(torch.int64) - 1  # floor(log2 a) for a > 0
     qexp = torch.where(fl < -6, torch.full_like(fl, -9), fl - 3)  # grid spacing exponent
-    q = torch.round(torch.ldexp(a, -qexp.to(torch.float64)))  # half-to-even
-    v = torch.ldexp(q, qexp.to(torch.float64))  # representable magnitude
+    q = torch.round(a * pow2(-qexp))  # half-to-even
+    v = q * pow2(qexp)  # representable magnitude
     # code from the exact value
     sub = v < 2.0 ** -6
-    code_sub = torch.ldexp(v, torch.full_like(v, 9.0)).to(torch.int64)
+    code_sub = (v * 512.0).to(torch.int64)
     _, ev = torch.frexp(torch.where(sub, torch.ones_like(v), v))
     e_field = ev.to(torch.int64) - 1 + 7
-    mant = (torch.ldexp(v, (-(ev.to(torch.int64) - 1)).to(torch.float64)) * 8.0 - 8.0).to(torch.int64)
+    mant = (v * pow2(-(ev.to(torch.int64) - 1)) * 8.0 - 8.0).to(torch.int64)
     code_norm = (e_field << 3) | mant
     code = torch.where(sub, code_sub, code_norm)
     code = torch.where(y < 0, code | 0x80, code)
@@ -223,7 +231,7 @@ def quantize_rows(x):
     xb = x.to(torch.float64).reshape(rows, M // 32, 32)
     amax = xb.abs().amax(dim=-1)
     sb = mx_scale_bytes(amax)
-    y = torch.ldexp(xb, (127 - sb.to(torch.int64)).to(torch.float64).unsqueeze(-1))
+    y = xb * pow2(127 - sb.to(torch.int64)).unsqueeze(-1)
     y = torch.clamp(y, -448.0, 448.0)
     codes = e4m3_encode_rne(y).reshape(rows, M)
     return codes, sb
