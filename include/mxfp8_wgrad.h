@@ -180,6 +180,46 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
  */
 int64_t mxw_fwd_grid_size(int E, int R, int N);
 
+/*
+ * mxfp8_quantize_tokens -- the token-axis MXFP8 quantiser that produces the
+ * weight gradient's operands (blog section 1: both operands are quantised
+ * along the token axis and handed over token-contiguous, with one E8M0
+ * scale per 32 tokens; the blog times its operator without this step,
+ * section 7).  From bf16 x [M, H] (tokens x hidden, hidden contiguous) to
+ * E4M3 codes q [H, M] and E8M0 scales s [H, M/32]; for every hidden column
+ * h and 32-token block b:
+ *
+ *   amax    = max |x[m][h]| over the block's tokens below `used`
+ *   s[h][b] = clamp(floor(log2 amax) - 8 + 127, 0, 254), 127 if amax == 0
+ *   q[h][m] = E4M3FN(x[m][h] / 2^(s[h][b] - 127)): round to nearest, ties to
+ *             the even code, saturated to +-448, zero encoded as +0; 0 for
+ *             m >= used
+ *
+ * (8 = floor(log2 448), the largest E4M3 binade: the OCP MX shared scale.)
+ * Call it on dY for A and on X for B.  `used` is offs[E-1] read on the
+ * device (tokens past the last expert become finite zeros, whatever x holds
+ * there), or M when offs is NULL.
+ *
+ * Arguments (caller-owned DEVICE memory on the current HIP device):
+ *   x     uint16 [M, H]    bf16 bit patterns.
+ *   offs  int32  [E]       cumulative expert ends (may be NULL: all tokens).
+ *   E     1 <= E <= MXW_MAX_EXPERTS when offs is not NULL.
+ *   M     0 <= M <= MXW_MAX_TOKENS, M % 32 == 0.
+ *   H     16 <= H <= 65536, H % 16 == 0.
+ *   q     uint8  [H, M]    codes, row stride M bytes.
+ *   s     uint8  [H, M/32] scales, row stride M/32 bytes.
+ *   stream  a hipStream_t, passed as void*.
+ *
+ * Host-checked preconditions return an error code and launch nothing:
+ * non-NULL x, q, s; x and q 16-byte aligned; the ranges above; a gfx950
+ * device.  Effects: one kernel on `stream`; allocates nothing; q and s are
+ * fully overwritten; the result depends only on x and `used`.
+ *
+ * Returns MXW_OK or a negative MXW_ERR_* code.
+ */
+int mxfp8_quantize_tokens(const uint16_t* x, const int32_t* offs, int E, int M, int H, uint8_t* q, uint8_t* s,
+                          void* stream);
+
 /* mxw_strerror -- a static, human-readable message for a return code. */
 const char* mxw_strerror(int code);
 

@@ -2,6 +2,7 @@
 
     out = wgrad(A, sA, B, sB, offs)        # bf16 [E, N, K]
     out = fwd(A, sA, B, sB, offs)          # bf16 [R, N]
+    q, s = quantize_tokens(x, offs)        # MXFP8 operand [H, M] from bf16 [M, H]
 
 computes, for every expert g (blog "Ragged MXFP8 Weight Gradients: A FlyDSL
 Grouped GEMM on MI355X", section 1),
@@ -15,7 +16,8 @@ row-ragged GEMM of the same layer (forward and data gradient):
     out[m] = A[m] B[g]^T   for the rows m of expert g, contraction over C
 
 from A [R, C] and B [E, N, C] (contraction innermost, 32-element E8M0 blocks
-along it).  Everything
+along it); and the token-axis quantiser that makes the weight gradient's
+operands from bf16 activations / gradients.  Everything
 runs in the HIP library ``lib/libmxfp8_wgrad.so`` (C ABI in
 ``include/mxfp8_wgrad.h``); this module only checks tensor metadata and passes
 device pointers and the current stream.  There is no fallback: if the library
@@ -29,7 +31,7 @@ import torch
 from .build import LIB as _LIB_PATH
 
 __all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "columns", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
-           "strerror", "version", "library_path", "MxwError"]
+           "quantize_tokens", "mxfp8_quantize_tokens", "strerror", "version", "library_path", "MxwError"]
 
 _lib = None
 
@@ -65,6 +67,8 @@ def _load():
     lib.mxfp8_grouped_fwd.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
     lib.mxw_fwd_grid_size.restype = ctypes.c_int64
     lib.mxw_fwd_grid_size.argtypes = [I, I, I]
+    lib.mxfp8_quantize_tokens.restype = I
+    lib.mxfp8_quantize_tokens.argtypes = [P, P, I, I, I, P, P, P]
     _lib = lib
     return lib
 
@@ -199,3 +203,39 @@ def fwd(A, sA, B, sB, offs, out=None, stream=None):
     if rc != 0:
         raise MxwError("mxfp8_grouped_fwd failed (%d): %s" % (rc, strerror(rc)))
     return out
+
+
+def mxfp8_quantize_tokens(x, offs, E, M, H, q, s, stream=0):
+    """Raw C-ABI call on device addresses (ints; offs may be 0).  Returns the status code."""
+    return _load().mxfp8_quantize_tokens(x, offs, int(E), int(M), int(H), q, s, stream)
+
+
+def quantize_tokens(x, offs=None, q=None, s=None, stream=None):
+    """Token-axis MXFP8 quantisation of bf16 x [M, H] -> (codes uint8 [H, M],
+    scales uint8 [H, M/32]), the weight gradient's operand layout.  Tokens at
+    or past offs[-1] (all tokens are used when offs is None) become code 0.
+    Runs on `stream` (default: the current stream) and does not synchronise."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("x must be a contiguous 2-D bf16 tensor on the GPU")
+    M, H = x.shape
+    dev = x.device
+    if offs is not None:
+        if offs.dtype != torch.int32 or offs.dim() != 1 or offs.device != dev or not offs.is_contiguous():
+            raise ValueError("offs must be a contiguous int32 vector on the same GPU")
+    if q is None:
+        q = torch.empty((H, M), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = torch.empty((H, M // 32), dtype=torch.uint8, device=dev)
+    if tuple(q.shape) != (H, M) or q.dtype != torch.uint8 or not q.is_contiguous() or q.device != dev:
+        raise ValueError("q must be a contiguous uint8 [H, M] tensor on the same GPU")
+    if tuple(s.shape) != (H, M // 32) or s.dtype != torch.uint8 or not s.is_contiguous() or s.device != dev:
+        raise ValueError("s must be a contiguous uint8 [H, M/32] tensor on the same GPU")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = mxfp8_quantize_tokens(x.data_ptr(), 0 if offs is None else offs.data_ptr(),
+                                   1 if offs is None else offs.shape[0], M, H, q.data_ptr(), s.data_ptr(),
+                                   stream.cuda_stream)
+    if rc != 0:
+        raise MxwError("mxfp8_quantize_tokens failed (%d): %s" % (rc, strerror(rc)))
+    return q, s

@@ -1169,6 +1169,104 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
   run_piece<GROUP, false, true>(p, sm, pc);
 }
 
+// ---- token-axis MXFP8 quantiser --------------------------------------------------
+// bf16 x [M, H] (tokens x hidden, hidden contiguous) -> E4M3 codes q [H, M]
+// (token-contiguous) and E8M0 scales s [H, M/32], the operand layout of the
+// weight gradient (blog section 1).  Per (hidden column h, 32-token block):
+// amax over the block (tokens at or past `used` count as 0 and get code 0),
+// scale byte clamp(floor(log2 amax) - 8 + 127, 0, 254) (127 for amax = 0),
+// codes = E4M3 round-to-nearest-even of x / 2^(byte - 127), saturated to
+// +-448, zero always encoded as +0.  HBM-bound: each element is read once
+// (2 bytes) and written once (1 byte plus 1/32 of a scale byte).
+//
+// A workgroup takes a tile of 128 tokens x 128 hidden: coalesced 16-byte
+// loads of the token rows (256 bytes each) into LDS; thread (h, b) reduces
+// and encodes hidden column h of blocks b and b + 2 straight from LDS (the 64
+// lanes of a wave read one 128-byte row segment at a time); the codes go back
+// through LDS as 128 hidden rows of 128 bytes, 16-byte chunk c of row r at
+// position c ^ ((r / 2) % 8) (the 16-byte writes of 16 lanes, rows r .. r+15
+// at one chunk, then hit 16 distinct bank groups), so that every global
+// store writes whole 128-byte lines of q.
+constexpr int kQTok = 128, kQHid = 128;
+struct QSmem {
+  uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (32 KiB)
+  uint8_t q[kQHid][kQTok];   // the codes, hidden rows, swizzled chunks (16 KiB)
+};
+
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
+                                                    int E, int M, int H, uint8_t* __restrict__ q,
+                                                    uint8_t* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) QSmem sm;
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * kQTok, h0 = blockIdx.y * kQHid;
+  int used = M;
+  if (offs) used = min(max(offs[E - 1], 0), M);
+  used = __builtin_amdgcn_readfirstlane(used);
+  // ---- load: chunk c = 256 k + tid is token row c / 16, hidden h0 + 8 (c % 16);
+  // rows at or past `used` are outside the descriptor's range and read as 0
+  {
+    const int rows = max(0, min(kQTok, used - m0));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)m0 * H, (uint32_t)rows * (uint32_t)H * 2u);
+    v4i v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = k * 256 + tid, r = c >> 4, h = h0 + (c & 15) * 8;
+      const uint32_t off = h < H ? ((uint32_t)r * (uint32_t)H + (uint32_t)h) * 2u : kOob;
+      v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = k * 256 + tid;
+      *(v4i*)&sm.x[c >> 4][(c & 15) * 8] = v[k];
+    }
+  }
+  __syncthreads();
+  // ---- encode: thread (h, b0) does column h of blocks b0 and b0 + 2 --------------
+  {
+    const int h = tid & 127, b0 = tid >> 7;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = b0 + 2 * bb;
+      float v[32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        v[i] = __builtin_bit_cast(float, (uint32_t)sm.x[b * 32 + i][h] << 16);
+        amax = fmaxf(amax, fabsf(v[i]));
+      }
+      // floor(log2 amax) = frexp exponent - 1 (exact, subnormals included)
+      int sb = amax == 0.0f ? 127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8 + 127;
+      sb = min(max(sb, 0), 254);
+      const int sh = 127 - sb;
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__builtin_ldexpf(v[4 * j + t], sh), -448.0f), 448.0f);
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+        // a code of magnitude 0 (including -0) becomes +0
+        const uint32_t z = (uint32_t)c & 0x7F7F7F7Fu;
+        const uint32_t nz = ((z + 0x7F7F7F7Fu) & 0x80808080u) >> 7;
+        w[j] = (uint32_t)c & (nz * 0xFFu);
+      }
+      const int sw = (h >> 1) & 7;
+      *(v4i*)&sm.q[h][((2 * b) ^ sw) * 16] = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *(v4i*)&sm.q[h][((2 * b + 1) ^ sw) * 16] = (v4i){(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+      if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(M >> 5) + (m0 >> 5) + b] = (uint8_t)sb;
+    }
+  }
+  __syncthreads();
+  // ---- store: chunk c = 256 k + tid is hidden row c / 8, tokens 16 (c % 8) .. +15
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = k * 256 + tid, r = c >> 3, c8 = c & 7;
+    const int h = h0 + r, m = m0 + c8 * 16;
+    if (h < H && m < M) *(v4i*)(q + (size_t)h * M + m) = *(const v4i*)&sm.q[r][(c8 ^ ((r >> 1) & 7)) * 16];
+  }
+}
+
 struct DeviceInfo {
   int checked;
   int ok;
@@ -1371,6 +1469,22 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
     hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   else
     hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
+  return MXW_OK;
+}
+
+int mxfp8_quantize_tokens(const uint16_t* x, const int32_t* offs, int E, int M, int H, uint8_t* q, uint8_t* s,
+                          void* stream) {
+  if (!x || !q || !s) return MXW_ERR_NULL;
+  if (M < 0 || M > MXW_MAX_TOKENS || (M & 31) || H < 16 || (H & 15) || H > 65536 ||
+      (offs && (E < 1 || E > MXW_MAX_EXPERTS)))
+    return MXW_ERR_DIM;
+  if (((uintptr_t)x | (uintptr_t)q) & 15) return MXW_ERR_ALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  if (M == 0) return MXW_OK;
+  const dim3 grid((unsigned)((M + kQTok - 1) / kQTok), (unsigned)((H + kQHid - 1) / kQHid));
+  hipLaunchKernelGGL(quant_kernel, grid, dim3(256), 0, (hipStream_t)stream, x, offs, E, M, H, q, s);
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
   return MXW_OK;
 }

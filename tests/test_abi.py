@@ -31,7 +31,7 @@ def test_library_built():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
-                          "mxw_fwd_grid_size", "mxw_strerror", "mxw_version"}
+                          "mxw_fwd_grid_size", "mxfp8_quantize_tokens", "mxw_strerror", "mxw_version"}
     lib = ctypes.CDLL(mxw.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -149,3 +149,28 @@ def test_fwd_python_face_validates_shapes():
         mxw.fwd(A, sA, B, sB, offs[:3])        # one offs entry per expert
     with pytest.raises(ValueError):
         mxw.fwd(A, sA, B, sB, offs)            # CPU tensors are refused: no host fallback
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, P, 4, 512, 128, P, P), -1),               # NULL x
+    ((P, P, 4, 512, 128, 0, P), -1),               # NULL q
+    ((P, P, 4, 512, 128, P, 0), -1),               # NULL s
+    ((P, P, 4, 500, 128, P, P), -2),               # M % 32 != 0
+    ((P, P, 4, -32, 128, P, P), -2),               # M < 0
+    ((P, P, 4, 512, 120, P, P), -2),               # H % 16 != 0
+    ((P, P, 4, 512, 8, P, P), -2),                 # H < 16
+    ((P, P, 0, 512, 128, P, P), -2),               # E = 0 with offs
+    ((P, P, 300, 512, 128, P, P), -2),             # E too large
+    ((P + 2, P, 4, 512, 128, P, P), -3),           # x misaligned
+    ((P, P, 4, 512, 128, P + 8, P), -3),           # q misaligned
+])
+def test_quantize_host_argument_checks(args, code):
+    assert mxw.mxfp8_quantize_tokens(*args) == code
+
+
+def test_quantize_python_face_validates():
+    import torch
+    with pytest.raises(ValueError):
+        mxw.quantize_tokens(torch.zeros((64, 32), dtype=torch.float32))   # not bf16
+    with pytest.raises(ValueError):
+        mxw.quantize_tokens(torch.zeros((64, 32), dtype=torch.bfloat16))  # CPU tensor: no host fallback
