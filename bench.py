@@ -22,6 +22,12 @@ mxfp8_grouped_fwd) is measured the same way with --workload 16b_fwd,
 16b_fwd_down, 16b_1k_fwd or 671b_fwd (rows = the base workload's routed
 tokens; useful work 2 * rows * C * N).
 
+The token-axis quantiser (mxfp8_quantize_tokens) is measured with
+--workload 16b_quant (or 671b_quant): one step quantises the base workload's
+dY [M, N] and X [M, K] (bf16, seeded) into its two MXFP8 operands; the metric
+is algorithmic HBM GB/s (2 bytes read, 1 + 1/32 bytes written per element)
+against the 8 TB/s HBM roof.
+
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
     --copy-calibration   run a plain 1 GiB device copy (counter calibration)
@@ -165,6 +171,65 @@ def bench_rows(args):
     print(json.dumps(res))
 
 
+QUANT_WORKLOADS = {"16b_quant": "16b_24k", "671b_quant": "671b_gateup"}
+HBM_PEAK_GBS = 8000.0
+
+
+def bench_quant(args):
+    import torch
+
+    import mxfp8_ragged_grouped_amd as mxw
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = QUANT_WORKLOADS[args.workload]
+    c = W.CONFIGS[base]
+    M, N, K = c["M"], c["N"], c["K"]
+    offs = torch.from_numpy(W.offs_from_sizes(W.routing_sizes(base)[0])).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 * c["cid"] + 555)
+    dy = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
+    xx = (0.5 * torch.randn((M, K), generator=g, device=dev)).to(torch.bfloat16)
+    qa = torch.empty((N, M), dtype=torch.uint8, device=dev)
+    sa = torch.empty((N, M // 32), dtype=torch.uint8, device=dev)
+    qb = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    sb = torch.empty((K, M // 32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mxw.quantize_tokens(dy, offs, q=qa, s=sa, stream=stream)
+        mxw.quantize_tokens(xx, offs, q=qb, s=sb, stream=stream)
+
+    ms, wall = time_steps(step, args, stream)
+    elems = float(M) * (N + K)
+    alg_bytes = elems * (2.0 + 1.0 + 1.0 / 32.0)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "MXFP8 token-axis quantiser HBM GB/s (algorithmic bytes: 2 read + 1 + 1/32 written per element)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->e4m3+e8m0/32", "data": "synthetic (seeded N(0,1) bf16 dY and 0.5 N(0,1) X)",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "elements": int(elems),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu:
+        import oracle
+        cols = 192
+        x_s = dy[:, :cols].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.quantize_tokens(x_s, used=int(offs[-1]))
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(M * cols * 3.03125 / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": "%s: the first %d of %d hidden columns of dY (%d x %d elements), %.1f s"
+                                         % (args.workload, cols, N, M, cols, dt)}
+    print(json.dumps(res))
+
+
 def time_steps(step, args, stream):
     """W untimed steps, then K timed ones between HIP events on `stream`."""
     import torch
@@ -210,6 +275,9 @@ def main():
 
     if args.workload in W.ROWS_CONFIGS:
         bench_rows(args)
+        return
+    if args.workload in QUANT_WORKLOADS:
+        bench_quant(args)
         return
 
     dev = torch.device("cuda:0")
