@@ -28,6 +28,12 @@ dY [M, N] and X [M, K] (bf16, seeded) into its two MXFP8 operands; the metric
 is algorithmic HBM GB/s (2 bytes read, 1 + 1/32 bytes written per element)
 against the 8 TB/s HBM roof.
 
+For the weight-gradient workloads the line also carries `bf16_context`: the
+same ragged problem in bf16 through torch._grouped_mm (dY^T [N, M] and X
+[M, K], contraction ragged by the same offs, hipBLASLt on ROCm), timed the same
+way in the same process, as the pages' "x BF16" comparison (context, not the
+metric).
+
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
     --copy-calibration   run a plain 1 GiB device copy (counter calibration)
@@ -162,7 +168,7 @@ def bench_rows(args):
                    "rows_used": int(np.sum(cfg["sizes"])), "routing_seed": cfg["routing_seed"],
                    "value_seed": cfg["value_seed"], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": load_traffic(args.workload)},
         "hbm_gbps_algorithmic": round(W.rows_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
     }
@@ -202,6 +208,7 @@ def bench_quant(args):
         mxw.quantize_tokens(xx, offs, q=qb, s=sb, stream=stream)
 
     ms, wall = time_steps(step, args, stream)
+    per_launch = load_traffic(args.workload)  # mean of the dY and X launches
     elems = float(M) * (N + K)
     alg_bytes = elems * (2.0 + 1.0 + 1.0 / 32.0)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
@@ -213,7 +220,8 @@ def bench_quant(args):
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "elements": int(elems),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if per_launch is None else 2 * per_launch},  # per step (two launches)
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu:
@@ -228,6 +236,31 @@ def bench_quant(args):
                                "sample": "%s: the first %d of %d hidden columns of dY (%d x %d elements), %.1f s"
                                          % (args.workload, cols, N, M, cols, dt)}
     print(json.dumps(res))
+
+
+def bf16_context(cfg, ours_tflops, args, stream):
+    """torch._grouped_mm on bf16 operands of the same shape and offs."""
+    import torch
+
+    dev = cfg["A"].device
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    a = torch.randn((N, M), generator=g, device=dev).to(torch.bfloat16)  # dY^T, contiguous
+    b = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)  # X
+    offs = cfg["offs"]
+    try:
+        ms, _ = time_steps(lambda: torch._grouped_mm(a, b, offs=offs), args, stream)
+    except Exception as ex:  # not every build has a grouped GEMM for this layout
+        return {"value": None, "error": str(ex)[:200]}
+    finally:
+        del a, b
+    import workloads as W
+    tf = W.useful_flops(cfg) / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "mxfp8_over_bf16": round(ours_tflops / tf, 3),
+            "what": "torch._grouped_mm(dY^T bf16 [N, M], X bf16 [M, K], offs) -> [E, N, K], same steps/warmup, "
+                    "same stream, this process"}
 
 
 def time_steps(step, args, stream):
@@ -256,6 +289,7 @@ def main():
     ap.add_argument("--workload", default="16b_24k")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 torch._grouped_mm context leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -324,6 +358,8 @@ def main():
         res["baseline_note"] = ("vs_baseline = value / 2,174 TFLOP/s, the blog's kernel at the 16B ragged shape on "
                                 "MI355X (their routing: linear ramp / ragged draw at 1.5x; ours: seeded Dirichlet "
                                 "at %.2fx)" % cfg["skew"])
+    if not args.no_bf16:
+        res["bf16_context"] = bf16_context(cfg, tflops, args, stream)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, cfg["A"].cpu().numpy(), cfg["sA"].cpu().numpy(),
                                            cfg["B"].cpu().numpy(), cfg["sB"].cpu().numpy(),
