@@ -984,9 +984,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   // ---- column mode: walk state -----------------------------------------------
   // Block b sits on XCD b % 8 (the dispatcher's round robin); with i = b / 8
   // its column is (i / kMem, b % 8) -- kMem members i % kMem on one XCD --
-  // numbered from the top so that later columns are dispatched first: a
-  // column's last region may wait for partials of later columns' first
-  // regions, never the reverse.
+  // numbered from the top (later spans are dispatched first; the numbering
+  // only places spans on XCDs, since no column ever waits for another).
   const int col = COL ? p.ncol - 1 - (((bid >> 3) / kMem) * 8 + (bid & 7)) : 0;
   const int member = (bid >> 3) % kMem;
   int nne = 0, kx = 0, rx = 0, Q = 0, x0 = 0, x1 = 0;
