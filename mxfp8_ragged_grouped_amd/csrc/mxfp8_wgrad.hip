@@ -6,7 +6,13 @@
 // (blog "Ragged MXFP8 Weight Gradients: A FlyDSL Grouped GEMM on MI355X",
 // section 1).  A = dY^T [N, M], B = X^T [K, M], token axis contiguous.
 //
-// Structure of one launch:
+// The same tile body also serves the row-ragged GEMM of the layer (forward
+// and data gradient: out[m] = A[m] B[g]^T over the rows m of expert g,
+// rows_kernel), and the file holds the token-axis quantiser that produces
+// the weight gradient's operands (quant_kernel); both are described where
+// they are defined.
+//
+// Structure of one weight-gradient launch:
 //   * work item = (expert, 256 x 256 output tile), computed by one 256-thread
 //     workgroup (4 wave64) that walks the expert's tokens in 64-token K-steps,
 //     keeps the tile's 65,536 FP32 sums in accumulator registers and stores
@@ -27,7 +33,9 @@
 //       unevenly: 1.3x the ideal span at 1.5 tiles per CU).  A region cut
 //       between columns is summed in a fixed order: its pieces count
 //       themselves in on a counter and the last to finish adds the others'
-//       FP32 partial tiles (no workgroup waits for another).
+//       FP32 partial tiles (no workgroup waits for another).  The tiles of a
+//       column that share a stripe split an L2 prefetch of it between them,
+//       one pair ahead of their loads.
 //   * staging: an LDS stage holds a pair of K-steps (256 rows x 128 tokens of
 //     A and of B, 64 KiB), filled by 16-byte LDS-direct buffer loads, 8 rows x
 //     128 bytes per instruction, so every memory request is one whole cache
@@ -41,7 +49,9 @@
 //     barrier per pair of K-steps, at the odd step: it certifies that the
 //     next pair has landed and that the current pair has been read, and that
 //     pair's stage is then refilled with the pair after next, its loads
-//     spread over the step's MFMAs.
+//     spread over the MFMAs of this odd step and the first ones of the next
+//     even step (a CU's vector memory path takes a 1 KiB load per ~16
+//     clocks: issued all at once they would hold up the MFMAs).
 //   * ragged head/tail: a 32-token sub-block is live iff it lies inside
 //     [start, end) (group boundaries are 32-aligned, blog section 1).  Dead
 //     sub-blocks are removed twice: their data loads are pointed out of the
