@@ -1,0 +1,105 @@
+"""Seeded random shapes for all three entry points against the oracle (needs an
+MI355X).  Shapes, routings, empty experts, unaligned row boundaries and
+padding garbage are drawn from fixed seeds; every case prints its parameters
+before it launches.  The weight-gradient cases include shapes that select
+column mode (long experts on few tiles).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_ragged_grouped_amd as mxw
+import oracle
+import workloads as W
+from helpers import BF16_NAN, bf16_bits, check_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print("[gpu-case] " + msg, flush=True)
+
+
+def random_sizes(rng, E, total, unit, empty_prob=0.2):
+    """E sizes, multiples of `unit`, summing to at most `total`."""
+    w = rng.dirichlet(np.full(E, 1.0))
+    w[rng.random(E) < empty_prob] = 0.0
+    if w.sum() == 0:
+        w[0] = 1.0
+    units = int(total * rng.uniform(0.7, 1.0)) // unit
+    s = np.floor(w / w.sum() * units).astype(np.int64) * unit
+    return s
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_wgrad_random_shapes(seed):
+    rng = np.random.default_rng(2000 + seed)
+    if seed % 3 == 0:  # column mode: long experts, few tiles
+        E = int(rng.integers(1, 4))
+        N = 16 * int(rng.integers(1, 33))
+        K = 16 * int(rng.integers(1, 49))
+        M = 32 * int(rng.integers(8192 * E // 32 + 1, 8192 * E // 32 + 400))
+    else:
+        E = int(rng.integers(1, 41))
+        N = 16 * int(rng.integers(1, 50))
+        K = 16 * int(rng.integers(1, 50))
+        M = 32 * int(rng.integers(1, 120))
+    sizes = random_sizes(rng, E, M, 32)
+    cfg = W.make_random(E, N, K, M, sizes, seed=2100 + seed, device=DEV)
+    used = int(sizes.sum())
+    cfg["A"][:, used:] = 0x7F  # NaN codes past the last expert
+    cfg["sB"][:, used // 32:] = 0xFF
+    say("wgrad fuzz %d: E=%d N=%d K=%d M=%d used=%d columns=%d" % (seed, E, N, K, M, used,
+                                                                    mxw.columns(E, M, N, K)))
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(BF16_NAN)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    torch.cuda.synchronize()
+    bits = bf16_bits(out)
+    ref = oracle.wgrad_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
+    check_close(bits, ref, what="wgrad fuzz %d" % seed)
+    for g in range(E):
+        if sizes[g] == 0:
+            assert (bits[g] == 0).all()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fwd_random_shapes(seed):
+    rng = np.random.default_rng(2200 + seed)
+    E = int(rng.integers(1, 21))
+    R = int(rng.integers(1, 3000))
+    C = 32 * int(rng.integers(1, 40))
+    N = 16 * int(rng.integers(1, 40))
+    sizes = random_sizes(rng, E, R, 1)
+    cfg = W.make_rows(E, R, C, N, sizes, seed=2300 + seed, device=DEV)
+    used = int(sizes.sum())
+    cfg["A"][used:] = 0x7F
+    say("fwd fuzz %d: E=%d R=%d C=%d N=%d used=%d" % (seed, E, R, C, N, used))
+    out = torch.empty((R, N), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(BF16_NAN)
+    mxw.fwd(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    torch.cuda.synchronize()
+    bits = bf16_bits(out)
+    ref = oracle.rows_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
+    check_close(bits[:used], ref[:used], what="fwd fuzz %d" % seed)
+    assert (bits[used:] == BF16_NAN).all()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_quantize_random_shapes(seed):
+    rng = np.random.default_rng(2400 + seed)
+    M = 32 * int(rng.integers(1, 200))
+    H = 16 * int(rng.integers(1, 80))
+    used = 32 * int(rng.integers(0, M // 32 + 1))
+    g = torch.Generator().manual_seed(2500 + seed)
+    x = (torch.randn((M, H), generator=g) * torch.exp2(torch.randint(-30, 30, (1, H), generator=g).float()))
+    x = x.to(torch.bfloat16)
+    x[used:] = float("nan")
+    say("quant fuzz %d: M=%d H=%d used=%d" % (seed, M, H, used))
+    q, s = mxw.quantize_tokens(x.to(DEV), torch.tensor([used], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_tokens(x.view(torch.int16).numpy().view(np.uint16), used=used)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
