@@ -23,6 +23,11 @@ gradient; blog section 1, XLA blog "non-contracting" ragged dot):
     out[m][n] = sum_{c < C} e4m3(X[m][c]) 2^(sX[m][c/32]-127)
                           * e4m3(W[g][n][c]) 2^(sW[g][n][c/32]-127),  m in [start_g, end_g)
 
+the same weight gradient on plain bf16 operands (XLA blog, "Contracting"
+ragged dot, Table 7's wgrad classes):
+
+    dW[g][n][k] = sum_{m in [start_g, end_g)} bf16(A[n][m]) * bf16(B[k][m])
+
 and the token-axis MXFP8 quantiser that produces the weight gradient's operands
 (scale byte clamp(floor(log2 amax) - 8 + 127, 0, 254), E4M3 round-to-nearest-even
 with saturation, transposed to token-contiguous).
@@ -87,6 +92,11 @@ def _load():
     lib.mxw_oracle_bf16_rne.restype = ctypes.c_uint16
     lib.mxw_oracle_bf16_rne.argtypes = [ctypes.c_double]
     lib.mxw_oracle_to_bf16.argtypes = [P, I64, P]
+    lib.mxw_oracle_bf16.restype = ctypes.c_double
+    lib.mxw_oracle_bf16.argtypes = [ctypes.c_uint]
+    lib.mxw_oracle_decode_bf16_plane.argtypes = [P, I, I64, I64, P]
+    lib.mxw_oracle_bf16_wgrad_f64.argtypes = [P, P, P, I, I64, I, I, P]
+    lib.mxw_oracle_bf16_wgrad_points.argtypes = [P, P, P, I, I64, I, I, P, P, P, I64, P]
     lib.mxw_oracle_max_threads.restype = I
     lib.mxw_oracle_set_threads.argtypes = [I]
     _lib = lib
@@ -261,6 +271,68 @@ def quantize_tokens(x_bits, used=None):
     s = np.empty((H, M // 32), np.uint8)
     _check(_load().mxw_oracle_quantize_tokens(_ptr(x_bits), M, H, used, _ptr(q), _ptr(s)))
     return q, s
+
+
+def _u16(a):
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        if a.dtype.itemsize != 2:
+            raise ValueError("expected 16-bit bf16 bit patterns, got %s" % a.dtype)
+        a = a.view(np.uint16)
+    return np.ascontiguousarray(a)
+
+
+def bf16(bits):
+    """Decode one bf16 bit pattern to a Python float."""
+    return _load().mxw_oracle_bf16(int(bits))
+
+
+def decode_bf16_plane(x, used=None):
+    """Decode a bf16 plane [rows, M] (uint16 bit patterns) to fp64; tokens at
+    or past `used` are 0."""
+    x = _u16(x)
+    rows, M = x.shape
+    used = M if used is None else int(used)
+    out = np.empty((rows, M), np.float64)
+    _check(_load().mxw_oracle_decode_bf16_plane(_ptr(x), rows, M, used, _ptr(out)))
+    return out
+
+
+def bf16_wgrad_f64(A, B, offs):
+    """BF16 contracting ragged dot, fp64 [E, N, K]: A [N, M] and B [K, M] are
+    bf16 bit patterns (uint16), token-contiguous; offs the cumulative ends
+    (any alignment)."""
+    A = _u16(A)
+    B = _u16(B)
+    N, M = A.shape
+    K = B.shape[0]
+    if B.shape[1] != M:
+        raise ValueError("A and B disagree on M")
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    E = offs.shape[0]
+    out = np.empty((E, N, K), np.float64)
+    _check(_load().mxw_oracle_bf16_wgrad_f64(_ptr(A), _ptr(B), _ptr(offs), E, M, N, K, _ptr(out)))
+    return out
+
+
+def bf16_wgrad_points(A, B, offs, g, n, k):
+    """BF16 dW[g[i], n[i], k[i]] in fp64 for each i, straight from the definition."""
+    A = _u16(A)
+    B = _u16(B)
+    N, M = A.shape
+    K = B.shape[0]
+    if B.shape[1] != M:
+        raise ValueError("A and B disagree on M")
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    g = np.ascontiguousarray(g, dtype=np.int32)
+    n = np.ascontiguousarray(n, dtype=np.int32)
+    k = np.ascontiguousarray(k, dtype=np.int32)
+    if not (g.shape == n.shape == k.shape) or g.ndim != 1:
+        raise ValueError("point index arrays must be 1-D and of equal length")
+    out = np.empty(g.shape[0], np.float64)
+    _check(_load().mxw_oracle_bf16_wgrad_points(_ptr(A), _ptr(B), _ptr(offs), offs.shape[0], M, N, K, _ptr(g),
+                                                _ptr(n), _ptr(k), g.shape[0], _ptr(out)))
+    return out
 
 
 def to_bf16_bits(x):

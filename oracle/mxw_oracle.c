@@ -472,3 +472,113 @@ void mxw_oracle_set_threads(int n) {
   (void)n;
 #endif
 }
+
+/*
+ * BF16 contracting ragged dot: the same weight gradient on plain bfloat16
+ * operands (ROCm blog "Group-GEMM in XLA": the "Contracting" variant of
+ * Table 1, and the wgrad_wi / wgrad_wo classes of Table 7, which are
+ * bfloat16 throughout).  For every expert g, n < N, k < K:
+ *
+ *   out[g][n][k] = sum over tokens m in [start_g, end_g) of bf16(A[n][m]) * bf16(B[k][m])
+ *
+ * A [N, M] and B [K, M] hold bf16 bit patterns, token-contiguous (row stride
+ * M elements).  The pages fix the classes' dimension numbers, not the
+ * storage order; this is the storage with the contracted axis innermost,
+ * the same as the MXFP8 operands.  The XLA ragged dot puts no alignment on
+ * the group sizes, so windows are checked with align = 1.
+ *
+ * bf16 is decoded from its bit fields: 1 sign bit, 8 exponent bits with bias
+ * 127 and 7 fraction bits; exponent field 0 holds zero and the subnormals
+ * f * 2^-133, field 255 holds infinity (f = 0) and NaN.  Every product of two
+ * decoded values is exact in fp64 (8 + 8 significant bits); the sum runs in
+ * ascending token order.
+ */
+double mxw_oracle_bf16(unsigned bits) {
+  bits &= 0xFFFFu;
+  unsigned sign = bits >> 15;
+  unsigned expo = (bits >> 7) & 0xFFu;
+  unsigned frac = bits & 0x7Fu;
+  double mag;
+  if (expo == 0xFFu) {
+    mag = frac ? NAN : INFINITY;
+  } else if (expo == 0) {
+    mag = ldexp((double)frac, -133); /* 0.fffffff * 2^-126 */
+  } else {
+    mag = ldexp(128.0 + (double)frac, (int)expo - 127 - 7); /* 1.fffffff * 2^(e-127) */
+  }
+  return sign ? -mag : mag;
+}
+
+/* Decode a bf16 plane [rows, M] to fp64; tokens at or past `used` become 0
+ * without being read as values (they belong to no expert). */
+int mxw_oracle_decode_bf16_plane(const uint16_t* x, int rows, int64_t M, int64_t used, double* out) {
+  if (!x || !out) return MXWO_ERR_NULL;
+  if (rows < 0 || M < 0 || used < 0 || used > M) return MXWO_ERR_DIM;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; ++r)
+    for (int64_t m = 0; m < M; ++m)
+      out[(int64_t)r * M + m] = m < used ? mxw_oracle_bf16(x[(int64_t)r * M + m]) : 0.0;
+  return MXWO_OK;
+}
+
+/* Full BF16 weight gradient [E, N, K] in fp64: windows, decode, contract. */
+int mxw_oracle_bf16_wgrad_f64(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int64_t M, int N,
+                              int K, double* out) {
+  if (!A || !B || !offs || !out) return MXWO_ERR_NULL;
+  if (E < 1 || M < 0 || N < 1 || K < 1) return MXWO_ERR_DIM;
+  int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  int64_t* end = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  double* Ad = (double*)malloc(sizeof(double) * (size_t)N * (size_t)(M > 0 ? M : 1));
+  double* Bd = (double*)malloc(sizeof(double) * (size_t)K * (size_t)(M > 0 ? M : 1));
+  int rc = MXWO_OK;
+  if (!start || !end || !Ad || !Bd) {
+    rc = MXWO_ERR_NOMEM;
+    goto done;
+  }
+  rc = mxw_oracle_windows(offs, E, M, 1, start, end);
+  if (rc) goto done;
+  rc = mxw_oracle_decode_bf16_plane(A, N, M, end[E - 1], Ad);
+  if (rc) goto done;
+  rc = mxw_oracle_decode_bf16_plane(B, K, M, end[E - 1], Bd);
+  if (rc) goto done;
+  rc = mxw_oracle_ragged_contract_f64(Ad, Bd, start, end, E, M, N, K, out);
+done:
+  free(start);
+  free(end);
+  free(Ad);
+  free(Bd);
+  return rc;
+}
+
+/* Selected outputs of the BF16 weight gradient, each straight from the
+ * definition (decode every term, ascending m): (pg[i], pn[i], pk[i]) -> out[i]. */
+int mxw_oracle_bf16_wgrad_points(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int64_t M, int N,
+                                 int K, const int32_t* pg, const int32_t* pn, const int32_t* pk, int64_t npts,
+                                 double* out) {
+  if (!A || !B || !offs || !pg || !pn || !pk || !out) return MXWO_ERR_NULL;
+  if (E < 1 || M < 0 || N < 1 || K < 1 || npts < 0) return MXWO_ERR_DIM;
+  int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  int64_t* end = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  if (!start || !end) {
+    free(start);
+    free(end);
+    return MXWO_ERR_NOMEM;
+  }
+  int rc = mxw_oracle_windows(offs, E, M, 1, start, end);
+  for (int64_t i = 0; rc == MXWO_OK && i < npts; ++i)
+    if (pg[i] < 0 || pg[i] >= E || pn[i] < 0 || pn[i] >= N || pk[i] < 0 || pk[i] >= K) rc = MXWO_ERR_DIM;
+  if (rc == MXWO_OK) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < npts; ++i) {
+      const int g = pg[i];
+      const uint16_t* arow = A + (int64_t)pn[i] * M;
+      const uint16_t* brow = B + (int64_t)pk[i] * M;
+      double acc = 0.0;
+      for (int64_t m = start[g]; m < end[g]; ++m) acc += mxw_oracle_bf16(arow[m]) * mxw_oracle_bf16(brow[m]);
+      out[i] = acc;
+    }
+  }
+  free(start);
+  free(end);
+  return rc;
+}

@@ -125,3 +125,20 @@ def test_useful_flops_and_bytes():
     cfg = dict(sizes=np.array([100 * 32, 0, 50 * 32]), N=1408, K=2048, E=3)
     assert W.useful_flops(cfg) == 2.0 * 4800 * 1408 * 2048
     assert W.algorithmic_bytes(cfg) == pytest.approx(4800 * 3456 * (1 + 1 / 32) + 2 * 3 * 1408 * 2048 + 12)
+
+
+def test_bf16_workload_recipe():
+    """The named bf16 workloads keep their base workload's shape and routing;
+    values are std * N(0, 1) rounded once to bf16, deterministic per seed."""
+    cfg = W.make_bf16_config("16b_1k_bf16")
+    base = W.CONFIGS["16b_1k"]
+    assert (cfg["E"], cfg["N"], cfg["K"], cfg["M"]) == (base["E"], base["N"], base["K"], base["M"])
+    sizes, _ = W.routing_sizes("16b_1k")
+    np.testing.assert_array_equal(cfg["sizes"], sizes)
+    np.testing.assert_array_equal(cfg["offs"].numpy(), W.offs_from_sizes(sizes))
+    assert cfg["A"].dtype == torch.bfloat16 and cfg["A"].shape == (1408, 8192) and cfg["B"].shape == (2048, 8192)
+    again = W.make_bf16_config("16b_1k_bf16")
+    assert torch.equal(cfg["A"].view(torch.int16), again["A"].view(torch.int16))
+    assert abs(float(cfg["A"].float().std()) - 1.0) < 0.01 and abs(float(cfg["B"].float().std()) - 0.5) < 0.01
+    bf = dict(sizes=np.array([100, 0, 60]), N=1408, K=2048, E=3)
+    assert W.bf16_algorithmic_bytes(bf) == 160 * 3456 * 2 + 2 * 3 * 1408 * 2048 + 12

@@ -365,3 +365,63 @@ def rows_algorithmic_bytes(cfg):
     mu = float(np.asarray(cfg["sizes"]).sum())
     C, N, E = cfg["C"], cfg["N"], cfg["E"]
     return mu * C * (1.0 + 1.0 / 32.0) + E * N * C * (1.0 + 1.0 / 32.0) + 2.0 * mu * N + 4.0 * E
+
+
+# --------------------------------------------------------------------------
+# BF16 contracting ragged dot (the same weight gradient on bf16 operands)
+# --------------------------------------------------------------------------
+# The XLA blog's wgrad classes (Table 7) are bfloat16; these workloads take a
+# named MXFP8 workload's shape and routing and draw the same value
+# distributions, rounded once to bf16 (round-to-nearest-even), stored
+# token-contiguous like the MXFP8 operands: A = dY^T [N, M], B = X^T [K, M].
+BF16_CONFIGS = {
+    "16b_bf16": "16b_24k",
+    "16b_1k_bf16": "16b_1k",
+    "671b_bf16": "671b_gateup",
+}
+
+
+def make_bf16_operand(rows, M, std, seed, device="cpu", chunk_rows=None):
+    """bf16 operand [rows, M]: std * N(0, 1) rounded to bf16, on `device`."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    if chunk_rows is None:
+        chunk_rows = max(1, min(rows, (1 << 24) // max(M, 1)))
+    x = torch.empty((rows, M), dtype=torch.bfloat16, device=device)
+    for r0, z in _gen_values(rows, M, "normal", std, gen, device, chunk_rows):
+        x[r0:r0 + z.shape[0]] = z.to(torch.bfloat16)
+    return x
+
+
+def make_bf16(E, N, K, M, sizes, seed, device="cpu", std=(1.0, 1.0)):
+    """A custom-shaped bf16 problem: A [N, M], B [K, M] (torch.bfloat16) and offs."""
+    sizes = np.asarray(sizes, np.int64)
+    if sizes.shape != (E,) or sizes.sum() > M:
+        raise ValueError("sizes must be [E] with sum <= M")
+    A = make_bf16_operand(N, M, std[0], seed, device)
+    B = make_bf16_operand(K, M, std[1], seed + 1, device)
+    return dict(name="custom_bf16", E=E, N=N, K=K, M=M, A=A, B=B,
+                offs=torch.from_numpy(offs_from_sizes(sizes)).to(device), sizes=sizes,
+                routing_seed=None, value_seed=seed, skew=float(sizes.max() / max(M / E, 1)))
+
+
+def make_bf16_config(name, device="cpu", seed=None):
+    """A named bf16 workload: the shape, routing and value spread of its base
+    MXFP8 workload, value seed 1000 * cid + 998."""
+    base = BF16_CONFIGS[name]
+    c = CONFIGS[base]
+    E, N, K, M = c["E"], c["N"], c["K"], c["M"]
+    sizes, rseed = routing_sizes(base)
+    vseed = 1000 * c["cid"] + 998 if seed is None else int(seed)
+    sa_std, sb_std = c["values"]
+    cfg = make_bf16(E, N, K, M, sizes, vseed, device, (sa_std, sb_std))
+    cfg.update(name=name, base=base, routing_seed=rseed, skew=float(sizes.max() / (M / E)))
+    return cfg
+
+
+def bf16_algorithmic_bytes(cfg):
+    """Each routed token's (N + K) bf16 values read once, the bf16 output
+    written once, offs read."""
+    mu = float(np.asarray(cfg["sizes"]).sum())
+    N, K, E = cfg["N"], cfg["K"], cfg["E"]
+    return mu * (N + K) * 2.0 + 2.0 * E * N * K + 4.0 * E
