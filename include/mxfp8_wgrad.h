@@ -103,6 +103,41 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
                         const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream);
 
 /*
+ * bf16_wgrad_grouped -- the same weight gradient on plain bfloat16 operands:
+ * the "contracting" ragged dot of the XLA blog ("Group-GEMM in XLA", Table 1,
+ * and the bfloat16 wgrad_wi / wgrad_wo classes of its Table 7, which contract
+ * the ragged token axis into one slab per expert).  For every expert g,
+ * n < N, k < K:
+ *
+ *     out[g][n][k] = sum_{m = start_g}^{end_g - 1} bf16(A[n][m]) * bf16(B[k][m])
+ *
+ * accumulated in FP32 on the bf16 MFMA (every product is exact in FP32) and
+ * rounded once to bf16, round-to-nearest-even.  Same windows as above.
+ *
+ * Arguments (caller-owned DEVICE memory on the current HIP device):
+ *   A     bf16 bit patterns [N, M] (dY^T), token-contiguous, row stride M.
+ *   B     bf16 bit patterns [K, M] (X^T), token-contiguous, row stride M.
+ *   offs  int32 [E] cumulative ends.  E, N, K, out, stream: as above.
+ *   M     0 <= M <= MXW_MAX_TOKENS / 2, M % 16 == 0.
+ * The pages give the classes' dimension numbers, not a storage order; the
+ * operands are taken with the contracted (token) axis innermost, as for the
+ * MXFP8 path.  Device-data preconditions: offs non-decreasing, every offs[g]
+ * a multiple of 16, offs[E-1] <= M (malformed offs: unspecified values, no
+ * out-of-bounds access).  Tokens in [offs[E-1], M) may hold anything, NaN and
+ * infinity included: they never reach the result.
+ *
+ * Effects, reproducibility, scheduling and workspace: as mxfp8_wgrad_grouped,
+ * planned on the token axis in bytes: the launch runs in column mode exactly
+ * when mxw_columns(E, 2 M, N, K) > 0, and shares the device's column-mode
+ * workspace with mxfp8_wgrad_grouped (launches of either on one device must
+ * not overlap in time when both run in column mode).
+ *
+ * Returns MXW_OK or a negative MXW_ERR_* code.
+ */
+int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
+                       uint16_t* out, void* stream);
+
+/*
  * mxw_grid_size -- the number of (expert, 256 x 256 output tile) work items
  * of (E, N, K), E * ceil(N/256) * ceil(K/256) (blog section 4: one block per
  * expert per output tile).  Outside column mode this is also the number of

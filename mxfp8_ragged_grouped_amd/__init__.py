@@ -1,6 +1,7 @@
 """MI355X-native MXFP8 ragged grouped GEMMs.
 
     out = wgrad(A, sA, B, sB, offs)        # bf16 [E, N, K]
+    out = wgrad_bf16(A, B, offs)           # bf16 [E, N, K] from bf16 operands
     out = fwd(A, sA, B, sB, offs)          # bf16 [R, N]
     q, s = quantize_tokens(x, offs)        # MXFP8 operand [H, M] from bf16 [M, H]
 
@@ -16,7 +17,9 @@ row-ragged GEMM of the same layer (forward and data gradient):
     out[m] = A[m] B[g]^T   for the rows m of expert g, contraction over C
 
 from A [R, C] and B [E, N, C] (contraction innermost, 32-element E8M0 blocks
-along it); and the token-axis quantiser that makes the weight gradient's
+along it); the same weight gradient on plain bf16 operands A = dY^T [N, M],
+B = X^T [K, M] (the XLA blog's "contracting" ragged dot); and the token-axis
+quantiser that makes the weight gradient's
 operands from bf16 activations / gradients.  Everything
 runs in the HIP library ``lib/libmxfp8_wgrad.so`` (C ABI in
 ``include/mxfp8_wgrad.h``); this module only checks tensor metadata and passes
@@ -30,7 +33,7 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["wgrad", "mxfp8_wgrad_grouped", "grid_size", "columns", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "wgrad_bf16", "bf16_wgrad_grouped", "grid_size", "columns", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
            "quantize_tokens", "mxfp8_quantize_tokens", "strerror", "version", "library_path", "MxwError"]
 
 _lib = None
@@ -55,6 +58,8 @@ def _load():
     I = ctypes.c_int
     lib.mxfp8_wgrad_grouped.restype = I
     lib.mxfp8_wgrad_grouped.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
+    lib.bf16_wgrad_grouped.restype = I
+    lib.bf16_wgrad_grouped.argtypes = [P, P, P, I, I, I, I, P, P]
     lib.mxw_grid_size.restype = ctypes.c_int64
     lib.mxw_grid_size.argtypes = [I, I, I]
     lib.mxw_strerror.restype = ctypes.c_char_p
@@ -148,6 +153,52 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None):
                                  E, M, N, K, out.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise MxwError("mxfp8_wgrad_grouped failed (%d): %s" % (rc, strerror(rc)))
+    return out
+
+
+def bf16_wgrad_grouped(A, B, offs, E, M, N, K, out, stream=0):
+    """Raw C-ABI call on device addresses (ints).  Returns the status code."""
+    lib = _load()
+    return lib.bf16_wgrad_grouped(A, B, offs, int(E), int(M), int(N), int(K), out, stream)
+
+
+def wgrad_bf16(A, B, offs, out=None, stream=None):
+    """dW [E, N, K] bf16 from bf16 operands: dW[g] = A[:, win_g] B[:, win_g]^T.
+
+    A: [N, M] and B: [K, M] bfloat16 (token axis contiguous), offs: [E] int32
+    cumulative expert ends (multiples of 16), all contiguous on one GPU.
+    `out` (optional) is a contiguous bf16 [E, N, K] tensor that is fully
+    overwritten.  Runs on `stream` (default: the current stream) and does not
+    synchronise.
+    """
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if A.dim() != 2 or B.dim() != 2 or offs.dim() != 1:
+        raise ValueError("A, B must be 2-D and offs 1-D")
+    N, M = A.shape
+    K = B.shape[0]
+    E = offs.shape[0]
+    if B.shape[1] != M:
+        raise ValueError("shape mismatch: A %s B %s" % (tuple(A.shape), tuple(B.shape)))
+    if offs.dtype != torch.int32:
+        raise TypeError("offs must be int32")
+    dev = A.device
+    for name, t in (("A", A), ("B", B), ("offs", offs)):
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("%s must be on the same GPU as A" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (E, N, K) or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bf16 [E, N, K] tensor on the same device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = bf16_wgrad_grouped(A.data_ptr(), B.data_ptr(), offs.data_ptr(), E, M, N, K, out.data_ptr(),
+                                stream.cuda_stream)
+    if rc != 0:
+        raise MxwError("bf16_wgrad_grouped failed (%d): %s" % (rc, strerror(rc)))
     return out
 
 

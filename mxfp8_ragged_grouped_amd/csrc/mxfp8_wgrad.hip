@@ -105,6 +105,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 256;                   // output tile edge, N and K
 constexpr int kStep = 64;                    // tokens per K-step (two 32-token sub-blocks)
@@ -277,6 +278,15 @@ __device__ __forceinline__ v16f mfma_e4m3_sel(int oa, int ob, const v8i& a, cons
   }
 }
 
+// v_mfma_f32_32x32x16_bf16 on half H of two fragments: bytes 16 H .. 16 H + 15
+// of each lane's 32 (8 bf16 values per lane and operand)
+template <int H>
+__device__ __forceinline__ v16f mfma_bf16(const v8i& a, const v8i& b, const v16f& c) {
+  const v4i ah = __builtin_shufflevector(a, a, 4 * H, 4 * H + 1, 4 * H + 2, 4 * H + 3);
+  const v4i bh = __builtin_shufflevector(b, b, 4 * H, 4 * H + 1, 4 * H + 2, 4 * H + 3);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), __builtin_bit_cast(v8bf, bh), c, 0, 0, 0);
+}
+
 // one MFMA operand fragment: the lane's two 16-byte runs of a 32-row block
 __device__ __forceinline__ v8i frag(const uint8_t* blk, int lo, int hi) {
   const v4i a = *(const v4i*)(blk + lo);
@@ -295,6 +305,9 @@ struct Params {
   // row-ragged GEMM: A [R, M], B [E, N, M], out [R, N] (contraction M, K unused)
   int E, M, N, K;
   int R;  // row-ragged GEMM: rows of A and out
+  // log2 of the bytes per token of A and B: 0 for E4M3 codes, 1 for bf16 (M,
+  // the row stride and every window are then in bytes: offs are shifted)
+  int tshift;
   int tilesN, tilesK;
   // XCD regions (0 = off): each expert's tilesN x tilesK grid is cut into 8
   // rectangles of regN x regK tiles, regB of them across the K direction;
@@ -369,8 +382,14 @@ struct Piece {
 };
 
 // ROWS: the row-ragged GEMM (out rows = A rows of one expert, out columns =
-// that expert's B rows); otherwise the weight gradient.
-template <bool GROUP, bool COL, bool ROWS>
+// that expert's B rows); otherwise the weight gradient.  BF: the weight
+// gradient on bf16 operands.  Everything along the token axis is then counted
+// in bytes (a staged 128-byte row holds 64 tokens, a "K-step" 32 and a
+// "sub-block" 16), there are no scales, and each MFMA slot runs two
+// v_mfma_f32_32x32x16_bf16 on the halves of the fragments that the E4M3
+// instruction takes whole: the same bytes per clock, at twice the
+// instruction count and half the FLOP per byte.
+template <bool GROUP, bool COL, bool ROWS, bool BF = false>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
   int tid = threadIdx.x;
   // opaque per piece: nothing derived from the thread index is hoisted out of
@@ -483,7 +502,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // time) so that every step issues the same count.
   constexpr int kGroupSteps = GROUP ? 8 : 2;
   constexpr int kAhead = GROUP ? 1 : 3;
-  constexpr int kScaleDma = GROUP ? 2 : 4;
+  constexpr int kScaleDma = BF ? 0 : (GROUP ? 2 : 4);
   // grouped: one operand's 16 bytes of group g for this lane's row, into
   // slot g % 3 (groups past the row's end read other rows' bytes or nothing;
   // they only reach steps past M, whose sub-blocks are all dead)
@@ -557,7 +576,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   const int qs = start >> 5, qn = (end - start) >> 5;
   {
     const int G0 = s0 / kGroupSteps;
-    if (GROUP) {
+    if (BF) {
+      // no scales
+    } else if (GROUP) {
       // groups G0 and G0 + 1; the loop fetches group G + 2 for both operands
       // during the two iterations that start in group G
 #pragma unroll
@@ -572,9 +593,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     for (int i = 0; i < kDataDma; ++i) dma_pair(i, 0, P0, l0);
 #pragma unroll
     for (int i = 0; i < kOddLoads; ++i) dma_pair(i, 1, P0 + 1, l1);
-    if (!GROUP) dma_scales(0, false);
+    if (!GROUP && !BF) dma_scales(0, false);
   }
-  wait_vm<GROUP ? kOddLoads : kOddLoads + kSlot>();  // scales and pair s0/2 landed (this wave)
+  wait_vm<(GROUP || BF) ? kOddLoads : kOddLoads + kSlot>();  // scales and pair s0/2 landed (this wave)
   __syncthreads();
 
   // Scale registers.  In lane l the MFMA takes the E8M0 byte of row l % 32 and
@@ -633,7 +654,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   v8i fa[2][4], fb[2][4];
   uint32_t sra[2][4], srb[2][4];  // [pair parity][32-row block]
   uint32_t rawa[4], rawb[4];
-  load_sregs(s0, sra[0], srb[0]);
+  if (!BF) load_sregs(s0, sra[0], srb[0]);
   {
     const uint8_t* ta = sm.data[0][0] + (wn * 128) * kRowBytes;
     const uint8_t* tb = sm.data[0][1] + (wk * 128) * kRowBytes;
@@ -692,8 +713,16 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int i = m >> 2, t = m & 3;  // B block i, A block t
-        acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
-                                  (int)sra[u >> 1][t]);
+        if constexpr (BF) {
+          // first halves into block m, second halves into block (m + 8) % 16:
+          // MFMAs on one accumulator stay 16 instructions apart
+          const int i2 = i ^ 2;
+          acc[i][t] = mfma_bf16<0>(fb[cur][i], fa[cur][t], acc[i][t]);
+          acc[i2][t] = mfma_bf16<1>(fb[cur][i2], fa[cur][t], acc[i2][t]);
+        } else {
+          acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
+                                    (int)sra[u >> 1][t]);
+        }
         if (m == 0 && (u & 1)) {
           const bool lok_e = (livep >> sbl_e) & 1u, lok_o = (livep >> sbl_o) & 1u;
 #pragma unroll
@@ -704,7 +733,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           // after the previous (even) step's data loads: its scale loads
           // (paired: kSlot; grouped: one at u = 0) and, in column mode, its
           // kPrefetch prefetches
-          if (!GROUP) wait_vm<kSlot + (COL ? kPrefetch : 0)>();
+          if (BF) wait_vm<COL ? kPrefetch : 0>();
+          else if (!GROUP) wait_vm<kSlot + (COL ? kPrefetch : 0)>();
           else if (u == 1) wait_vm<1 + (COL ? kPrefetch : 0)>();
           else wait_vm<COL ? kPrefetch : 0>();
           __builtin_amdgcn_s_barrier();
@@ -741,12 +771,12 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
         if (m >= 7 && m < 11) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
-        if (GROUP && (u & 1) && m == 10) {
+        if (!BF && GROUP && (u & 1) && m == 10) {
           int sq = s;
           asm volatile("" : "+s"(sq));
           read_raw(sq + 1, rawa, rawb);
         }
-        if (m == 15) {  // after the step's data loads (vmcnt order)
+        if (!BF && m == 15) {  // after the step's data loads (vmcnt order)
           if (!GROUP) {
             dma_scales(sgrp, sreal);
           } else if (u == 0) {
@@ -760,7 +790,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           asm volatile("" : "+s"(sp));
           // odd step: the next pair's scale registers (its raw bytes landed
           // with the pair, certified by this step's barrier)
-          if (u & 1) {
+          if (!BF && (u & 1)) {
             if (GROUP) finish_sregs(sp + 1, rawa, rawb, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
             else load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
           }
@@ -923,8 +953,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 
 // GROUP: scale rows are 16-byte aligned (M % 512 == 0) and scales are loaded
 // 8 K-steps at a time; otherwise 2 K-steps at a time.  COL: column mode (see
-// Params); otherwise one workgroup per (expert, tile).
-template <bool GROUP, bool COL>
+// Params); otherwise one workgroup per (expert, tile).  BF: bf16 operands.
+template <bool GROUP, bool COL, bool BF = false>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -935,10 +965,11 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   const int T = p.tilesN * p.tilesK;
   const int bid = blockIdx.x;
 
-  // ---- windows from offs (clamped to [0, M], monotone) ----------------------
+  // ---- windows from offs (clamped to [0, M], monotone; in bytes) -------------
   if (tid < E) {
-    int e = min(max(p.offs[tid], 0), M);
-    const int s = tid ? min(max(p.offs[tid - 1], 0), M) : 0;
+    const int Mt = M >> p.tshift;  // tokens
+    int e = min(max(p.offs[tid], 0), Mt) << p.tshift;
+    const int s = tid ? min(max(p.offs[tid - 1], 0), Mt) << p.tshift : 0;
     if (e < s) e = s;
     sm.start[tid] = s;
     sm.len[tid] = e - s;
@@ -1068,7 +1099,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       zero_tile(p, pc.g, pc.tn, pc.tk);
       return;
     }
-    run_piece<GROUP, false, false>(p, sm, pc);
+    run_piece<GROUP, false, false, BF>(p, sm, pc);
   } else {
     // ---- column mode: the pieces of this column, in sequence order -------------
     for (;;) {
@@ -1104,7 +1135,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       // LDS reads are done in every wave before new loads land
       wait_vm_all();
       __syncthreads();
-      run_piece<GROUP, true, false>(p, sm, pc);
+      run_piece<GROUP, true, false, BF>(p, sm, pc);
     }
   }
 }
@@ -1358,6 +1389,74 @@ int plan_columns(int E, int M, int N, int K, int cus, int* regions) {
   return 0;
 }
 
+// One weight-gradient launch (E4M3 operands with scales when tshift = 0,
+// bf16 operands when tshift = 1).  Mb: bytes per row of A and B.  Sizes and
+// pointers are validated by the caller.
+int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const int32_t* offs,
+                 int E, int Mb, int tshift, int N, int K, uint16_t* out, void* stream) {
+  const int64_t grid = (int64_t)E * ((N + kTile - 1) / kTile) * ((K + kTile - 1) / kTile);
+  if (grid <= 0 || grid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
+  int rc = check_device();
+  if (rc) return rc;
+  Params p = {};
+  p.A = A;
+  p.sA = sA;
+  p.B = B;
+  p.sB = sB;
+  p.offs = offs;
+  p.out = out;
+  p.E = E;
+  p.M = Mb;
+  p.N = N;
+  p.K = K;
+  p.tshift = tshift;
+  p.tilesN = (N + kTile - 1) / kTile;
+  p.tilesK = (K + kTile - 1) / kTile;
+  // XCD regions: split the tile grid a x b = 8 ways into equal rectangles,
+  // the most square split (fewest distinct A + B stripes per rectangle)
+  p.regN = p.regK = p.regB = p.band = 0;
+  int best = 1 << 30;
+  for (int a = 1; a <= 8; a *= 2) {
+    const int b = 8 / a;
+    if (p.tilesN % a || p.tilesK % b) continue;
+    const int rn = p.tilesN / a, rk = p.tilesK / b;
+    if (rn + rk < best) {
+      best = rn + rk;
+      p.regN = rn;
+      p.regK = rk;
+      p.regB = b;
+    }
+  }
+  if (p.regN) {
+    // about 32 co-resident workgroups per XCD: bands of ~32 / regK rows
+    p.band = (32 + p.regK - 1) / p.regK;
+    if (p.band > p.regN) p.band = p.regN;
+  }
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  p.hov = kColHov;
+  const int ncol = plan_columns(E, Mb, N, K, dev < 64 ? g_dev[dev].cus : 0, &p.regions);
+  p.ncol = ncol;
+  if (ncol) {
+    rc = get_workspace(dev, ncol, &p.part, &p.flags);
+    if (rc) return rc;
+  }
+  const dim3 g((unsigned)(ncol ? ncol * kMem : grid)), blk(kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (tshift) {
+    if (ncol) hipLaunchKernelGGL((wgrad_kernel<false, true, true>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((wgrad_kernel<false, false, true>), g, blk, 0, st, p);
+  } else if ((Mb & 511) == 0) {
+    if (ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
+  } else {
+    if (ncol) hipLaunchKernelGGL((wgrad_kernel<false, true>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((wgrad_kernel<false, false>), g, blk, 0, st, p);
+  }
+  if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
+  return MXW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1383,64 +1482,18 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
       (N & 15) || (K & 15) || N > 65536 || K > 65536)
     return MXW_ERR_DIM;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
-  const int64_t grid = mxw_grid_size(E, N, K);
-  if (grid <= 0 || grid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
-  int rc = check_device();
-  if (rc) return rc;
-  Params p;
-  p.A = A;
-  p.sA = sA;
-  p.B = B;
-  p.sB = sB;
-  p.offs = offs;
-  p.out = out;
-  p.E = E;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.tilesN = (N + kTile - 1) / kTile;
-  p.tilesK = (K + kTile - 1) / kTile;
-  // XCD regions: split the tile grid a x b = 8 ways into equal rectangles,
-  // the most square split (fewest distinct A + B stripes per rectangle)
-  p.regN = p.regK = p.regB = p.band = 0;
-  int best = 1 << 30;
-  for (int a = 1; a <= 8; a *= 2) {
-    const int b = 8 / a;
-    if (p.tilesN % a || p.tilesK % b) continue;
-    const int rn = p.tilesN / a, rk = p.tilesK / b;
-    if (rn + rk < best) {
-      best = rn + rk;
-      p.regN = rn;
-      p.regK = rk;
-      p.regB = b;
-    }
-  }
-  if (p.regN) {
-    // about 32 co-resident workgroups per XCD: bands of ~32 / regK rows
-    p.band = (32 + p.regK - 1) / p.regK;
-    if (p.band > p.regN) p.band = p.regN;
-  }
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  p.part = nullptr;
-  p.flags = nullptr;
-  p.hov = kColHov;
-  const int ncol = plan_columns(E, M, N, K, dev < 64 ? g_dev[dev].cus : 0, &p.regions);
-  p.ncol = ncol;
-  if (ncol) {
-    rc = get_workspace(dev, ncol, &p.part, &p.flags);
-    if (rc) return rc;
-    if ((M & 511) == 0)
-      hipLaunchKernelGGL((wgrad_kernel<true, true>), dim3((unsigned)(ncol * kMem)), dim3(kThreads), 0, (hipStream_t)stream, p);
-    else
-      hipLaunchKernelGGL((wgrad_kernel<false, true>), dim3((unsigned)(ncol * kMem)), dim3(kThreads), 0, (hipStream_t)stream, p);
-  } else if ((M & 511) == 0) {
-    hipLaunchKernelGGL((wgrad_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
-  } else {
-    hipLaunchKernelGGL((wgrad_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
-  }
-  if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
-  return MXW_OK;
+  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, stream);
+}
+
+int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
+                       uint16_t* out, void* stream) {
+  if (!A || !B || !offs || !out) return MXW_ERR_NULL;
+  if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS / 2 || (M & 15) || N < 16 || K < 16 ||
+      (N & 15) || (K & 15) || N > 65536 || K > 65536)
+    return MXW_ERR_DIM;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
+  // planned and run in bytes along the token axis: 2 M per row
+  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 1, N, K, out, stream);
 }
 
 int64_t mxw_fwd_grid_size(int E, int R, int N) {
@@ -1510,6 +1563,6 @@ const char* mxw_strerror(int code) {
   }
 }
 
-int mxw_version(void) { return 300; }
+int mxw_version(void) { return 400; }
 
 }  // extern "C"

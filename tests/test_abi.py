@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "mxfp8_wgrad.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(mx\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?!#)\s*[\w\s\*]*?\b([a-z]\w+)\s*\(", text, flags=re.M)))
 
 
 def declared_macros():
@@ -30,7 +30,7 @@ def test_library_built():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"mxfp8_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
+    assert set(names) >= {"mxfp8_wgrad_grouped", "bf16_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
                           "mxw_fwd_grid_size", "mxfp8_quantize_tokens", "mxw_strerror", "mxw_version"}
     lib = ctypes.CDLL(mxw.library_path())
     for n in names:
@@ -78,6 +78,39 @@ P = 0x10000
 ])
 def test_host_argument_checks(args, code):
     assert mxw.mxfp8_wgrad_grouped(*args) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, P, P, 4, 512, 128, 256, P), -1),            # NULL A
+    ((P, 0, P, 4, 512, 128, 256, P), -1),            # NULL B
+    ((P, P, 0, 4, 512, 128, 256, P), -1),            # NULL offs
+    ((P, P, P, 4, 512, 128, 256, 0), -1),            # NULL out
+    ((P, P, P, 0, 512, 128, 256, P), -2),            # E = 0
+    ((P, P, P, 257, 512, 128, 256, P), -2),          # E too large
+    ((P, P, P, 4, 520, 128, 256, P), -2),            # M % 16 != 0
+    ((P, P, P, 4, -16, 128, 256, P), -2),            # M < 0
+    ((P, P, P, 4, 512, 136, 256, P), -2),            # N % 16 != 0
+    ((P, P, P, 4, 512, 128, 0, P), -2),              # K < 16
+    ((P, P, P, 4, 4 * 1024 * 1024 + 16, 128, 256, P), -2),  # M beyond half the MXFP8 token range
+    ((P + 2, P, P, 4, 512, 128, 256, P), -3),        # A misaligned
+    ((P, P + 8, P, 4, 512, 128, 256, P), -3),        # B misaligned
+    ((P, P, P, 4, 512, 128, 256, P + 4), -3),        # out misaligned
+])
+def test_bf16_host_argument_checks(args, code):
+    assert mxw.bf16_wgrad_grouped(*args) == code
+
+
+def test_bf16_python_face_validates():
+    import torch
+    A = torch.zeros((128, 512), dtype=torch.bfloat16)
+    B = torch.zeros((256, 512), dtype=torch.bfloat16)
+    offs = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        mxw.wgrad_bf16(A.float(), B, offs)            # not bf16
+    with pytest.raises(ValueError):
+        mxw.wgrad_bf16(A, B[:, :256].contiguous(), offs)  # M mismatch
+    with pytest.raises(ValueError):
+        mxw.wgrad_bf16(A, B, offs)                    # CPU tensors are refused: no host fallback
 
 
 def test_python_face_validates_shapes():

@@ -1,4 +1,4 @@
-"""Seeded random shapes for all three entry points against the oracle (needs an
+"""Seeded random shapes for every entry point against the oracle (needs an
 MI355X).  Shapes, routings, empty experts, unaligned row boundaries and
 padding garbage are drawn from fixed seeds; every case prints its parameters
 before it launches.  The weight-gradient cases include shapes that select
@@ -103,3 +103,36 @@ def test_quantize_random_shapes(seed):
     rq, rs = oracle.quantize_tokens(x.view(torch.int16).numpy().view(np.uint16), used=used)
     np.testing.assert_array_equal(s.cpu().numpy(), rs)
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bf16_wgrad_random_shapes(seed):
+    rng = np.random.default_rng(2600 + seed)
+    if seed % 4 == 0:  # column mode: long experts, few tiles
+        E = int(rng.integers(1, 4))
+        N = 16 * int(rng.integers(1, 33))
+        K = 16 * int(rng.integers(1, 49))
+        M = 16 * int(rng.integers(4096 * E // 16 + 1, 4096 * E // 16 + 400))
+    else:
+        E = int(rng.integers(1, 41))
+        N = 16 * int(rng.integers(1, 50))
+        K = 16 * int(rng.integers(1, 50))
+        M = 16 * int(rng.integers(1, 200))
+    sizes = random_sizes(rng, E, M, 16)
+    cfg = W.make_bf16(E, N, K, M, sizes, seed=2700 + seed, device=DEV)
+    used = int(sizes.sum())
+    cfg["A"].view(torch.int16)[:, used:] = 0x7FC0  # NaN past the last expert
+    cfg["B"].view(torch.int16)[:, used:] = -128    # 0xFF80, -inf
+    say("bf16 fuzz %d: E=%d N=%d K=%d M=%d used=%d columns(2M)=%d" % (seed, E, N, K, M, used,
+                                                                       mxw.columns(E, 2 * M, N, K)))
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(BF16_NAN)
+    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out)
+    torch.cuda.synchronize()
+    bits = bf16_bits(out)
+    u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.bf16_wgrad_f64(u16(cfg["A"]), u16(cfg["B"]), cfg["offs"].cpu().numpy())
+    check_close(bits, ref, what="bf16 fuzz %d" % seed)
+    for g in range(E):
+        if sizes[g] == 0:
+            assert (bits[g] == 0).all()

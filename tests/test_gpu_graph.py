@@ -73,3 +73,16 @@ def test_quantize_graph_replay():
     s = torch.empty((272, 20), dtype=torch.uint8, device=DEV)
     say("graph quantize")
     replay_check(lambda: mxw.quantize_tokens(x, offs, q=q, s=s), [q, s], "quantize")
+
+
+@pytest.mark.parametrize("mode", ["per_tile", "column"])
+def test_bf16_graph_replay(mode):
+    if mode == "column":
+        cfg = W.make_bf16(2, 512, 768, 16416, [8992, 7392], seed=1303, device=DEV)
+        assert mxw.columns(cfg["E"], 2 * cfg["M"], cfg["N"], cfg["K"]) > 0
+    else:
+        cfg = W.make_bf16(3, 272, 528, 1024, [96, 0, 800], seed=1304, device=DEV)
+        assert mxw.columns(cfg["E"], 2 * cfg["M"], cfg["N"], cfg["K"]) == 0
+    out = torch.empty((cfg["E"], cfg["N"], cfg["K"]), dtype=torch.bfloat16, device=DEV)
+    say("graph bf16 wgrad %s" % mode)
+    replay_check(lambda: mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out), [out], "bf16 wgrad " + mode)
