@@ -28,6 +28,11 @@ dY [M, N] and X [M, K] (bf16, seeded) into its two MXFP8 operands; the metric
 is algorithmic HBM GB/s (2 bytes read, 1 + 1/32 bytes written per element)
 against the 8 TB/s HBM roof.
 
+The same weight gradient on bf16 operands (bf16_wgrad_grouped, the XLA blog's
+contracting ragged dot) is measured with --workload 16b_bf16, 16b_1k_bf16 or
+671b_bf16 (the base workload's shape and routing), against the 2.5 PFLOP/s
+dense BF16 MFMA peak, with torch._grouped_mm timed on the same operands.
+
 For the weight-gradient workloads the line also carries `bf16_context`: the
 same ragged problem in bf16 through torch._grouped_mm (dY^T [N, M] and X
 [M, K], contraction ragged by the same offs, hipBLASLt on ROCm), timed the same
@@ -52,6 +57,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP8 wgrad TFLOP/s (2·M·N·K) at 16B/671B shapes; % of MXFP8 MFMA peak"
 PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 MFMA peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA peak
 PAGES_TFLOPS_16B = 2174.0  # the blog's shipping kernel at the 16B ragged shape, MI355X
 KERNEL_SRC = os.path.join(ROOT, "mxfp8_ragged_grouped_amd", "csrc", "mxfp8_wgrad.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -174,6 +180,85 @@ def bench_rows(args):
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_rows(cfg, *(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
+    print(json.dumps(res))
+
+
+def cpu_baseline_bf16(cfg, A, B, offs, budget_s=25.0):
+    """The bf16 oracle on a bounded sample, chosen as for the MXFP8 weight
+    gradient: every s-th row of A and of B, all routed tokens."""
+    import oracle
+
+    used = float(np.sum(cfg["sizes"]))
+
+    def run(stride):
+        A_s, B_s = np.ascontiguousarray(A[::stride]), np.ascontiguousarray(B[::stride])
+        t0 = time.perf_counter()
+        oracle.bf16_wgrad_f64(A_s, B_s, offs)
+        return time.perf_counter() - t0, A_s.shape[0], B_s.shape[0]
+
+    t_probe = run(8)[0]
+    stride = next(s for s in (1, 2, 4, 8) if t_probe * (8 // s) ** 2 <= budget_s or s == 8)
+    dt, na, nb = run(stride)
+    return {"value": 2.0 * used * na * nb / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "%s: %s of A and of B (%d x %d of %d x %d outputs per expert, all "
+                                        "%d routed tokens), fp64, %.1f s" % (
+                                            cfg["name"], {1: "every row", 2: "every 2nd row", 4: "every 4th row",
+                                                          8: "every 8th row"}[stride], na, nb, cfg["N"], cfg["K"],
+                                            int(used), dt)}
+
+
+def bench_bf16(args):
+    """BF16 contracting ragged dot (bf16_wgrad_grouped) on a named bf16
+    workload, with torch._grouped_mm on the very same operands beside it."""
+    import torch
+
+    import mxfp8_ragged_grouped_amd as mxw
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.make_bf16_config(args.workload, device=dev)
+    E, N, K, M = cfg["E"], cfg["N"], cfg["K"], cfg["M"]
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out, stream=stream)
+
+    ms, wall = time_steps(step, args, stream)
+    flops = W.useful_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "BF16 contracting ragged dot (weight gradient) TFLOP/s (2·M·N·K); % of BF16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->fp32acc->bf16",
+        "data": "synthetic (the base workload's seeded routing, N(0,1) values rounded to bf16, token-contiguous)",
+        "config": {"workload": args.workload, "base": cfg["base"], "E": E, "N": N, "K": K, "M": M,
+                   "busiest_over_mean": round(cfg["skew"], 3), "routing_seed": cfg["routing_seed"],
+                   "value_seed": cfg["value_seed"], "columns": mxw.columns(E, 2 * M, N, K),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(args.workload)},
+        "hbm_gbps_algorithmic": round(W.bf16_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_bf16:
+        # the same operands through torch._grouped_mm (X as a contiguous [M, K])
+        xb = cfg["B"].t().contiguous()
+        try:
+            tms, _ = time_steps(lambda: torch._grouped_mm(cfg["A"], xb, offs=cfg["offs"]), args, stream)
+            ttf = flops / (tms * 1e-3) / 1e12
+            res["torch_grouped_mm"] = {"value": round(ttf, 1), "unit": "TFLOP/s", "ms": round(tms, 4),
+                                       "ours_over_torch": round(tflops / ttf, 3),
+                                       "what": "torch._grouped_mm(A [N, M], X [M, K], offs) on the same bf16 "
+                                               "values, same steps/warmup, same stream, this process"}
+        except Exception as ex:  # not every build has a grouped GEMM for this layout
+            res["torch_grouped_mm"] = {"value": None, "error": str(ex)[:200]}
+        del xb
+    if not args.no_cpu:
+        u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        res["cpu_baseline"] = cpu_baseline_bf16(cfg, u16(cfg["A"]), u16(cfg["B"]), cfg["offs"].cpu().numpy())
     print(json.dumps(res))
 
 
@@ -312,6 +397,9 @@ def main():
         return
     if args.workload in QUANT_WORKLOADS:
         bench_quant(args)
+        return
+    if args.workload in W.BF16_CONFIGS:
+        bench_bf16(args)
         return
 
     dev = torch.device("cuda:0")
