@@ -39,8 +39,13 @@ same ragged problem in bf16 through torch._grouped_mm (dY^T [N, M] and X
 way in the same process, as the pages' "x BF16" comparison (context, not the
 metric).
 
+The weight-gradient lines also carry `power`: socket power, joules per step and
+the mean shader clock over a ~4 s back-to-back run (amdsmi, read-only), and
+the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
+
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
+    --no-power           skip the power leg
     --copy-calibration   run a plain 1 GiB device copy (counter calibration)
 """
 import argparse
@@ -243,6 +248,8 @@ def bench_bf16(args):
         "hbm_gbps_algorithmic": round(W.bf16_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_power:
+        res["power"] = power_leg(step, ms, stream, tflops, PEAK_BF16_TFLOPS)
     if not args.no_bf16:
         # the same operands through torch._grouped_mm (X as a contiguous [M, K])
         xb = cfg["B"].t().contiguous()
@@ -348,6 +355,86 @@ def bf16_context(cfg, ours_tflops, args, stream):
                     "same stream, this process"}
 
 
+def power_leg(step, ms_per_step, stream, tflops=None, peak=None, seconds=4.0):
+    """Socket power, energy per step and shader clock while `step` runs back to
+    back for about `seconds` (amdsmi, read-only).  A sampler thread polls the
+    energy accumulator and the GPU metrics table every 20 ms while the main
+    thread keeps the GPU busy.  The accumulator advances about once a second,
+    so power is taken between its first and last updates inside the busy
+    window (energy difference over the firmware timestamps), and the clock is
+    the mean of the current-GFX-clock readings in that window.  Returns a dict
+    (with "error" if amdsmi is unavailable)."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as ex:  # no amdsmi on this host
+        return {"error": "amdsmi unavailable: %s" % str(ex)[:120]}
+    try:
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", 0),
+                                   getattr(props, "pci_device_id", 0))
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = next((x for x in handles if amdsmi.amdsmi_get_gpu_device_bdf(x).lower().startswith(want)), None)
+        if h is None:
+            return {"error": "no amdsmi handle for PCI %s" % want}
+        limit_w = amdsmi.amdsmi_get_power_info(h).get("power_limit")
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                t = time.perf_counter()
+                try:
+                    e = amdsmi.amdsmi_get_energy_count(h)
+                    gm = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    samples.append((t, e["energy_accumulator"], e["timestamp"], e["counter_resolution"],
+                                    gm.get("current_gfxclk"), gm.get("current_socket_power")))
+                except Exception:
+                    pass
+                stop.wait(0.02)
+
+        n = max(1, int(seconds * 1e3 / ms_per_step))
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        win = [x for x in samples if t0 + 0.3 <= x[0] <= t1]  # skip the ramp-up
+        edges = [x for i, x in enumerate(win) if i == 0 or x[1] != win[i - 1][1]]
+        if len(edges) < 3:
+            return {"error": "too few energy-counter updates in the busy window (%d)" % len(edges)}
+        a, b = edges[1], edges[-1]  # first and last update seen inside the window
+        joules = (b[1] - a[1]) * a[3] * 1e-6
+        secs = (b[2] - a[2]) * 1e-9
+        watts = joules / secs
+        clks = [x[4] for x in win if isinstance(x[4], (int, float)) and x[4] > 0]
+        clk = sum(clks) / len(clks) if clks else None
+        res = {"avg_socket_w": round(watts, 1), "joules_per_step": round(watts * ms_per_step * 1e-3, 4),
+               "gfxclk_mhz_mean": round(clk, 1) if clk else None,
+               "power_limit_w": round(limit_w / 1e6, 1) if isinstance(limit_w, (int, float)) else None,
+               "window_s": round(secs, 3), "steps_run": n,
+               "how": "amdsmi energy accumulator between its first and last update in a ~%.0f s back-to-back run; "
+                      "clock = mean current GFX clock over the same run" % seconds}
+        if clk and tflops and peak:
+            # the peak scales with the shader clock (peak quoted at 2.4 GHz)
+            res["clock_normalised_frac"] = round(tflops / (peak * clk / 2400.0), 4)
+        return res
+    except Exception as ex:
+        return {"error": str(ex)[:200]}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def time_steps(step, args, stream):
     """W untimed steps, then K timed ones between HIP events on `stream`."""
     import torch
@@ -375,6 +462,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 torch._grouped_mm context leg")
+    ap.add_argument("--no-power", action="store_true", help="skip the power / energy / clock leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -446,6 +534,8 @@ def main():
         res["baseline_note"] = ("vs_baseline = value / 2,174 TFLOP/s, the blog's kernel at the 16B ragged shape on "
                                 "MI355X (their routing: linear ramp / ragged draw at 1.5x; ours: seeded Dirichlet "
                                 "at %.2fx)" % cfg["skew"])
+    if not args.no_power:
+        res["power"] = power_leg(step, ms, stream, tflops, PEAK_TFLOPS)
     if not args.no_bf16:
         res["bf16_context"] = bf16_context(cfg, tflops, args, stream)
     if not args.no_cpu:
