@@ -42,8 +42,8 @@ extern "C" {
 #define MXW_ERR_DIM (-2)    /* a size outside the supported range */
 #define MXW_ERR_ALIGN (-3)  /* A, B or out not 16-byte aligned */
 #define MXW_ERR_DEVICE (-4) /* current device is not gfx950, or no device */
-#define MXW_ERR_LAUNCH (-5) /* the kernel launch failed (hipGetLastError), or the
-                               column-mode workspace could not be allocated */
+#define MXW_ERR_LAUNCH (-5) /* a kernel launch failed (hipGetLastError), or a
+                               workspace could not be allocated */
 
 /* Supported ranges (checked on the host, no device access). */
 #define MXW_MAX_EXPERTS 256
@@ -78,8 +78,9 @@ extern "C" {
  * unspecified values but no out-of-bounds access: windows are clamped to
  * [0, M] and every load is range-checked.
  *
- * Effects: enqueues one kernel on `stream` and returns without synchronising.
- * `out` is completely overwritten; an expert with no tokens gets exact +0.0.
+ * Effects: enqueues the kernel (after the scale pre-shuffle below, when it
+ * runs) on `stream` and returns without synchronising.  `out` is completely
+ * overwritten; an expert with no tokens gets exact +0.0.
  * Inputs are never written.  The result is bitwise reproducible run to run:
  * for given (E, M, N, K, offs) every output element is summed in a fixed
  * order, whatever the timing (no atomics on data).
@@ -93,9 +94,25 @@ extern "C" {
  * The library allocates that workspace (128 MiB on a 256-CU device) with
  * hipMalloc on the first column-mode call on a device, synchronising the
  * device once, and keeps it until the process ends; every launch leaves the
- * counters at zero.  Column-mode launches on one device must not overlap in
- * time (launches on different streams would race on the workspace).
- * Otherwise the call allocates nothing and keeps no state.
+ * counters at zero.
+ *
+ * Scale pre-shuffle: when the experts are long (M >= 4096 E) or the scale
+ * rows are not 16-byte aligned (M % 512 != 0), the call first launches a
+ * short kernel that rewrites sA and sB into a device workspace, each 256-row
+ * band's 16-byte groups of 8 K-steps made contiguous (and the scales of
+ * tokens past offs[E-1] cleared), so that the main kernel's scale loads read
+ * consecutive bytes.  The workspace holds (ceil(N/256) + ceil(K/256)) *
+ * ceil(M/512) * 4 KiB (21 MiB at the 16B shape with 196,608 tokens, 88 MiB
+ * at 671B gate/up with 262,144); it is allocated with hipMalloc on the first
+ * such call on a device, grown when a later call needs more (synchronising
+ * the device before the old one is freed) and kept until the process ends.
+ *
+ * Launches of mxfp8_wgrad_grouped or bf16_wgrad_grouped that use a workspace
+ * (column mode, or the scale pre-shuffle) must not overlap in time on one
+ * device: launches on different streams would race on it.  A call that uses
+ * neither allocates nothing and keeps no state.  Capture into a HIP graph
+ * after one eager call of the same or a larger shape (the capture must not
+ * allocate).
  *
  * Returns MXW_OK or a negative MXW_ERR_* code.
  */

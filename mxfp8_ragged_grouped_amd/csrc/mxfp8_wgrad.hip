@@ -63,13 +63,16 @@
 //     its row that holds the pair's 4 bytes (2 K-steps x 2 sub-blocks), shifts
 //     its own sub-block's bytes to bytes 0 and 2, clears dead sub-blocks, and
 //     the MFMA picks byte 0 or 2 with op_sel (blog sections 5.2 and 5.6): no
-//     unpacking and no relayout through LDS.  When every row of the scale
-//     planes starts 16-byte aligned (M a multiple of 512) one 16-byte load per
-//     row brings 8 K-steps of scales (GROUP = true); otherwise the two aligned
-//     dwords around a row's 4 bytes of 2 K-steps are loaded.  A scale load
-//     per row per step would double the number of L1 -> L2 requests of a
-//     step (every lane hits a different row), which measurably slows the
-//     data stream.
+//     unpacking and no relayout through LDS.  One 16-byte load per row brings
+//     8 K-steps of scales (GROUP = true).  In the caller's planes those 16
+//     bytes of 256 rows lie in 256 cache lines, and at long experts that
+//     costs the weight gradient ~6%; it then first rewrites the planes so that
+//     a band's groups are contiguous (scale_shuffle_kernel).  The same runs
+//     when scale rows are not 16-byte aligned (M % 512 != 0); the row-ragged
+//     GEMM reads its planes directly, with the two aligned dwords around a
+//     row's 4 bytes of 2 K-steps when C % 512 != 0.  A scale load per row per
+//     step would double the number of L1 -> L2 requests of a step (every lane
+//     hits a different row), which measurably slows the data stream.
 //   * contraction: v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
 //     per-32 E8M0 scales, FP32 accumulation (blog section 3).  Operand roles
 //     are swapped (B feeds the instruction's first operand) so that each lane
@@ -135,6 +138,8 @@ constexpr int kColHov = 3;
 // tokens; below that the per-piece costs outweigh the better packing
 constexpr int kColWaves = 4;
 constexpr int kColTokens = 8192;
+// the weight gradient shuffles its scale planes when M >= kShufTokens * E
+constexpr int kShufTokens = 4096;
 
 // LDS layout (159 KiB of the 160 KiB per CU).
 struct Smem {
@@ -317,6 +322,12 @@ struct Params {
   // each column on one XCD (one workgroup per CU); the (expert, region) work
   // sequence is cut into ncol equal spans, one per column, and a region cut
   // between columns is summed through FP32 partial tiles
+  // weight gradient on E4M3 operands: the scale planes rewritten per call by
+  // scale_shuffle_kernel as [256-row band][group of 8 K-steps][256 rows][16
+  // bytes], sgroups groups per band (see there)
+  const uint8_t* sAs;
+  const uint8_t* sBs;
+  int sgroups;
   float* part;      // [ncol][2][kMem][kTile * kTile] partial tiles (a column's first / last piece)
   uint32_t* flags;  // [ncol][kMem] arrival counters of cut regions, 0 between launches
   int ncol;
@@ -424,16 +435,23 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   }
 
   // ---- buffer resources, rebased to this tile's 256-row bands ----------------
+  // SHUF: the weight gradient's grouped scale loads read the shuffled planes,
+  // in which the 16-byte groups of a band's 256 rows are contiguous (when
+  // the host made them: p.sAs != null)
+  const bool SHUF = GROUP && !ROWS && !BF && p.sAs != nullptr;
   const uint32_t sbytes = (uint32_t)M >> 5;  // scale bytes per row
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + arow * M, (uint32_t)rowsA * (uint32_t)M);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + brow * M, (uint32_t)rowsB * (uint32_t)M);
   // scale planes are read as whole dwords; rounding the range up to 4 bytes
   // keeps every dword entirely inside or outside it (bytes past the plane
   // belong to tokens >= M, which are always masked)
+  const uint32_t band_bytes = (uint32_t)p.sgroups * (uint32_t)(kTile * 16);
   const __amdgpu_buffer_rsrc_t rsA =
-      make_rsrc(p.sA + arow * sbytes, ((uint32_t)rowsA * sbytes + 3u) & ~3u);
+      SHUF ? make_rsrc(p.sAs + (size_t)pc.tn * band_bytes, band_bytes)
+           : make_rsrc(p.sA + arow * sbytes, ((uint32_t)rowsA * sbytes + 3u) & ~3u);
   const __amdgpu_buffer_rsrc_t rsB =
-      make_rsrc(p.sB + brow * sbytes, ((uint32_t)rowsB * sbytes + 3u) & ~3u);
+      SHUF ? make_rsrc(p.sBs + (size_t)pc.tk * band_bytes, band_bytes)
+           : make_rsrc(p.sB + brow * sbytes, ((uint32_t)rowsB * sbytes + 3u) & ~3u);
 
   // ---- per-lane DMA geometry -------------------------------------------------
   // Data: a stage holds a pair of K-steps (128 tokens, one cache line per row).
@@ -456,8 +474,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     vrow[q] = (uint32_t)((wave * 8 + ((q + rot) & 7)) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
-  // Scales: lane l of wave w fetches scale row 64 w + l.
-  const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * sbytes;
+  // Scales: lane l of wave w fetches scale row 64 w + l (shuffled planes: the
+  // 16 bytes of that row in each group of 4 KiB)
+  const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * (SHUF ? 16u : sbytes);
   const int sbl_e = ch_e >> 1, sbl_o = ch_o >> 1;  // this lane's 32-token sub-block within a pair
   const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[0][0][wave * 8 * 1024]));
   // Column mode L2 prefetch.  The tiles of a region that share an A (B) stripe
@@ -508,7 +527,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // they only reach steps past M, whose sub-blocks are all dead)
   auto dma_scale_grp = [&](int g, int op) {
     const uint32_t dst = lds_addr(&sm.raw[(((g % 3) * 2 + op) * kTile + wave * 64) * 4]);
-    dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), srow_off + 16u * (uint32_t)g, 0u);
+    dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst),
+          srow_off + (SHUF ? (uint32_t)(kTile * 16) : 16u) * (uint32_t)g, 0u);
   };
   auto dma_scales = [&](int grp_idx, bool real) {
     {
@@ -1227,6 +1247,70 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
 // position c ^ ((r / 2) % 8) (the 16-byte writes of 16 lanes, rows r .. r+15
 // at one chunk, then hit 16 distinct bank groups), so that every global
 // store writes whole 128-byte lines of q.
+// Per-call scale pre-shuffle for the weight gradient (blog section 5.6 names
+// a per-call scale pre-shuffle; this one exists for the memory path).  In the
+// caller's planes [R, M/32] a workgroup's 16-byte group of 8 K-steps sits in
+// 256 different rows, so each scale load of the K-loop touches 64 cache lines
+// per wave for 1 KiB (its data loads touch 8), and the address unit and the L1
+// fill path pay per line: measured, that costs the weight gradient ~6% at the
+// 16B shape.  Rewritten as [band b = r / 256][group G][r % 256][16 bytes],
+// the same loads read 1 KiB of consecutive bytes.  Rows past R, bytes past
+// M/32 and the sub-blocks of tokens past offs[E-1] (padding, which may hold
+// 0xFF = NaN scales) become 0.  One workgroup per (operand, band, 8 groups):
+// each wave reads 8 rows x 128 bytes at a time (consecutive lanes, consecutive
+// bytes) and writes, per group, 8 rows x 16 bytes contiguous.
+struct ShufArgs {
+  const uint8_t* s[2];  // A, B scale planes [R, M/32]
+  uint8_t* out[2];
+  int R[2];             // rows of A, B
+  int bands[2];         // ceil(R / 256)
+  int M, groups, octets;
+  const int32_t* offs;
+  int E;
+};
+
+__global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
+  int blk = blockIdx.x;
+  const int op = blk >= a.bands[0] * a.octets;
+  if (op) blk -= a.bands[0] * a.octets;
+  const int b = blk / a.octets, o = blk - b * a.octets;
+  const uint32_t sb = (uint32_t)a.M >> 5;  // bytes per row
+  const int R = a.R[op];
+  int used = a.offs[a.E - 1];
+  used = min(max(used, 0), a.M);
+  const int qlim = used >> 5;  // sub-blocks (bytes) of a row that belong to an expert
+  // this band's rows of the plane, the size rounded up to a dword (offsets
+  // below are dword-aligned from this base: every dword is entirely inside
+  // or outside the checked range)
+  const int rows = min(kTile, R - b * kTile);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.s[op] + (size_t)b * kTile * sb, ((uint32_t)rows * sb + 3u) & ~3u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = i * 256 + (int)threadIdx.x;  // chunk: row c / 8, group 8 o + c % 8
+    const int r = c >> 3, G = 8 * o + (c & 7);
+    if (G >= a.groups) continue;
+    const int q0 = 16 * G;  // first sub-block of the chunk
+    const int nvalid = r < rows ? min(max(qlim - q0, 0), 16) : 0;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (nvalid > 0) {
+      // the 5 dwords around the chunk, funnel-shifted
+      const uint32_t off = (uint32_t)r * sb + (uint32_t)q0;
+      const uint32_t al = off & ~3u, sh = (off & 3u) * 8u;
+      uint32_t v[5];
+#pragma unroll
+      for (int d = 0; d < 5; ++d) v[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(al + 4u * d), 0, 0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int keep = min(max(nvalid - 4 * d, 0), 4);  // valid bytes in this dword
+        const uint32_t x = __builtin_amdgcn_alignbit(v[d + 1], v[d], sh);
+        w[d] = keep == 4 ? x : (x & ((1u << (8 * keep)) - 1u));
+      }
+    }
+    *(v4i*)(a.out[op] + (((size_t)b * a.groups + G) * kTile + r) * 16) = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  }
+}
+
 constexpr int kQTok = 128, kQHid = 128;
 struct QSmem {
   uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (32 KiB)
@@ -1353,6 +1437,38 @@ int get_workspace(int dev, int ncol, float** part, uint32_t** flags) {
   return MXW_OK;
 }
 
+// Shuffled scale planes of the weight gradient, one buffer per device
+// (shared by every call on it, like the column-mode workspace): grown on
+// demand (the device is synchronised before an old buffer is freed) and kept
+// until the process ends.
+struct ScaleWs {
+  uint8_t* buf;
+  size_t bytes;
+};
+ScaleWs g_scale_ws[64];
+std::mutex g_scale_mutex;
+
+int get_scale_workspace(int dev, size_t bytes, uint8_t** out) {
+  if (dev < 0 || dev >= 64) return MXW_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scale_mutex);
+  ScaleWs& w = g_scale_ws[dev];
+  if (w.bytes < bytes) {
+    if (w.buf) {
+      if (hipDeviceSynchronize() != hipSuccess) return MXW_ERR_LAUNCH;
+      (void)hipFree(w.buf);
+      w.buf = nullptr;
+      w.bytes = 0;
+    }
+    const size_t want = (bytes + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);  // whole MiB
+    void* ptr = nullptr;
+    if (hipMalloc(&ptr, want) != hipSuccess) return MXW_ERR_LAUNCH;
+    w.buf = (uint8_t*)ptr;
+    w.bytes = want;
+  }
+  *out = w.buf;
+  return MXW_OK;
+}
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXW_ERR_DEVICE;
@@ -1446,12 +1562,46 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   if (tshift) {
     if (ncol) hipLaunchKernelGGL((wgrad_kernel<false, true, true>), g, blk, 0, st, p);
     else hipLaunchKernelGGL((wgrad_kernel<false, false, true>), g, blk, 0, st, p);
-  } else if ((Mb & 511) == 0) {
+  } else {
+    // E4M3: when the experts are long (M >= 4096 E) or the scale rows are not
+    // 16-byte aligned (M % 512 != 0), shuffle the scale planes and take the
+    // grouped path on them; otherwise read the caller's planes directly
+    // (grouped loads; at short experts the extra pass costs more than the
+    // scattered scale loads do: ~4 us against ~1 us at 1,024 tokens per expert)
+    if ((Mb & 511) == 0 && (int64_t)Mb < (int64_t)kShufTokens * E) {
+      p.sAs = p.sBs = nullptr;
+      p.sgroups = 0;
+      if (ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
+      else hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
+      if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
+      return MXW_OK;
+    }
+    ShufArgs sa;
+    sa.s[0] = sA;
+    sa.s[1] = sB;
+    sa.R[0] = N;
+    sa.R[1] = K;
+    sa.bands[0] = p.tilesN;
+    sa.bands[1] = p.tilesK;
+    sa.M = Mb;
+    sa.groups = (Mb + 511) / 512 > 0 ? (Mb + 511) / 512 : 1;
+    sa.octets = (sa.groups + 7) / 8;
+    sa.offs = offs;
+    sa.E = E;
+    const size_t bytesA = (size_t)sa.bands[0] * sa.groups * kTile * 16;
+    const size_t bytesB = (size_t)sa.bands[1] * sa.groups * kTile * 16;
+    uint8_t* ws = nullptr;
+    rc = get_scale_workspace(dev, bytesA + bytesB, &ws);
+    if (rc) return rc;
+    sa.out[0] = ws;
+    sa.out[1] = ws + bytesA;
+    p.sAs = sa.out[0];
+    p.sBs = sa.out[1];
+    p.sgroups = sa.groups;
+    hipLaunchKernelGGL(scale_shuffle_kernel, dim3((unsigned)((sa.bands[0] + sa.bands[1]) * sa.octets)), dim3(256), 0, st,
+                       sa);
     if (ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
     else hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
-  } else {
-    if (ncol) hipLaunchKernelGGL((wgrad_kernel<false, true>), g, blk, 0, st, p);
-    else hipLaunchKernelGGL((wgrad_kernel<false, false>), g, blk, 0, st, p);
   }
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
   return MXW_OK;
