@@ -526,7 +526,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "kernels_per_call": 2 if mxw.scale_shuffle(E, M) else 1,
+                     "timed": "the whole call (scale_shuffle_kernel, when it runs, then wgrad_kernel); traffic is "
+                              "wgrad_kernel's"},
         "hbm_gbps_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
     }

@@ -174,6 +174,14 @@ int64_t mxw_grid_size(int E, int N, int K);
 int mxw_columns(int E, int M, int N, int K);
 
 /*
+ * mxw_scale_shuffle -- 1 if mxfp8_wgrad_grouped with (E, M) runs the scale
+ * pre-shuffle kernel before the main kernel (M >= 4096 E or M % 512 != 0),
+ * 0 if it launches the main kernel alone, MXW_ERR_DIM for invalid sizes.
+ * Host-only: no device access.
+ */
+int mxw_scale_shuffle(int E, int M);
+
+/*
  * mxfp8_grouped_fwd -- the row-ragged MXFP8 grouped GEMM: the forward and
  * data-gradient GEMMs of the same MoE layer.  (Blog section 1: the weight
  * gradient is one of three grouped GEMMs per expert layer; the other two keep

@@ -33,7 +33,7 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["wgrad", "mxfp8_wgrad_grouped", "wgrad_bf16", "bf16_wgrad_grouped", "grid_size", "columns", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "wgrad_bf16", "bf16_wgrad_grouped", "grid_size", "columns", "scale_shuffle", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
            "quantize_tokens", "mxfp8_quantize_tokens", "strerror", "version", "library_path", "MxwError"]
 
 _lib = None
@@ -68,6 +68,8 @@ def _load():
     lib.mxw_version.argtypes = []
     lib.mxw_columns.restype = I
     lib.mxw_columns.argtypes = [I, I, I, I]
+    lib.mxw_scale_shuffle.restype = I
+    lib.mxw_scale_shuffle.argtypes = [I, I]
     lib.mxfp8_grouped_fwd.restype = I
     lib.mxfp8_grouped_fwd.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
     lib.mxw_fwd_grid_size.restype = ctypes.c_int64
@@ -97,6 +99,15 @@ def columns(E, M, N, K):
     if rc < 0:
         raise MxwError("mxw_columns failed: %s" % strerror(rc))
     return rc
+
+
+def scale_shuffle(E, M):
+    """True if an MXFP8 weight-gradient call of (E, M) runs the scale
+    pre-shuffle kernel before the main kernel."""
+    rc = _load().mxw_scale_shuffle(int(E), int(M))
+    if rc < 0:
+        raise MxwError("mxw_scale_shuffle failed: %s" % strerror(rc))
+    return bool(rc)
 
 
 def mxfp8_wgrad_grouped(A, sA, B, sB, offs, E, M, N, K, out, stream=0):

@@ -1294,17 +1294,28 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
     const int nvalid = r < rows ? min(max(qlim - q0, 0), 16) : 0;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (nvalid > 0) {
-      // the 5 dwords around the chunk, funnel-shifted
       const uint32_t off = (uint32_t)r * sb + (uint32_t)q0;
-      const uint32_t al = off & ~3u, sh = (off & 3u) * 8u;
-      uint32_t v[5];
+      uint32_t x[4];
+      if ((sb & 15u) == 0) {
+        // 16-byte aligned rows (M % 512 == 0): one load per chunk
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        x[0] = (uint32_t)v.x;
+        x[1] = (uint32_t)v.y;
+        x[2] = (uint32_t)v.z;
+        x[3] = (uint32_t)v.w;
+      } else {
+        // the 5 dwords around the chunk, funnel-shifted
+        const uint32_t al = off & ~3u, sh = (off & 3u) * 8u;
+        uint32_t v[5];
 #pragma unroll
-      for (int d = 0; d < 5; ++d) v[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(al + 4u * d), 0, 0);
+        for (int d = 0; d < 5; ++d) v[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(al + 4u * d), 0, 0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) x[d] = __builtin_amdgcn_alignbit(v[d + 1], v[d], sh);
+      }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int keep = min(max(nvalid - 4 * d, 0), 4);  // valid bytes in this dword
-        const uint32_t x = __builtin_amdgcn_alignbit(v[d + 1], v[d], sh);
-        w[d] = keep == 4 ? x : (x & ((1u << (8 * keep)) - 1u));
+        w[d] = keep == 4 ? x[d] : (x[d] & ((1u << (8 * keep)) - 1u));
       }
     }
     *(v4i*)(a.out[op] + (((size_t)b * a.groups + G) * kTile + r) * 16) = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
@@ -1469,6 +1480,9 @@ int get_scale_workspace(int dev, size_t bytes, uint8_t** out) {
   return MXW_OK;
 }
 
+// whether an E4M3 weight-gradient call of (E, M) pre-shuffles its scales
+bool uses_scale_shuffle(int E, int M) { return (M & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXW_ERR_DEVICE;
@@ -1568,7 +1582,7 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     // grouped path on them; otherwise read the caller's planes directly
     // (grouped loads; at short experts the extra pass costs more than the
     // scattered scale loads do: ~4 us against ~1 us at 1,024 tokens per expert)
-    if ((Mb & 511) == 0 && (int64_t)Mb < (int64_t)kShufTokens * E) {
+    if (!uses_scale_shuffle(E, Mb)) {
       p.sAs = p.sBs = nullptr;
       p.sgroups = 0;
       if (ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
@@ -1618,6 +1632,11 @@ int mxw_columns(int E, int M, int N, int K) {
   int dev = 0, regions = 0;
   (void)hipGetDevice(&dev);
   return plan_columns(E, M, N, K, dev < 64 ? g_dev[dev].cus : 0, &regions);
+}
+
+int mxw_scale_shuffle(int E, int M) {
+  if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || (M & 31)) return MXW_ERR_DIM;
+  return uses_scale_shuffle(E, M) ? 1 : 0;
 }
 
 int64_t mxw_grid_size(int E, int N, int K) {

@@ -129,6 +129,19 @@ def test_python_face_validates_shapes():
         mxw.wgrad(A, sA, B, sB, offs.to(torch.int64))
 
 
+def test_scale_shuffle_rule():
+    """The pre-shuffle runs at long experts (M >= 4096 E) or unaligned scale
+    rows (M % 512 != 0); host-only, no device needed."""
+    assert mxw.scale_shuffle(8, 196608) and mxw.scale_shuffle(32, 262144)
+    assert not mxw.scale_shuffle(8, 8192)          # 1,024 tokens per expert, aligned rows
+    assert mxw.scale_shuffle(8, 8192 + 32)         # M % 512 != 0
+    assert mxw.scale_shuffle(1, 4096) and not mxw.scale_shuffle(2, 4096)
+    with pytest.raises(mxw.MxwError):
+        mxw.scale_shuffle(0, 512)
+    with pytest.raises(mxw.MxwError):
+        mxw.scale_shuffle(4, 500)
+
+
 def test_columns_host_checks():
     """mxw_columns rejects invalid sizes on the host, before any device query."""
     lib = ctypes.CDLL(mxw.library_path())
