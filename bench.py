@@ -40,8 +40,9 @@ way in the same process, as the pages' "x BF16" comparison (context, not the
 metric).
 
 The weight-gradient lines also carry `power`: socket power, joules per step and
-the mean shader clock over a ~4 s back-to-back run (amdsmi, read-only), and
-the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
+the mean shader clock over a ~4 s back-to-back run (amdsmi, read-only), the
+clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz), and the
+time per step sustained over that run (HIP events around all of it).
 
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
@@ -399,11 +400,16 @@ def power_leg(step, ms_per_step, stream, tflops=None, peak=None, seconds=4.0):
         torch.cuda.synchronize()
         th = threading.Thread(target=sampler, daemon=True)
         th.start()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        ev0.record(stream)
         for _ in range(n):
             step()
+        ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        sustained_ms = ev0.elapsed_time(ev1) / n
         stop.set()
         th.join()
         win = [x for x in samples if t0 + 0.3 <= x[0] <= t1]  # skip the ramp-up
@@ -416,15 +422,20 @@ def power_leg(step, ms_per_step, stream, tflops=None, peak=None, seconds=4.0):
         watts = joules / secs
         clks = [x[4] for x in win if isinstance(x[4], (int, float)) and x[4] > 0]
         clk = sum(clks) / len(clks) if clks else None
-        res = {"avg_socket_w": round(watts, 1), "joules_per_step": round(watts * ms_per_step * 1e-3, 4),
+        res = {"avg_socket_w": round(watts, 1), "joules_per_step": round(watts * sustained_ms * 1e-3, 4),
                "gfxclk_mhz_mean": round(clk, 1) if clk else None,
                "power_limit_w": round(limit_w / 1e6, 1) if isinstance(limit_w, (int, float)) else None,
                "window_s": round(secs, 3), "steps_run": n,
+               "sustained_ms_per_step": round(sustained_ms, 5),
                "how": "amdsmi energy accumulator between its first and last update in a ~%.0f s back-to-back run; "
-                      "clock = mean current GFX clock over the same run" % seconds}
+                      "clock = mean current GFX clock over the same run; joules = power x sustained time per "
+                      "step" % seconds}
+        if tflops:
+            res["sustained_tflops"] = round(tflops * ms_per_step / sustained_ms, 2)
         if clk and tflops and peak:
-            # the peak scales with the shader clock (peak quoted at 2.4 GHz)
-            res["clock_normalised_frac"] = round(tflops / (peak * clk / 2400.0), 4)
+            # over the same run as the clock; the peak scales with the shader
+            # clock (quoted at 2.4 GHz)
+            res["clock_normalised_frac"] = round(res["sustained_tflops"] / (peak * clk / 2400.0), 4)
         return res
     except Exception as ex:
         return {"error": str(ex)[:200]}
