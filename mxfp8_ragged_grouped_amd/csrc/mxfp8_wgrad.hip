@@ -140,6 +140,12 @@ constexpr int kColWaves = 4;
 constexpr int kColTokens = 8192;
 // the weight gradient shuffles its scale planes when M >= kShufTokens * E
 constexpr int kShufTokens = 4096;
+// row-ragged GEMM: whole-tile scale blocks in the raw area when C <= kWholeC
+// (256 rows x C / 32 bytes per operand, plus the dword read past a row's last
+// pair, within kWholeOp dwords each)
+constexpr int kWholeC = 1504;
+constexpr int kWholeOp = 3072;
+static_assert(kTile * (kWholeC / 32) / 4 + 2 <= kWholeOp, "whole-tile scale block fits");
 
 // LDS layout (159 KiB of the 160 KiB per CU).
 struct Smem {
@@ -400,7 +406,11 @@ struct Piece {
 // v_mfma_f32_32x32x16_bf16 on the halves of the fragments that the E4M3
 // instruction takes whole: the same bytes per clock, at twice the
 // instruction count and half the FLOP per byte.
-template <bool GROUP, bool COL, bool ROWS, bool BF = false>
+// WHOLE (row-ragged GEMM with C <= kWholeC): the tile's whole scale blocks
+// (its 256 A rows and 256 B rows are consecutive rows of the planes, so each
+// block is one contiguous range of 256 C / 32 bytes) are DMA'd once, in the
+// prologue, with coalesced dword loads; the K-loop then loads no scales.
+template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
   int tid = threadIdx.x;
   // opaque per piece: nothing derived from the thread index is hoisted out of
@@ -521,7 +531,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // time) so that every step issues the same count.
   constexpr int kGroupSteps = GROUP ? 8 : 2;
   constexpr int kAhead = GROUP ? 1 : 3;
-  constexpr int kScaleDma = BF ? 0 : (GROUP ? 2 : 4);
+  constexpr int kScaleDma = (BF || WHOLE) ? 0 : (GROUP ? 2 : 4);
   // grouped: one operand's 16 bytes of group g for this lane's row, into
   // slot g % 3 (groups past the row's end read other rows' bytes or nothing;
   // they only reach steps past M, whose sub-blocks are all dead)
@@ -598,6 +608,15 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     const int G0 = s0 / kGroupSteps;
     if (BF) {
       // no scales
+    } else if (WHOLE) {
+      // A's block into raw[0 ..), B's into raw[kWholeOp ..), 256 bytes per
+      // instruction (each dword entirely inside or outside the checked range)
+      const int nA = (int)((kTile * sbytes + 255u) >> 8);
+      for (int k = wave; k < 2 * nA; k += 4) {
+        const int op = k >= nA, kk = k - op * nA;
+        const uint32_t dst = lds_addr(&sm.raw[op * kWholeOp + kk * 64]);
+        dma4(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), (uint32_t)kk * 256u + 4u * (uint32_t)lane);
+      }
     } else if (GROUP) {
       // groups G0 and G0 + 1; the loop fetches group G + 2 for both operands
       // during the two iterations that start in group G
@@ -613,9 +632,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     for (int i = 0; i < kDataDma; ++i) dma_pair(i, 0, P0, l0);
 #pragma unroll
     for (int i = 0; i < kOddLoads; ++i) dma_pair(i, 1, P0 + 1, l1);
-    if (!GROUP && !BF) dma_scales(0, false);
+    if (!GROUP && !BF && !WHOLE) dma_scales(0, false);
   }
-  wait_vm<(GROUP || BF) ? kOddLoads : kOddLoads + kSlot>();  // scales and pair s0/2 landed (this wave)
+  wait_vm<(GROUP || BF || WHOLE) ? kOddLoads : kOddLoads + kSlot>();  // scales and pair s0/2 landed (this wave)
   __syncthreads();
 
   // Scale registers.  In lane l the MFMA takes the E8M0 byte of row l % 32 and
@@ -634,7 +653,12 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     for (int i = 0; i < 4; ++i) {
       const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
       uint32_t a, b;
-      if (GROUP) {
+      if (WHOLE) {
+        // the 4 bytes of steps x, x + 1 of each row (x is even)
+        const uint32_t ba = (uint32_t)RA * sbytes + 2u * (uint32_t)x, bb = (uint32_t)RB * sbytes + 2u * (uint32_t)x;
+        a = __builtin_amdgcn_alignbit(sm.raw[(ba >> 2) + 1], sm.raw[ba >> 2], (ba & 3u) * 8u);
+        b = __builtin_amdgcn_alignbit(sm.raw[kWholeOp + (bb >> 2) + 1], sm.raw[kWholeOp + (bb >> 2)], (bb & 3u) * 8u);
+      } else if (GROUP) {
         const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
         a = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
         b = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
@@ -753,7 +777,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           // after the previous (even) step's data loads: its scale loads
           // (paired: kSlot; grouped: one at u = 0) and, in column mode, its
           // kPrefetch prefetches
-          if (BF) wait_vm<COL ? kPrefetch : 0>();
+          if (BF || WHOLE) wait_vm<COL ? kPrefetch : 0>();
           else if (!GROUP) wait_vm<kSlot + (COL ? kPrefetch : 0)>();
           else if (u == 1) wait_vm<1 + (COL ? kPrefetch : 0)>();
           else wait_vm<COL ? kPrefetch : 0>();
@@ -796,7 +820,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           asm volatile("" : "+s"(sq));
           read_raw(sq + 1, rawa, rawb);
         }
-        if (!BF && m == 15) {  // after the step's data loads (vmcnt order)
+        if (!BF && !WHOLE && m == 15) {  // after the step's data loads (vmcnt order)
           if (!GROUP) {
             dma_scales(sgrp, sreal);
           } else if (u == 0) {
@@ -1169,7 +1193,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
 // a row tile (sharing its A rows) and the row tiles of an expert (sharing its
 // B) meet in one L2.  The grid is sized on the host for the most row tiles
 // any offs can give (R / 256 + E); blocks past the actual count exit.
-template <bool GROUP>
+template <bool GROUP, bool WHOLE = false>
 __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int tid = threadIdx.x;
@@ -1226,7 +1250,7 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
   pc.ar0 = __builtin_amdgcn_readfirstlane(sm.start[g]) + (mt - __builtin_amdgcn_readfirstlane(sm.pre[g])) * kTile;
   pc.ra = min(kTile, __builtin_amdgcn_readfirstlane(sm.start[g]) + __builtin_amdgcn_readfirstlane(sm.len[g]) - pc.ar0);
   __syncthreads();  // the scan's LDS words are not reused below, but keep the waves together
-  run_piece<GROUP, false, true>(p, sm, pc);
+  run_piece<GROUP, false, true, false, WHOLE>(p, sm, pc);
 }
 
 // ---- token-axis MXFP8 quantiser --------------------------------------------------
@@ -1696,7 +1720,9 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
   p.R = R;
   p.tilesN = (N + kTile - 1) / kTile;
   p.tilesK = 0;
-  if ((C & 511) == 0)
+  if (C <= kWholeC)
+    hipLaunchKernelGGL((rows_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  else if ((C & 511) == 0)
     hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   else
     hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);

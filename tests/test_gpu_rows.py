@@ -56,6 +56,9 @@ ROWS_CASES = [
     (2, 600, 512, 256, [512, 88]),              # C % 512 == 0 (grouped scale path)
     (5, 1024, 1408, 336, [200, 0, 0, 600, 224]),  # the 16B down-projection width as C
     (6, 520, 2048, 1408, [100, 32, 0, 200, 96, 64]),  # 16B gate/up widths
+    (3, 520, 1440, 272, [0, 260, 200]),         # whole-tile scale blocks, 45-byte scale rows (odd)
+    (2, 600, 1504, 128, [300, 257]),            # the largest C with whole-tile scale blocks
+    (2, 300, 1568, 160, [150, 100]),            # C % 512 != 0 above it: the paired scale path
 ]
 
 
