@@ -1347,7 +1347,10 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
 }
 
 constexpr int kQTok = 128, kQHid = 128;
-struct QSmem {
+// The codes overwrite the bf16 tile once every thread holds its encoded
+// blocks in registers: 32 KiB per workgroup, 5 workgroups per CU (3 with
+// separate areas).
+union QSmem {
   uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (32 KiB)
   uint8_t q[kQHid][kQTok];   // the codes, hidden rows, swizzled chunks (16 KiB)
 };
@@ -1383,6 +1386,8 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
   // ---- encode: thread (h, b0) does column h of blocks b0 and b0 + 2 --------------
   {
     const int h = tid & 127, b0 = tid >> 7;
+    uint32_t wq[2][8];
+    int sq[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int b = b0 + 2 * bb;
@@ -1397,7 +1402,6 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
       int sb = amax == 0.0f ? 127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8 + 127;
       sb = min(max(sb, 0), 254);
       const int sh = 127 - sb;
-      uint32_t w[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float y[4];
@@ -1408,12 +1412,19 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
         // a code of magnitude 0 (including -0) becomes +0
         const uint32_t z = (uint32_t)c & 0x7F7F7F7Fu;
         const uint32_t nz = ((z + 0x7F7F7F7Fu) & 0x80808080u) >> 7;
-        w[j] = (uint32_t)c & (nz * 0xFFu);
+        wq[bb][j] = (uint32_t)c & (nz * 0xFFu);
       }
-      const int sw = (h >> 1) & 7;
+      sq[bb] = sb;
+    }
+    __syncthreads();  // every thread has read its columns of the bf16 tile
+    const int sw = (h >> 1) & 7;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = b0 + 2 * bb;
+      const uint32_t* w = wq[bb];
       *(v4i*)&sm.q[h][((2 * b) ^ sw) * 16] = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       *(v4i*)&sm.q[h][((2 * b + 1) ^ sw) * 16] = (v4i){(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-      if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(M >> 5) + (m0 >> 5) + b] = (uint8_t)sb;
+      if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(M >> 5) + (m0 >> 5) + b] = (uint8_t)sq[bb];
     }
   }
   __syncthreads();
