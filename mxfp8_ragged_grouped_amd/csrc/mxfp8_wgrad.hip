@@ -1346,13 +1346,12 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
   }
 }
 
-constexpr int kQTok = 128, kQHid = 128;
+constexpr int kQTok = 128, kQHid = 64;
 // The codes overwrite the bf16 tile once every thread holds its encoded
-// blocks in registers: 32 KiB per workgroup, 5 workgroups per CU (3 with
-// separate areas).
+// block in registers: 16 KiB per workgroup.
 union QSmem {
-  uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (32 KiB)
-  uint8_t q[kQHid][kQTok];   // the codes, hidden rows, swizzled chunks (16 KiB)
+  uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (16 KiB)
+  uint8_t q[kQHid][kQTok];   // the codes, hidden rows, swizzled chunks (8 KiB)
 };
 
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
@@ -1364,73 +1363,63 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
   int used = M;
   if (offs) used = min(max(offs[E - 1], 0), M);
   used = __builtin_amdgcn_readfirstlane(used);
-  // ---- load: chunk c = 256 k + tid is token row c / 16, hidden h0 + 8 (c % 16);
-  // rows at or past `used` are outside the descriptor's range and read as 0
+  // ---- load: chunk c = 256 k + tid is token row c / 8, hidden h0 + 8 (c % 8)
+  // (one 128-byte line per row); rows at or past `used` are outside the
+  // descriptor's range and read as 0
   {
     const int rows = max(0, min(kQTok, used - m0));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)m0 * H, (uint32_t)rows * (uint32_t)H * 2u);
-    v4i v[8];
+    v4i v[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = k * 256 + tid, r = c >> 4, h = h0 + (c & 15) * 8;
+    for (int k = 0; k < 4; ++k) {
+      const int c = k * 256 + tid, r = c >> 3, h = h0 + (c & 7) * 8;
       const uint32_t off = h < H ? ((uint32_t)r * (uint32_t)H + (uint32_t)h) * 2u : kOob;
       v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       const int c = k * 256 + tid;
-      *(v4i*)&sm.x[c >> 4][(c & 15) * 8] = v[k];
+      *(v4i*)&sm.x[c >> 3][(c & 7) * 8] = v[k];
     }
   }
   __syncthreads();
-  // ---- encode: thread (h, b0) does column h of blocks b0 and b0 + 2 --------------
+  // ---- encode: thread (h, b) does column h of 32-token block b -------------------
   {
-    const int h = tid & 127, b0 = tid >> 7;
-    uint32_t wq[2][8];
-    int sq[2];
+    const int h = tid & 63, b = tid >> 6;
+    uint32_t wq[8];
+    float v[32];
+    float amax = 0.0f;
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int b = b0 + 2 * bb;
-      float v[32];
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        v[i] = __builtin_bit_cast(float, (uint32_t)sm.x[b * 32 + i][h] << 16);
-        amax = fmaxf(amax, fabsf(v[i]));
-      }
-      // floor(log2 amax) = frexp exponent - 1 (exact, subnormals included)
-      int sb = amax == 0.0f ? 127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8 + 127;
-      sb = min(max(sb, 0), 254);
-      const int sh = 127 - sb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float y[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__builtin_ldexpf(v[4 * j + t], sh), -448.0f), 448.0f);
-        int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
-        // a code of magnitude 0 (including -0) becomes +0
-        const uint32_t z = (uint32_t)c & 0x7F7F7F7Fu;
-        const uint32_t nz = ((z + 0x7F7F7F7Fu) & 0x80808080u) >> 7;
-        wq[bb][j] = (uint32_t)c & (nz * 0xFFu);
-      }
-      sq[bb] = sb;
+    for (int i = 0; i < 32; ++i) {
+      v[i] = __builtin_bit_cast(float, (uint32_t)sm.x[b * 32 + i][h] << 16);
+      amax = fmaxf(amax, fabsf(v[i]));
     }
-    __syncthreads();  // every thread has read its columns of the bf16 tile
+    // floor(log2 amax) = frexp exponent - 1 (exact, subnormals included)
+    int sb = amax == 0.0f ? 127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8 + 127;
+    sb = min(max(sb, 0), 254);
+    const int sh = 127 - sb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__builtin_ldexpf(v[4 * j + t], sh), -448.0f), 448.0f);
+      int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+      // a code of magnitude 0 (including -0) becomes +0
+      const uint32_t z = (uint32_t)c & 0x7F7F7F7Fu;
+      const uint32_t nz = ((z + 0x7F7F7F7Fu) & 0x80808080u) >> 7;
+      wq[j] = (uint32_t)c & (nz * 0xFFu);
+    }
+    __syncthreads();  // every thread has read its column of the bf16 tile
     const int sw = (h >> 1) & 7;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int b = b0 + 2 * bb;
-      const uint32_t* w = wq[bb];
-      *(v4i*)&sm.q[h][((2 * b) ^ sw) * 16] = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      *(v4i*)&sm.q[h][((2 * b + 1) ^ sw) * 16] = (v4i){(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-      if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(M >> 5) + (m0 >> 5) + b] = (uint8_t)sq[bb];
-    }
+    *(v4i*)&sm.q[h][((2 * b) ^ sw) * 16] = (v4i){(int)wq[0], (int)wq[1], (int)wq[2], (int)wq[3]};
+    *(v4i*)&sm.q[h][((2 * b + 1) ^ sw) * 16] = (v4i){(int)wq[4], (int)wq[5], (int)wq[6], (int)wq[7]};
+    if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(M >> 5) + (m0 >> 5) + b] = (uint8_t)sb;
   }
   __syncthreads();
   // ---- store: chunk c = 256 k + tid is hidden row c / 8, tokens 16 (c % 8) .. +15
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 2; ++k) {
     const int c = k * 256 + tid, r = c >> 3, c8 = c & 7;
     const int h = h0 + r, m = m0 + c8 * 16;
     if (h < H && m < M) *(v4i*)(q + (size_t)h * M + m) = *(const v4i*)&sm.q[r][(c8 ^ ((r >> 1) & 7)) * 16];
