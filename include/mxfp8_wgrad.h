@@ -104,8 +104,10 @@ extern "C" {
  * consecutive bytes.  The workspace holds (ceil(N/256) + ceil(K/256)) *
  * ceil(M/512) * 4 KiB (21 MiB at the 16B shape with 196,608 tokens, 88 MiB
  * at 671B gate/up with 262,144); it is allocated with hipMalloc on the first
- * such call on a device, grown when a later call needs more (synchronising
- * the device before the old one is freed) and kept until the process ends.
+ * such call on a device and replaced by a buffer of the next power of two
+ * when a later call needs more.  Replaced buffers are not freed (a HIP graph
+ * captured earlier may still use them; what is kept stays below twice the
+ * largest size), and all are kept until the process ends.
  *
  * Launches of mxfp8_wgrad_grouped or bf16_wgrad_grouped that use a workspace
  * (column mode, or the scale pre-shuffle) must not overlap in time on one

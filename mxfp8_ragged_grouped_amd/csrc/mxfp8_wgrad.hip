@@ -1473,9 +1473,11 @@ int get_workspace(int dev, int ncol, float** part, uint32_t** flags) {
 }
 
 // Shuffled scale planes of the weight gradient, one buffer per device
-// (shared by every call on it, like the column-mode workspace): grown on
-// demand (the device is synchronised before an old buffer is freed) and kept
-// until the process ends.
+// (shared by every call on it, like the column-mode workspace).  A call that
+// needs more than the current buffer allocates a new one of the next power of
+// two and leaves the old one allocated: a HIP graph captured earlier may still
+// use it, so it is never freed (what is kept stays below twice the largest
+// buffer).  Kept until the process ends.
 struct ScaleWs {
   uint8_t* buf;
   size_t bytes;
@@ -1488,16 +1490,11 @@ int get_scale_workspace(int dev, size_t bytes, uint8_t** out) {
   std::lock_guard<std::mutex> lock(g_scale_mutex);
   ScaleWs& w = g_scale_ws[dev];
   if (w.bytes < bytes) {
-    if (w.buf) {
-      if (hipDeviceSynchronize() != hipSuccess) return MXW_ERR_LAUNCH;
-      (void)hipFree(w.buf);
-      w.buf = nullptr;
-      w.bytes = 0;
-    }
-    const size_t want = (bytes + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);  // whole MiB
+    size_t want = (size_t)1 << 20;
+    while (want < bytes) want <<= 1;
     void* ptr = nullptr;
     if (hipMalloc(&ptr, want) != hipSuccess) return MXW_ERR_LAUNCH;
-    w.buf = (uint8_t*)ptr;
+    w.buf = (uint8_t*)ptr;  // the previous buffer, if any, stays allocated
     w.bytes = want;
   }
   *out = w.buf;

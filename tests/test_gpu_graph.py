@@ -86,3 +86,42 @@ def test_bf16_graph_replay(mode):
     out = torch.empty((cfg["E"], cfg["N"], cfg["K"]), dtype=torch.bfloat16, device=DEV)
     say("graph bf16 wgrad %s" % mode)
     replay_check(lambda: mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out), [out], "bf16 wgrad " + mode)
+
+
+def test_wgrad_graph_survives_scale_workspace_growth():
+    """A graph captured on a shape that uses the scale pre-shuffle keeps
+    replaying correctly after a larger call has replaced the device's scale
+    workspace (replaced buffers stay allocated)."""
+    small = W.make_random(2, 272, 528, 8224, [4000, 4128], seed=1305, device=DEV)
+    assert mxw.scale_shuffle(2, 8224)
+    out = torch.empty((2, 272, 528), dtype=torch.bfloat16, device=DEV)
+    fn = lambda: mxw.wgrad(small["A"], small["sA"], small["B"], small["sB"], small["offs"], out=out)
+    say("graph + scale workspace growth: capture on the small shape")
+    fn()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    # a larger call: (4 + 4) bands x 128 groups x 4 KiB of shuffled scales
+    big = W.make_random(4, 1024, 1024, 65536, [16384, 0, 30000 // 32 * 32, 18944], seed=1306, device=DEV)
+    assert mxw.scale_shuffle(4, 65536)
+    say("graph + scale workspace growth: larger eager call, then replays")
+    ob = mxw.wgrad(big["A"], big["sA"], big["B"], big["sB"], big["offs"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(ob.float()).all().item()
+    for r in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay %d after growth differs" % r
+    # the small shape eagerly (now on the larger buffer) gives the same bits
+    fn()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
