@@ -1309,6 +1309,32 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
   const int rows = min(kTile, R - b * kTile);
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.s[op] + (size_t)b * kTile * sb, ((uint32_t)rows * sb + 3u) & ~3u);
+  auto keep_bytes = [](uint32_t x, int keep) { return keep >= 4 ? x : (keep <= 0 ? 0u : x & ((1u << (8 * keep)) - 1u)); };
+  if ((sb & 15u) == 0) {
+    // 16-byte aligned rows (M % 512 == 0): one load per chunk, all eight in
+    // flight before any store (the compiler cannot tell the buffer loads from
+    // the global stores, so a load-store loop would wait out each load)
+    v4i v[8];
+    int nv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 256 + (int)threadIdx.x;  // chunk: row c / 8, group 8 o + c % 8
+      const int r = c >> 3, G = 8 * o + (c & 7), q0 = 16 * G;
+      nv[i] = (r < rows && G < a.groups) ? min(max(qlim - q0, 0), 16) : 0;
+      const uint32_t off = nv[i] > 0 ? (uint32_t)r * sb + (uint32_t)q0 : kOob;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 256 + (int)threadIdx.x;
+      const int r = c >> 3, G = 8 * o + (c & 7);
+      if (G >= a.groups) continue;
+      const v4i w = {(int)keep_bytes((uint32_t)v[i].x, nv[i]), (int)keep_bytes((uint32_t)v[i].y, nv[i] - 4),
+                     (int)keep_bytes((uint32_t)v[i].z, nv[i] - 8), (int)keep_bytes((uint32_t)v[i].w, nv[i] - 12)};
+      *(v4i*)(a.out[op] + (((size_t)b * a.groups + G) * kTile + r) * 16) = w;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = i * 256 + (int)threadIdx.x;  // chunk: row c / 8, group 8 o + c % 8
@@ -1319,28 +1345,13 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (nvalid > 0) {
       const uint32_t off = (uint32_t)r * sb + (uint32_t)q0;
-      uint32_t x[4];
-      if ((sb & 15u) == 0) {
-        // 16-byte aligned rows (M % 512 == 0): one load per chunk
-        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-        x[0] = (uint32_t)v.x;
-        x[1] = (uint32_t)v.y;
-        x[2] = (uint32_t)v.z;
-        x[3] = (uint32_t)v.w;
-      } else {
-        // the 5 dwords around the chunk, funnel-shifted
-        const uint32_t al = off & ~3u, sh = (off & 3u) * 8u;
-        uint32_t v[5];
+      // unaligned rows: the 5 dwords around the chunk, funnel-shifted
+      const uint32_t al = off & ~3u, sh = (off & 3u) * 8u;
+      uint32_t v[5];
 #pragma unroll
-        for (int d = 0; d < 5; ++d) v[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(al + 4u * d), 0, 0);
+      for (int d = 0; d < 5; ++d) v[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(al + 4u * d), 0, 0);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) x[d] = __builtin_amdgcn_alignbit(v[d + 1], v[d], sh);
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int keep = min(max(nvalid - 4 * d, 0), 4);  // valid bytes in this dword
-        w[d] = keep == 4 ? x[d] : (x[d] & ((1u << (8 * keep)) - 1u));
-      }
+      for (int d = 0; d < 4; ++d) w[d] = keep_bytes(__builtin_amdgcn_alignbit(v[d + 1], v[d], sh), nvalid - 4 * d);
     }
     *(v4i*)(a.out[op] + (((size_t)b * a.groups + G) * kTile + r) * 16) = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
   }
