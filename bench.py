@@ -2,11 +2,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one call of the whole hot path (mxfp8_wgrad_grouped: windows from
-offs, tile scheduling, masked head/tail staging, scale relayout, block-scaled
-MFMA contraction, bf16 epilogue; a single kernel) on seeded synthetic inputs
-already resident in HBM.  The default workload is the DeepSeek-V3 16B expert
-shape at production token count (E=8, N=1408, K=2048, 24,576 tokens/expert,
+One step is one call of the whole hot path (windows from offs, tile
+scheduling, masked head/tail staging, scale relayout, block-scaled MFMA
+contraction, bf16 epilogue) on seeded synthetic inputs already resident in
+HBM.  The headline times mxfp8_wgrad_grouped_ws with a workspace allocated
+once beforehand: at the default workload a call is two kernels, the scale
+pre-shuffle and the main kernel in column mode, and the time is the whole
+call's.  The line also carries `plain_entry`: the same problem through
+mxfp8_wgrad_grouped, the entry point that takes no workspace (one kernel, one
+workgroup per output tile, scales read from the caller's planes).
+
+Timing method (stated in the line as `timing`): W untimed warm-up steps, then
+an untimed pre-run of back-to-back steps for about 2 s so that clocks and
+power reach the state they keep under sustained load, a synchronisation, then
+exactly K steps between HIP events on the launch stream.  `sustained` adds two
+further passes of >= 3 s (>= 1 s for the small workloads) with an event every
+8 steps, reporting the mean and median time per step of each pass.
+
+The default workload is the DeepSeek-V3 16B expert shape at production token
+count (E=8, N=1408, K=2048, 24,576 tokens/expert,
 Dirichlet routing with the busiest expert ~1.5x the mean): the shape the
 blog "Ragged MXFP8 Weight Gradients: A FlyDSL Grouped GEMM on MI355X" quotes
 2,174 TFLOP/s at (sections 5.6 and 7).
@@ -40,9 +54,8 @@ way in the same process, as the pages' "x BF16" comparison (context, not the
 metric).
 
 The weight-gradient lines also carry `power`: socket power, joules per step and
-the mean shader clock over a ~4 s back-to-back run (amdsmi, read-only), the
-clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz), and the
-time per step sustained over that run (HIP events around all of it).
+the mean shader clock over the first sustained pass (amdsmi, read-only), and
+the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
 
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
@@ -227,13 +240,16 @@ def bench_bf16(args):
     E, N, K, M = cfg["E"], cfg["N"], cfg["K"], cfg["M"]
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
+    ws = torch.empty(max(mxw.bf16_workspace_size(E, M, N, K), 1), dtype=torch.uint8, device=dev)
+    plain = args.entry == "plain"
 
     def step():
-        mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out, stream=stream)
+        mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out, stream=stream, workspace=ws, plain=plain)
 
     ms, wall = time_steps(step, args, stream)
     flops = W.useful_flops(cfg)
-    tflops = flops / (ms * 1e-3) / 1e12
+    tflops_of = lambda t_ms: flops / (t_ms * 1e-3) / 1e12
+    tflops = tflops_of(ms)
     res = {
         "metric": "BF16 contracting ragged dot (weight gradient) TFLOP/s (2·M·N·K); % of BF16 MFMA peak",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -242,15 +258,22 @@ def bench_bf16(args):
         "data": "synthetic (the base workload's seeded routing, N(0,1) values rounded to bf16, token-contiguous)",
         "config": {"workload": args.workload, "base": cfg["base"], "E": E, "N": N, "K": K, "M": M,
                    "busiest_over_mean": round(cfg["skew"], 3), "routing_seed": cfg["routing_seed"],
-                   "value_seed": cfg["value_seed"], "columns": mxw.columns(E, 2 * M, N, K),
+                   "value_seed": cfg["value_seed"], "columns": 0 if plain else mxw.columns(E, 2 * M, N, K),
+                   "entry": "bf16_wgrad_grouped" if plain else "bf16_wgrad_grouped_ws",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(args.workload)},
         "hbm_gbps_algorithmic": round(W.bf16_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
+        "timing": "%d untimed warm-up steps, an untimed ~2 s back-to-back pre-run, a synchronisation, then exactly "
+                  "%d steps between HIP events on the launch stream" % (args.warmup, args.steps),
     }
-    if not args.no_power:
-        res["power"] = power_leg(step, ms, stream, tflops, PEAK_BF16_TFLOPS)
+    if not args.no_sustained:
+        sus = sustained_leg(step, ms, stream, 1.0 if M // E < 8192 else 3.0, tflops_of_ms=tflops_of,
+                            peak=PEAK_BF16_TFLOPS, power=not args.no_power)
+        if "power" in sus:
+            res["power"] = sus.pop("power")
+        res["sustained"] = sus
     if not args.no_bf16:
         # the same operands through torch._grouped_mm (X as a contiguous [M, K])
         xb = cfg["B"].t().contiguous()
@@ -353,105 +376,129 @@ def bf16_context(cfg, ours_tflops, args, stream):
     return {"value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
             "mxfp8_over_bf16": round(ours_tflops / tf, 3),
             "what": "torch._grouped_mm(dY^T bf16 [N, M], X bf16 [M, K], offs) -> [E, N, K], same steps/warmup, "
-                    "same stream, this process"}
+                    "same stream, this process",
+            "comparable_to_pages": False,
+            "note": "the blog's ~900 TFLOP/s BF16 comparator is its own library GEMM with its library versions; "
+                    "torch._grouped_mm on this image takes another path, so this ratio is not the pages' "
+                    "'x BF16' figure"}
 
 
-def power_leg(step, ms_per_step, stream, tflops=None, peak=None, seconds=4.0):
-    """Socket power, energy per step and shader clock while `step` runs back to
-    back for about `seconds` (amdsmi, read-only).  A sampler thread polls the
-    energy accumulator and the GPU metrics table every 20 ms while the main
-    thread keeps the GPU busy.  The accumulator advances about once a second,
+class _Power:
+    """Socket power and shader clock sampled while the GPU runs (amdsmi,
+    read-only).  A sampler thread polls the energy accumulator and the GPU
+    metrics table every 20 ms.  The accumulator advances about once a second,
     so power is taken between its first and last updates inside the busy
     window (energy difference over the firmware timestamps), and the clock is
-    the mean of the current-GFX-clock readings in that window.  Returns a dict
-    (with "error" if amdsmi is unavailable)."""
-    import threading
+    the mean of the current-GFX-clock readings in that window."""
 
-    import torch
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-    except Exception as ex:  # no amdsmi on this host
-        return {"error": "amdsmi unavailable: %s" % str(ex)[:120]}
-    try:
-        props = torch.cuda.get_device_properties(torch.cuda.current_device())
-        want = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", 0),
-                                   getattr(props, "pci_device_id", 0))
-        handles = amdsmi.amdsmi_get_processor_handles()
-        h = next((x for x in handles if amdsmi.amdsmi_get_gpu_device_bdf(x).lower().startswith(want)), None)
-        if h is None:
-            return {"error": "no amdsmi handle for PCI %s" % want}
-        limit_w = amdsmi.amdsmi_get_power_info(h).get("power_limit")
-        samples, stop = [], threading.Event()
-
-        def sampler():
-            while not stop.is_set():
-                t = time.perf_counter()
-                try:
-                    e = amdsmi.amdsmi_get_energy_count(h)
-                    gm = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                    samples.append((t, e["energy_accumulator"], e["timestamp"], e["counter_resolution"],
-                                    gm.get("current_gfxclk"), gm.get("current_socket_power")))
-                except Exception:
-                    pass
-                stop.wait(0.02)
-
-        n = max(1, int(seconds * 1e3 / ms_per_step))
-        torch.cuda.synchronize()
-        th = threading.Thread(target=sampler, daemon=True)
-        th.start()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(n):
-            step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        sustained_ms = ev0.elapsed_time(ev1) / n
-        stop.set()
-        th.join()
-        win = [x for x in samples if t0 + 0.3 <= x[0] <= t1]  # skip the ramp-up
-        edges = [x for i, x in enumerate(win) if i == 0 or x[1] != win[i - 1][1]]
-        if len(edges) < 3:
-            return {"error": "too few energy-counter updates in the busy window (%d)" % len(edges)}
-        a, b = edges[1], edges[-1]  # first and last update seen inside the window
-        joules = (b[1] - a[1]) * a[3] * 1e-6
-        secs = (b[2] - a[2]) * 1e-9
-        watts = joules / secs
-        clks = [x[4] for x in win if isinstance(x[4], (int, float)) and x[4] > 0]
-        clk = sum(clks) / len(clks) if clks else None
-        res = {"avg_socket_w": round(watts, 1), "joules_per_step": round(watts * sustained_ms * 1e-3, 4),
-               "gfxclk_mhz_mean": round(clk, 1) if clk else None,
-               "power_limit_w": round(limit_w / 1e6, 1) if isinstance(limit_w, (int, float)) else None,
-               "window_s": round(secs, 3), "steps_run": n,
-               "sustained_ms_per_step": round(sustained_ms, 5),
-               "how": "amdsmi energy accumulator between its first and last update in a ~%.0f s back-to-back run; "
-                      "clock = mean current GFX clock over the same run; joules = power x sustained time per "
-                      "step" % seconds}
-        if tflops:
-            res["sustained_tflops"] = round(tflops * ms_per_step / sustained_ms, 2)
-        if clk and tflops and peak:
-            # over the same run as the clock; the peak scales with the shader
-            # clock (quoted at 2.4 GHz)
-            res["clock_normalised_frac"] = round(res["sustained_tflops"] / (peak * clk / 2400.0), 4)
-        return res
-    except Exception as ex:
-        return {"error": str(ex)[:200]}
-    finally:
+    def __init__(self):
+        import threading
+        import torch
+        self.error = None
+        self.samples = []
+        self.stop = threading.Event()
         try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+        except Exception as ex:  # no amdsmi on this host
+            self.error = "amdsmi unavailable: %s" % str(ex)[:120]
+            return
+        try:
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            want = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", 0),
+                                       getattr(props, "pci_device_id", 0))
+            hs = amdsmi.amdsmi_get_processor_handles()
+            self.h = next((x for x in hs if amdsmi.amdsmi_get_gpu_device_bdf(x).lower().startswith(want)), None)
+            if self.h is None:
+                self.error = "no amdsmi handle for PCI %s" % want
+                return
+            self.limit_w = amdsmi.amdsmi_get_power_info(self.h).get("power_limit")
+        except Exception as ex:
+            self.error = str(ex)[:200]
+            return
+        self.th = threading.Thread(target=self._run, daemon=True)
+        self.th.start()
+
+    def _run(self):
+        a = self.amdsmi
+        while not self.stop.is_set():
+            t = time.perf_counter()
+            try:
+                e = a.amdsmi_get_energy_count(self.h)
+                gm = a.amdsmi_get_gpu_metrics_info(self.h)
+                self.samples.append((t, e["energy_accumulator"], e["timestamp"], e["counter_resolution"],
+                                     gm.get("current_gfxclk"), gm.get("current_socket_power")))
+            except Exception:
+                pass
+            self.stop.wait(0.02)
+
+    def finish(self, t0, t1, sustained_ms, tflops=None, peak=None):
+        if self.error:
+            return {"error": self.error}
+        self.stop.set()
+        self.th.join()
+        try:
+            win = [x for x in self.samples if t0 + 0.3 <= x[0] <= t1]  # skip the ramp-up
+            edges = [x for i, x in enumerate(win) if i == 0 or x[1] != win[i - 1][1]]
+            if len(edges) < 3:
+                return {"error": "too few energy-counter updates in the busy window (%d)" % len(edges)}
+            a, b = edges[1], edges[-1]  # first and last update seen inside the window
+            joules = (b[1] - a[1]) * a[3] * 1e-6
+            secs = (b[2] - a[2]) * 1e-9
+            watts = joules / secs
+            clks = [x[4] for x in win if isinstance(x[4], (int, float)) and x[4] > 0]
+            clk = sum(clks) / len(clks) if clks else None
+            lim = self.limit_w
+            res = {"avg_socket_w": round(watts, 1), "joules_per_step": round(watts * sustained_ms * 1e-3, 4),
+                   "gfxclk_mhz_mean": round(clk, 1) if clk else None,
+                   "power_limit_w": round(lim / 1e6, 1) if isinstance(lim, (int, float)) else None,
+                   "window_s": round(secs, 3),
+                   "how": "amdsmi energy accumulator between its first and last update in the first sustained "
+                          "pass; clock = mean current GFX clock over it; joules = power x that pass's mean time "
+                          "per step"}
+            if clk and tflops and peak:
+                # the peak scales with the shader clock (quoted at 2.4 GHz)
+                res["clock_normalised_frac"] = round(tflops / (peak * clk / 2400.0), 4)
+            return res
+        except Exception as ex:
+            return {"error": str(ex)[:200]}
+        finally:
+            try:
+                self.amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
 
 
-def time_steps(step, args, stream):
-    """W untimed steps, then K timed ones between HIP events on `stream`."""
+def _estimate_ms(step, stream, n=8):
+    """Rough time per step from a short burst (sizes the untimed pre-run)."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return max(a.elapsed_time(b) / n, 1e-3)
+
+
+def time_steps(step, args, stream, prerun_s=2.0):
+    """W untimed warm-up steps; an untimed pre-run of back-to-back steps for
+    about prerun_s seconds, so that the timed steps run at the clock and power
+    the chip keeps under sustained load (a short window straight after a few
+    warm-up steps catches the clock still ramping); a synchronisation; then
+    exactly K steps between HIP events on `stream`.  Returns (ms per step,
+    wall seconds of the timed region)."""
     import torch
 
     for _ in range(args.warmup):
         step()
+    torch.cuda.synchronize()
+    if prerun_s > 0:
+        est = _estimate_ms(step, stream)
+        for _ in range(int(prerun_s * 1e3 / est)):
+            step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -464,6 +511,40 @@ def time_steps(step, args, stream):
     return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
 
 
+def sustained_leg(step, ms_per_step, stream, seconds, passes=2, chunk=8, tflops_of_ms=None, peak=None, power=True):
+    """`passes` back-to-back runs of about `seconds` each, with a HIP event on
+    `stream` every `chunk` steps: per pass, the mean and median time per step
+    over its chunks.  The socket power and clock are sampled over the first
+    pass (when power is true)."""
+    import torch
+
+    out = {"passes": [], "chunk_steps": chunk, "seconds_per_pass": seconds}
+    pw = None
+    for k in range(passes):
+        nch = max(2, int(seconds * 1e3 / (ms_per_step * chunk)))
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nch + 1)]
+        torch.cuda.synchronize()
+        if k == 0 and power:
+            pw = _Power()
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for c in range(nch):
+            for _ in range(chunk):
+                step()
+            evs[c + 1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per = np.array([evs[c].elapsed_time(evs[c + 1]) / chunk for c in range(nch)])
+        rec = {"steps": nch * chunk, "seconds": round(float(per.sum() * chunk / 1e3), 3),
+               "mean_ms": round(float(per.mean()), 5), "median_ms": round(float(np.median(per)), 5)}
+        if tflops_of_ms:
+            rec["mean_tflops"] = round(tflops_of_ms(rec["mean_ms"]), 2)
+        out["passes"].append(rec)
+        if k == 0 and pw is not None:
+            out["power"] = pw.finish(t0, t1, rec["mean_ms"], rec.get("mean_tflops"), peak)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -473,7 +554,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 torch._grouped_mm context leg")
-    ap.add_argument("--no-power", action="store_true", help="skip the power / energy / clock leg")
+    ap.add_argument("--no-power", action="store_true", help="skip the power / energy / clock sampling")
+    ap.add_argument("--no-sustained", action="store_true", help="skip the two sustained passes (and power)")
+    ap.add_argument("--no-plain", action="store_true", help="skip timing the entry point without a workspace")
+    ap.add_argument("--entry", choices=("ws", "plain"), default="ws",
+                    help="weight-gradient entry point of the headline: mxfp8_wgrad_grouped_ws (default) or "
+                         "mxfp8_wgrad_grouped")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -507,17 +593,33 @@ def main():
     E, N, K, M = cfg["E"], cfg["N"], cfg["K"], cfg["M"]
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
+    ws_bytes = mxw.workspace_size(E, M, N, K)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    plain_first = args.entry == "plain"
 
-    def step():
-        mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=stream)
+    def step_ws():
+        mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=stream, workspace=ws)
 
+    def step_plain():
+        mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=stream, plain=True)
+
+    step = step_plain if plain_first else step_ws
     ms, wall = time_steps(step, args, stream)
 
     flops = W.useful_flops(cfg)
-    tflops = flops / (ms * 1e-3) / 1e12
+    tflops_of = lambda t_ms: flops / (t_ms * 1e-3) / 1e12
+    tflops = tflops_of(ms)
     alg_bytes = W.algorithmic_bytes(cfg)
     traffic = load_traffic(args.workload)
+    small = M // E < 8192  # the small-token workloads: 1 s sustained passes
 
+    if plain_first:
+        kernels = 1
+        timed = "the whole call of mxfp8_wgrad_grouped (one kernel, wgrad_kernel)"
+    else:
+        kernels = 2 if mxw.scale_shuffle(E, M) else 1
+        timed = ("the whole call of mxfp8_wgrad_grouped_ws (%s); traffic is wgrad_kernel's" %
+                 ("scale_shuffle_kernel then wgrad_kernel" if kernels == 2 else "wgrad_kernel"))
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -534,22 +636,37 @@ def main():
         "config": {"workload": args.workload, "E": E, "N": N, "K": K, "M": M,
                    "tokens_per_expert_mean": M // E, "busiest_over_mean": round(cfg["skew"], 3),
                    "routing_seed": cfg["routing_seed"], "value_seed": cfg["value_seed"],
+                   "entry": "mxfp8_wgrad_grouped" if plain_first else "mxfp8_wgrad_grouped_ws",
+                   "workspace_bytes": 0 if plain_first else ws_bytes,
+                   "columns": 0 if plain_first else mxw.columns(E, M, N, K),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_TFLOPS, 4),
-                     "traffic": traffic,
-                     "kernels_per_call": 2 if mxw.scale_shuffle(E, M) else 1,
-                     "timed": "the whole call (scale_shuffle_kernel, when it runs, then wgrad_kernel); traffic is "
-                              "wgrad_kernel's"},
+                     "traffic": None if plain_first else traffic,
+                     "kernels_per_call": kernels, "timed": timed},
         "hbm_gbps_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
+        "timing": "%d untimed warm-up steps, an untimed ~2 s back-to-back pre-run (steady clock and power), a "
+                  "synchronisation, then exactly %d steps between HIP events on the launch stream" % (
+                      args.warmup, args.steps),
     }
     if args.workload == "16b_24k":
         res["baseline_note"] = ("vs_baseline = value / 2,174 TFLOP/s, the blog's kernel at the 16B ragged shape on "
                                 "MI355X (their routing: linear ramp / ragged draw at 1.5x; ours: seeded Dirichlet "
                                 "at %.2fx)" % cfg["skew"])
-    if not args.no_power:
-        res["power"] = power_leg(step, ms, stream, tflops, PEAK_TFLOPS)
+    if not args.no_sustained:
+        sus = sustained_leg(step, ms, stream, 1.0 if small else 3.0, tflops_of_ms=tflops_of, peak=PEAK_TFLOPS,
+                            power=not args.no_power)
+        if "power" in sus:
+            res["power"] = sus.pop("power")
+        res["sustained"] = sus
+    if not args.no_plain and not plain_first:
+        pms, _ = time_steps(step_plain, args, stream, prerun_s=1.0)
+        ptf = tflops_of(pms)
+        res["plain_entry"] = {"entry": "mxfp8_wgrad_grouped", "ms_per_step": round(pms, 5),
+                              "tflops": round(ptf, 2), "frac": round(ptf / PEAK_TFLOPS, 4),
+                              "what": "the entry point without a workspace (one workgroup per output tile, scales "
+                                      "from the caller's planes), same timing method, this process"}
     if not args.no_bf16:
         res["bf16_context"] = bf16_context(cfg, tflops, args, stream)
     if not args.no_cpu:

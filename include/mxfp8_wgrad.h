@@ -30,6 +30,7 @@
 #ifndef MXFP8_WGRAD_H
 #define MXFP8_WGRAD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -38,12 +39,13 @@ extern "C" {
 
 /* Return codes. */
 #define MXW_OK 0
-#define MXW_ERR_NULL (-1)   /* a required pointer is NULL */
-#define MXW_ERR_DIM (-2)    /* a size outside the supported range */
-#define MXW_ERR_ALIGN (-3)  /* A, B or out not 16-byte aligned */
-#define MXW_ERR_DEVICE (-4) /* current device is not gfx950, or no device */
-#define MXW_ERR_LAUNCH (-5) /* a kernel launch failed (hipGetLastError), or a
-                               workspace could not be allocated */
+#define MXW_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MXW_ERR_DIM (-2)       /* a size outside the supported range */
+#define MXW_ERR_ALIGN (-3)     /* A, B or out not 16-byte aligned */
+#define MXW_ERR_DEVICE (-4)    /* current device is not gfx950, or no device */
+#define MXW_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError) */
+#define MXW_ERR_WORKSPACE (-6) /* workspace NULL, smaller than its size query,
+                                  or not 256-byte aligned */
 
 /* Supported ranges (checked on the host, no device access). */
 #define MXW_MAX_EXPERTS 256
@@ -63,7 +65,7 @@ extern "C" {
  *   E     number of experts, 1 <= E <= MXW_MAX_EXPERTS.
  *   M     token-axis length of A and B (routed tokens plus any padding),
  *         0 <= M <= MXW_MAX_TOKENS, M % 32 == 0.
- *   N, K  output dimensions, each >= 16 and a multiple of 16.
+ *   N, K  output dimensions, each >= 16 and a multiple of 16, <= 65536.
  *   out   bf16 bit patterns [E, N, K], row-major (k contiguous).
  *   stream  a hipStream_t (NULL = the default stream), passed as void*.
  *
@@ -76,50 +78,85 @@ extern "C" {
  * Tokens in [offs[E-1], M) belong to no expert and may hold anything (NaN
  * codes, 0xFF scales): they never reach the result.  Malformed offs give
  * unspecified values but no out-of-bounds access: windows are clamped to
- * [0, M] and every load is range-checked.
+ * [0, M] and made monotone, every load is range-checked, and every store
+ * lands inside out.
  *
- * Effects: enqueues the kernel (after the scale pre-shuffle below, when it
- * runs) on `stream` and returns without synchronising.  `out` is completely
- * overwritten; an expert with no tokens gets exact +0.0.
- * Inputs are never written.  The result is bitwise reproducible run to run:
- * for given (E, M, N, K, offs) every output element is summed in a fixed
- * order, whatever the timing (no atomics on data).
+ * Effects: enqueues one kernel on `stream` and returns without
+ * synchronising.  It allocates nothing, keeps no state between calls, takes
+ * no lock and never writes its inputs, so it may run concurrently on any
+ * number of streams and be captured into a HIP graph at any time, the very
+ * first call included.  `out` is completely overwritten; an expert with no
+ * tokens gets exact +0.0.
  *
- * Scheduling and state: with few output tiles per compute unit and long
- * experts (mxw_columns() > 0) the launch runs in column mode, one workgroup
- * per CU, and a region of tiles cut between columns is summed through FP32
- * partial tiles in a device workspace plus one arrival counter per region:
- * the last piece of a region to finish adds the others' partials, so no
- * workgroup ever waits for another and the kernel needs no co-residency.
- * The library allocates that workspace (128 MiB on a 256-CU device) with
- * hipMalloc on the first column-mode call on a device, synchronising the
- * device once, and keeps it until the process ends; every launch leaves the
- * counters at zero.
- *
- * Scale pre-shuffle: when the experts are long (M >= 4096 E) or the scale
- * rows are not 16-byte aligned (M % 512 != 0), the call first launches a
- * short kernel that rewrites sA and sB into a device workspace, each 256-row
- * band's 16-byte groups of 8 K-steps made contiguous (and the scales of
- * tokens past offs[E-1] cleared), so that the main kernel's scale loads read
- * consecutive bytes.  The workspace holds (ceil(N/256) + ceil(K/256)) *
- * ceil(M/512) * 4 KiB (21 MiB at the 16B shape with 196,608 tokens, 88 MiB
- * at 671B gate/up with 262,144); it is allocated with hipMalloc on the first
- * such call on a device and replaced by a buffer of the next power of two
- * when a later call needs more.  Replaced buffers are not freed (a HIP graph
- * captured earlier may still use them; what is kept stays below twice the
- * largest size), and all are kept until the process ends.
- *
- * Launches of mxfp8_wgrad_grouped or bf16_wgrad_grouped that use a workspace
- * (column mode, or the scale pre-shuffle) must not overlap in time on one
- * device: launches on different streams would race on it.  A call that uses
- * neither allocates nothing and keeps no state.  Capture into a HIP graph
- * after one eager call of the same or a larger shape (the capture must not
- * allocate).
+ * Scheduling and bits: one workgroup per (expert, 256 x 256 output tile)
+ * (blog section 4), experts taken longest first (section 5.4), no atomics.
+ * Each output element is one workgroup's sum over its expert's window in
+ * token order, so the result depends only on that expert's window of A, sA,
+ * B and sB: it is bitwise reproducible run to run, and unchanged by the
+ * other experts' sizes, by the padding past offs[E-1] and by M.
  *
  * Returns MXW_OK or a negative MXW_ERR_* code.
  */
 int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                         const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream);
+
+/*
+ * mxfp8_wgrad_workspace_size -- bytes of device workspace that
+ * mxfp8_wgrad_grouped_ws needs for (E, M, N, K) on the current device (0 if
+ * it needs none), or a negative MXW_ERR_* code.  Reads device properties
+ * only.  128 MiB of FP32 partial tiles on a 256-CU device when the launch
+ * runs in column mode (mxw_columns() > 0), plus (ceil(N/256) + ceil(K/256))
+ * * ceil(M/512) * 4 KiB of shuffled scales when it pre-shuffles
+ * (mxw_scale_shuffle()): 149 MiB at the 16B shape with 196,608 tokens,
+ * 88 MiB at 671B gate/up with 262,144.
+ */
+int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K);
+
+/*
+ * mxfp8_wgrad_grouped_ws -- the same weight gradient, given a caller-owned
+ * device workspace, which lets the launch use two faster schedules where they
+ * pay (the blog does not describe either):
+ *  - column mode (few output tiles per compute unit, long experts): one
+ *    workgroup per CU; 16 workgroups on one XCD form a column that streams
+ *    regions of up to 16 tiles of one expert together through that XCD's L2.
+ *    The K-step-weighted sequence of (expert, region) pieces is cut into one
+ *    equal span per column, and a region cut between columns is summed in a
+ *    fixed order through FP32 partial tiles in the workspace: the last of
+ *    its pieces to finish (found with a device-scope counter) adds the
+ *    others' partials.  No workgroup ever waits for another.
+ *  - the scale pre-shuffle (M >= 4096 E or M % 512 != 0): a short first
+ *    kernel rewrites sA and sB into the workspace so that the main kernel's
+ *    scale loads read consecutive bytes (the blog has a per-call pre-shuffle
+ *    too, section 5.6).
+ *
+ * Arguments: as mxfp8_wgrad_grouped, plus
+ *   workspace        caller-owned device memory, 256-byte aligned, of at
+ *                    least mxfp8_wgrad_workspace_size(E, M, N, K) bytes
+ *                    (may be NULL when that size is 0).  Its contents are
+ *                    undefined on entry and on exit: the call's first kernel
+ *                    initialises what the others read.
+ *   workspace_bytes  its size.
+ *
+ * Effects: enqueues one or two kernels on `stream`, returns without
+ * synchronising, allocates nothing and keeps no state; graph-capturable at
+ * any time.  The workspace is in use until the call's work on `stream` has
+ * finished: calls that run concurrently (other streams, overlapping graph
+ * replays) need workspaces of their own.  `out` is completely overwritten.
+ *
+ * Bits: bitwise reproducible run to run for the same (offs, M) on the same
+ * device, but in column mode an output element is the sum of FP32 partials
+ * whose cut points depend on the whole of offs, on M (through the mode
+ * choice) and on the device's CU count: dW[g] may then differ, within the
+ * tolerance of FP32 summation order, from mxfp8_wgrad_grouped's result and
+ * from the result of a call whose other experts or padding differ.  Without
+ * column mode the bits equal mxfp8_wgrad_grouped's.
+ *
+ * Returns MXW_OK or a negative MXW_ERR_* code (MXW_ERR_WORKSPACE for a
+ * missing, short or misaligned workspace).
+ */
+int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                           const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * bf16_wgrad_grouped -- the same weight gradient on plain bfloat16 operands:
@@ -145,11 +182,9 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
  * out-of-bounds access).  Tokens in [offs[E-1], M) may hold anything, NaN and
  * infinity included: they never reach the result.
  *
- * Effects, reproducibility, scheduling and workspace: as mxfp8_wgrad_grouped,
- * planned on the token axis in bytes: the launch runs in column mode exactly
- * when mxw_columns(E, 2 M, N, K) > 0, and shares the device's column-mode
- * workspace with mxfp8_wgrad_grouped (launches of either on one device must
- * not overlap in time when both run in column mode).
+ * Effects, reproducibility and scheduling: as mxfp8_wgrad_grouped (one
+ * kernel, allocates nothing, keeps no state; each output element one
+ * workgroup's sum in token order).
  *
  * Returns MXW_OK or a negative MXW_ERR_* code.
  */
@@ -157,15 +192,31 @@ int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs
                        uint16_t* out, void* stream);
 
 /*
+ * bf16_wgrad_workspace_size -- bytes of device workspace bf16_wgrad_grouped_ws
+ * needs for (E, M, N, K) on the current device (0 if none), or a negative
+ * MXW_ERR_* code.  Planned on the token axis in bytes: column mode exactly
+ * when mxw_columns(E, 2 M, N, K) > 0; there are no scales to shuffle.
+ */
+int64_t bf16_wgrad_workspace_size(int E, int M, int N, int K);
+
+/*
+ * bf16_wgrad_grouped_ws -- bf16_wgrad_grouped with a caller-owned workspace
+ * for column mode, with the workspace contract, effects and bits of
+ * mxfp8_wgrad_grouped_ws (a first one-workgroup kernel clears the counters).
+ */
+int bf16_wgrad_grouped_ws(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
+                          uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mxw_grid_size -- the number of (expert, 256 x 256 output tile) work items
  * of (E, N, K), E * ceil(N/256) * ceil(K/256) (blog section 4: one block per
- * expert per output tile).  Outside column mode this is also the number of
- * workgroups launched.  Returns 0 for invalid sizes.
+ * expert per output tile): the workgroups mxfp8_wgrad_grouped launches, and
+ * mxfp8_wgrad_grouped_ws outside column mode.  Returns 0 for invalid sizes.
  */
 int64_t mxw_grid_size(int E, int N, int K);
 
 /*
- * mxw_columns -- the number of columns mxfp8_wgrad_grouped uses for
+ * mxw_columns -- the number of columns mxfp8_wgrad_grouped_ws uses for
  * (E, M, N, K) on the current device: 0 when it launches one workgroup per
  * work item, otherwise the column count of column mode (16 workgroups per
  * column, one per compute unit).  Column mode is chosen when the work items
@@ -176,7 +227,7 @@ int64_t mxw_grid_size(int E, int N, int K);
 int mxw_columns(int E, int M, int N, int K);
 
 /*
- * mxw_scale_shuffle -- 1 if mxfp8_wgrad_grouped with (E, M) runs the scale
+ * mxw_scale_shuffle -- 1 if mxfp8_wgrad_grouped_ws with (E, M) runs the scale
  * pre-shuffle kernel before the main kernel (M >= 4096 E or M % 512 != 0),
  * 0 if it launches the main kernel alone, MXW_ERR_DIM for invalid sizes.
  * Host-only: no device access.

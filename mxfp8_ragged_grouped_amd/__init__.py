@@ -1,6 +1,7 @@
 """MI355X-native MXFP8 ragged grouped GEMMs.
 
     out = wgrad(A, sA, B, sB, offs)        # bf16 [E, N, K]
+    out = wgrad(..., plain=True)           # the entry point that takes no workspace
     out = wgrad_bf16(A, B, offs)           # bf16 [E, N, K] from bf16 operands
     out = fwd(A, sA, B, sB, offs)          # bf16 [R, N]
     q, s = quantize_tokens(x, offs)        # MXFP8 operand [H, M] from bf16 [M, H]
@@ -25,6 +26,14 @@ runs in the HIP library ``lib/libmxfp8_wgrad.so`` (C ABI in
 ``include/mxfp8_wgrad.h``); this module only checks tensor metadata and passes
 device pointers and the current stream.  There is no fallback: if the library
 is missing, or the device is not a gfx950, calls raise.
+
+The weight gradients have two entry points each.  mxfp8_wgrad_grouped (and
+bf16_wgrad_grouped) touch no memory but their operands and output: one
+workgroup per (expert, output tile).  The _ws variants take a caller-owned
+workspace (sized by mxfp8_wgrad_workspace_size) for column mode and the
+scale pre-shuffle.  wgrad() and wgrad_bf16() use the _ws variants unless
+plain=True, taking the workspace from torch's caching allocator on the
+stream the call runs on (or from `workspace`, a uint8 device tensor).
 """
 import ctypes
 import os
@@ -33,8 +42,10 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["wgrad", "mxfp8_wgrad_grouped", "wgrad_bf16", "bf16_wgrad_grouped", "grid_size", "columns", "scale_shuffle", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size",
-           "quantize_tokens", "mxfp8_quantize_tokens", "strerror", "version", "library_path", "MxwError"]
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "mxfp8_wgrad_grouped_ws", "workspace_size", "wgrad_bf16",
+           "bf16_wgrad_grouped", "bf16_wgrad_grouped_ws", "bf16_workspace_size", "grid_size", "columns",
+           "scale_shuffle", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size", "quantize_tokens", "mxfp8_quantize_tokens",
+           "strerror", "version", "library_path", "MxwError"]
 
 _lib = None
 
@@ -58,8 +69,17 @@ def _load():
     I = ctypes.c_int
     lib.mxfp8_wgrad_grouped.restype = I
     lib.mxfp8_wgrad_grouped.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
+    S = ctypes.c_size_t
+    lib.mxfp8_wgrad_grouped_ws.restype = I
+    lib.mxfp8_wgrad_grouped_ws.argtypes = [P, P, P, P, P, I, I, I, I, P, P, S, P]
+    lib.mxfp8_wgrad_workspace_size.restype = ctypes.c_int64
+    lib.mxfp8_wgrad_workspace_size.argtypes = [I, I, I, I]
     lib.bf16_wgrad_grouped.restype = I
     lib.bf16_wgrad_grouped.argtypes = [P, P, P, I, I, I, I, P, P]
+    lib.bf16_wgrad_grouped_ws.restype = I
+    lib.bf16_wgrad_grouped_ws.argtypes = [P, P, P, I, I, I, I, P, P, S, P]
+    lib.bf16_wgrad_workspace_size.restype = ctypes.c_int64
+    lib.bf16_wgrad_workspace_size.argtypes = [I, I, I, I]
     lib.mxw_grid_size.restype = ctypes.c_int64
     lib.mxw_grid_size.argtypes = [I, I, I]
     lib.mxw_strerror.restype = ctypes.c_char_p
@@ -116,6 +136,47 @@ def mxfp8_wgrad_grouped(A, sA, B, sB, offs, E, M, N, K, out, stream=0):
     return lib.mxfp8_wgrad_grouped(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, stream)
 
 
+def mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, E, M, N, K, out, workspace, workspace_bytes, stream=0):
+    """Raw C-ABI call on device addresses (ints).  Returns the status code."""
+    lib = _load()
+    return lib.mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, workspace,
+                                      int(workspace_bytes), stream)
+
+
+def workspace_size(E, M, N, K):
+    """Bytes of workspace mxfp8_wgrad_grouped_ws needs for this shape on the
+    current device (0: none).  Raises MxwError on a status code."""
+    rc = _load().mxfp8_wgrad_workspace_size(int(E), int(M), int(N), int(K))
+    if rc < 0:
+        raise MxwError("mxfp8_wgrad_workspace_size failed: %s" % strerror(rc))
+    return int(rc)
+
+
+def bf16_workspace_size(E, M, N, K):
+    """Bytes of workspace bf16_wgrad_grouped_ws needs (0: none)."""
+    rc = _load().bf16_wgrad_workspace_size(int(E), int(M), int(N), int(K))
+    if rc < 0:
+        raise MxwError("bf16_wgrad_workspace_size failed: %s" % strerror(rc))
+    return int(rc)
+
+
+def _workspace(need, dev, stream, workspace):
+    """(pointer, bytes, tensor): the caller's workspace, or a fresh one from
+    torch's caching allocator on `stream` (stream-ordered reuse)."""
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the same GPU")
+        nbytes = workspace.numel() * workspace.element_size()
+        if nbytes < need:
+            raise ValueError("workspace holds %d bytes, the call needs %d" % (nbytes, need))
+        return workspace.data_ptr(), nbytes, workspace
+    if need == 0:
+        return 0, 0, None
+    with torch.cuda.stream(stream):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    return ws.data_ptr(), need, ws
+
+
 def _as_u8(t, name):
     if t.dtype == torch.uint8:
         return t
@@ -124,14 +185,17 @@ def _as_u8(t, name):
     raise TypeError("%s must be uint8 (or float8_e4m3fn for data), got %s" % (name, t.dtype))
 
 
-def wgrad(A, sA, B, sB, offs, out=None, stream=None):
+def wgrad(A, sA, B, sB, offs, out=None, stream=None, workspace=None, plain=False):
     """dW [E, N, K] bf16 from MXFP8 operands (see module docstring).
 
     A: [N, M] uint8/float8_e4m3fn, sA: [N, M/32] uint8, B: [K, M], sB: [K, M/32],
     offs: [E] int32 cumulative expert ends, all on one CUDA(HIP) device and
     contiguous.  `out` (optional) is a contiguous bf16 [E, N, K] tensor that is
     fully overwritten.  Runs on `stream` (default: the current stream) and does
-    not synchronise.
+    not synchronise.  plain=True calls mxfp8_wgrad_grouped (no workspace);
+    otherwise mxfp8_wgrad_grouped_ws with `workspace` (a contiguous device
+    tensor of at least workspace_size() bytes) or one taken from torch's
+    caching allocator on that stream.
     """
     A = _as_u8(A, "A")
     B = _as_u8(B, "B")
@@ -160,10 +224,16 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        rc = mxfp8_wgrad_grouped(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
-                                 E, M, N, K, out.data_ptr(), stream.cuda_stream)
+        if plain:
+            rc = mxfp8_wgrad_grouped(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
+                                     E, M, N, K, out.data_ptr(), stream.cuda_stream)
+        else:
+            wp, wb, ws = _workspace(workspace_size(E, M, N, K), dev, stream, workspace)
+            rc = mxfp8_wgrad_grouped_ws(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
+                                        E, M, N, K, out.data_ptr(), wp, wb, stream.cuda_stream)
+            del ws
     if rc != 0:
-        raise MxwError("mxfp8_wgrad_grouped failed (%d): %s" % (rc, strerror(rc)))
+        raise MxwError("mxfp8_wgrad_grouped%s failed (%d): %s" % ("" if plain else "_ws", rc, strerror(rc)))
     return out
 
 
@@ -173,14 +243,21 @@ def bf16_wgrad_grouped(A, B, offs, E, M, N, K, out, stream=0):
     return lib.bf16_wgrad_grouped(A, B, offs, int(E), int(M), int(N), int(K), out, stream)
 
 
-def wgrad_bf16(A, B, offs, out=None, stream=None):
+def bf16_wgrad_grouped_ws(A, B, offs, E, M, N, K, out, workspace, workspace_bytes, stream=0):
+    """Raw C-ABI call on device addresses (ints).  Returns the status code."""
+    lib = _load()
+    return lib.bf16_wgrad_grouped_ws(A, B, offs, int(E), int(M), int(N), int(K), out, workspace,
+                                     int(workspace_bytes), stream)
+
+
+def wgrad_bf16(A, B, offs, out=None, stream=None, workspace=None, plain=False):
     """dW [E, N, K] bf16 from bf16 operands: dW[g] = A[:, win_g] B[:, win_g]^T.
 
     A: [N, M] and B: [K, M] bfloat16 (token axis contiguous), offs: [E] int32
     cumulative expert ends (multiples of 16), all contiguous on one GPU.
     `out` (optional) is a contiguous bf16 [E, N, K] tensor that is fully
     overwritten.  Runs on `stream` (default: the current stream) and does not
-    synchronise.
+    synchronise.  plain / workspace: as for wgrad().
     """
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("A and B must be bfloat16")
@@ -206,10 +283,16 @@ def wgrad_bf16(A, B, offs, out=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        rc = bf16_wgrad_grouped(A.data_ptr(), B.data_ptr(), offs.data_ptr(), E, M, N, K, out.data_ptr(),
-                                stream.cuda_stream)
+        if plain:
+            rc = bf16_wgrad_grouped(A.data_ptr(), B.data_ptr(), offs.data_ptr(), E, M, N, K, out.data_ptr(),
+                                    stream.cuda_stream)
+        else:
+            wp, wb, ws = _workspace(bf16_workspace_size(E, M, N, K), dev, stream, workspace)
+            rc = bf16_wgrad_grouped_ws(A.data_ptr(), B.data_ptr(), offs.data_ptr(), E, M, N, K, out.data_ptr(),
+                                       wp, wb, stream.cuda_stream)
+            del ws
     if rc != 0:
-        raise MxwError("bf16_wgrad_grouped failed (%d): %s" % (rc, strerror(rc)))
+        raise MxwError("bf16_wgrad_grouped%s failed (%d): %s" % ("" if plain else "_ws", rc, strerror(rc)))
     return out
 
 

@@ -335,7 +335,7 @@ struct Params {
   const uint8_t* sBs;
   int sgroups;
   float* part;      // [ncol][2][kMem][kTile * kTile] partial tiles (a column's first / last piece)
-  uint32_t* flags;  // [ncol][kMem] arrival counters of cut regions, 0 between launches
+  uint32_t* flags;  // [ncol][kMem] arrival counters of cut regions, cleared by the call's first kernel
   int ncol;
   int regions;  // regions of up to kMem tiles per expert
   int hov;      // per-region cost, in K-steps, added to the split's weights
@@ -941,8 +941,6 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       }
       for (uint64_t m = todo; m; m &= m - 1) add_partial(slot(__builtin_ctzll(m)), std::true_type{});
     }
-    // the finisher leaves the counter at 0 for the next launch
-    if (finish && tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue ------------------------------------------------------------------
@@ -1280,7 +1278,9 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
 // 16B shape.  Rewritten as [band b = r / 256][group G][r % 256][16 bytes],
 // the same loads read 1 KiB of consecutive bytes.  Rows past R, bytes past
 // M/32 and the sub-blocks of tokens past offs[E-1] (padding, which may hold
-// 0xFF = NaN scales) become 0.  One workgroup per (operand, band, 8 groups):
+// 0xFF = NaN scales; past the largest offs value, so that malformed offs
+// still keep every window's scales) become 0.  One workgroup per (operand,
+// band, 8 groups):
 // each wave reads 8 rows x 128 bytes at a time (consecutive lanes, consecutive
 // bytes) and writes, per group, 8 rows x 16 bytes contiguous.
 struct ShufArgs {
@@ -1291,18 +1291,29 @@ struct ShufArgs {
   int M, groups, octets;
   const int32_t* offs;
   int E;
+  // column mode's arrival counters, cleared here for the main kernel that
+  // follows on the stream (nullptr when it does not run in column mode)
+  uint32_t* flags;
+  int nflags;
 };
 
 __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
   int blk = blockIdx.x;
+  if (blk == 0 && a.flags)
+    for (int i = (int)threadIdx.x; i < a.nflags; i += 256) a.flags[i] = 0u;
   const int op = blk >= a.bands[0] * a.octets;
   if (op) blk -= a.bands[0] * a.octets;
   const int b = blk / a.octets, o = blk - b * a.octets;
   const uint32_t sb = (uint32_t)a.M >> 5;  // bytes per row
   const int R = a.R[op];
-  int used = a.offs[a.E - 1];
-  used = min(max(used, 0), a.M);
-  const int qlim = used >> 5;  // sub-blocks (bytes) of a row that belong to an expert
+  // tokens past the largest clamped offs belong to no expert's window
+  // (offs[E-1] when offs is well formed)
+  __shared__ int used_max;
+  if (threadIdx.x == 0) used_max = 0;
+  __syncthreads();
+  for (int g = (int)threadIdx.x; g < a.E; g += 256) atomicMax(&used_max, min(max(a.offs[g], 0), a.M));
+  __syncthreads();
+  const int qlim = used_max >> 5;  // sub-blocks (bytes) of a row that may belong to an expert
   // this band's rows of the plane, the size rounded up to a dword (offsets
   // below are dword-aligned from this base: every dword is entirely inside
   // or outside the checked range)
@@ -1355,6 +1366,12 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
     }
     *(v4i*)(a.out[op] + (((size_t)b * a.groups + G) * kTile + r) * 16) = (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
   }
+}
+
+// Clears column mode's arrival counters before a launch that has no scale
+// pre-shuffle to do it (the bf16 weight gradient).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += 256) p[i] = 0u;
 }
 
 constexpr int kQTok = 128, kQHid = 64;
@@ -1440,95 +1457,31 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
 struct DeviceInfo {
   int checked;
   int ok;
-  int cus;          // compute units
-  float* part;      // column-mode workspace (allocated on first use, kept)
-  uint32_t* flags;
-  int ncol;         // columns the workspace holds
+  int cus;  // compute units
 };
 DeviceInfo g_dev[64];
-std::mutex g_ws_mutex;
+std::mutex g_dev_mutex;
 
-// Column-mode workspace of the current device: ncol x 2 x kMem FP32 partial
-// tiles and ncol x kMem arrival counters (zeroed once; the piece that
-// finishes a region resets its counter).
-int get_workspace(int dev, int ncol, float** part, uint32_t** flags) {
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  DeviceInfo& d = g_dev[dev];
-  if (!d.part || d.ncol < ncol) {
-    if (d.part) {
-      if (hipDeviceSynchronize() != hipSuccess) return MXW_ERR_LAUNCH;
-      (void)hipFree(d.part);
-      (void)hipFree(d.flags);
-      d.part = nullptr;
-      d.flags = nullptr;
-    }
-    void* pp = nullptr;
-    void* fp = nullptr;
-    if (hipMalloc(&pp, (size_t)ncol * 2 * kMem * kTile * kTile * sizeof(float)) != hipSuccess) return MXW_ERR_LAUNCH;
-    if (hipMalloc(&fp, (size_t)ncol * kMem * sizeof(uint32_t)) != hipSuccess) {
-      (void)hipFree(pp);
-      return MXW_ERR_LAUNCH;
-    }
-    if (hipMemset(fp, 0, (size_t)ncol * kMem * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      (void)hipFree(pp);
-      (void)hipFree(fp);
-      return MXW_ERR_LAUNCH;
-    }
-    d.part = (float*)pp;
-    d.flags = (uint32_t*)fp;
-    d.ncol = ncol;
-  }
-  *part = d.part;
-  *flags = d.flags;
-  return MXW_OK;
-}
-
-// Shuffled scale planes of the weight gradient, one buffer per device
-// (shared by every call on it, like the column-mode workspace).  A call that
-// needs more than the current buffer allocates a new one of the next power of
-// two and leaves the old one allocated: a HIP graph captured earlier may still
-// use it, so it is never freed (what is kept stays below twice the largest
-// buffer).  Kept until the process ends.
-struct ScaleWs {
-  uint8_t* buf;
-  size_t bytes;
-};
-ScaleWs g_scale_ws[64];
-std::mutex g_scale_mutex;
-
-int get_scale_workspace(int dev, size_t bytes, uint8_t** out) {
-  if (dev < 0 || dev >= 64) return MXW_ERR_DEVICE;
-  std::lock_guard<std::mutex> lock(g_scale_mutex);
-  ScaleWs& w = g_scale_ws[dev];
-  if (w.bytes < bytes) {
-    size_t want = (size_t)1 << 20;
-    while (want < bytes) want <<= 1;
-    void* ptr = nullptr;
-    if (hipMalloc(&ptr, want) != hipSuccess) return MXW_ERR_LAUNCH;
-    w.buf = (uint8_t*)ptr;  // the previous buffer, if any, stays allocated
-    w.bytes = want;
-  }
-  *out = w.buf;
-  return MXW_OK;
-}
-
-// whether an E4M3 weight-gradient call of (E, M) pre-shuffles its scales
-bool uses_scale_shuffle(int E, int M) { return (M & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
-
-int check_device() {
+// Reads device properties once per device (no allocation, no stream work).
+int check_device(int* cus = nullptr) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXW_ERR_DEVICE;
-  if (dev < 64 && g_dev[dev].checked) return g_dev[dev].ok ? MXW_OK : MXW_ERR_DEVICE;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXW_ERR_DEVICE;
-  const int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) {
-    g_dev[dev].ok = ok;
-    g_dev[dev].cus = prop.multiProcessorCount;
-    g_dev[dev].checked = 1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MXW_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXW_ERR_DEVICE;
+    d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = 1;
   }
-  return ok ? MXW_OK : MXW_ERR_DEVICE;
+  if (cus) *cus = d.cus;
+  return d.ok ? MXW_OK : MXW_ERR_DEVICE;
 }
+
+// whether an E4M3 weight-gradient call with a workspace pre-shuffles its
+// scales for (E, M)
+bool uses_scale_shuffle(int E, int M) { return (M & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
 
 // Columns of a column-mode launch (0: one workgroup per work item) and the
 // regions per expert.  Column mode when the work items fill the chip only a
@@ -1551,15 +1504,79 @@ int plan_columns(int E, int M, int N, int K, int cus, int* regions) {
   return 0;
 }
 
+constexpr size_t kWsAlign = 4096;
+size_t round_ws(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+// The plan of one weight-gradient launch.  Without a workspace: one workgroup
+// per (expert, tile), scales read from the caller's planes.  With one (the
+// _ws entry points): column mode and the scale pre-shuffle where they pay,
+// their buffers carved from the workspace as
+//   [arrival counters: ncol * kMem words][FP32 partial tiles: ncol * 2 * kMem
+//    * 256 KiB][shuffled scale planes of A, then of B]
+// each part starting on a 4 KiB boundary.
+struct Plan {
+  int ncol, regions;
+  bool shuffle;
+  int sgroups;
+  size_t flags_off, part_off, scaleA_off, scaleB_off, bytes;
+};
+
+Plan make_plan(int E, int Mb, int tshift, int N, int K, int cus, bool ws) {
+  Plan pl = {};
+  const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
+  if (!ws) {
+    int regions = 0;
+    (void)plan_columns(E, Mb, N, K, cus, &regions);
+    pl.regions = regions;
+    return pl;
+  }
+  pl.ncol = plan_columns(E, Mb, N, K, cus, &pl.regions);
+  pl.shuffle = tshift == 0 && uses_scale_shuffle(E, Mb);
+  size_t off = 0;
+  if (pl.ncol) {
+    pl.flags_off = off;
+    off = round_ws(off + (size_t)pl.ncol * kMem * sizeof(uint32_t));
+    pl.part_off = off;
+    off = round_ws(off + (size_t)pl.ncol * 2 * kMem * kTile * kTile * sizeof(float));
+  }
+  if (pl.shuffle) {
+    pl.sgroups = (Mb + 511) / 512 > 0 ? (Mb + 511) / 512 : 1;
+    pl.scaleA_off = off;
+    off = round_ws(off + (size_t)tN * pl.sgroups * kTile * 16);
+    pl.scaleB_off = off;
+    off = round_ws(off + (size_t)tK * pl.sgroups * kTile * 16);
+  }
+  pl.bytes = off;
+  return pl;
+}
+
+// Bytes of workspace a _ws call of this shape needs on the current device
+// (0: none), or a negative MXW_ERR_* code.
+int64_t wgrad_ws_bytes(int E, int Mb, int tshift, int N, int K) {
+  int cus = 0;
+  const int rc = check_device(&cus);
+  if (rc) return rc;
+  return (int64_t)make_plan(E, Mb, tshift, N, K, cus, true).bytes;
+}
+
 // One weight-gradient launch (E4M3 operands with scales when tshift = 0,
-// bf16 operands when tshift = 1).  Mb: bytes per row of A and B.  Sizes and
+// bf16 operands when tshift = 1).  Mb: bytes per row of A and B.  use_ws:
+// the _ws plan on workspace ws of ws_bytes bytes; otherwise the plain plan,
+// which touches no memory but the operands and out.  Sizes and operand
 // pointers are validated by the caller.
 int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const int32_t* offs,
-                 int E, int Mb, int tshift, int N, int K, uint16_t* out, void* stream) {
+                 int E, int Mb, int tshift, int N, int K, uint16_t* out, bool use_ws, void* ws, size_t ws_bytes,
+                 void* stream) {
   const int64_t grid = (int64_t)E * ((N + kTile - 1) / kTile) * ((K + kTile - 1) / kTile);
   if (grid <= 0 || grid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
-  int rc = check_device();
+  int cus = 0;
+  int rc = check_device(&cus);
   if (rc) return rc;
+  const Plan pl = make_plan(E, Mb, tshift, N, K, cus, use_ws);
+  if (use_ws && pl.bytes) {
+    if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MXW_ERR_WORKSPACE;
+  }
+  uint8_t* wsb = (uint8_t*)ws;
   Params p = {};
   p.A = A;
   p.sA = sA;
@@ -1594,34 +1611,40 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     p.band = (32 + p.regK - 1) / p.regK;
     if (p.band > p.regN) p.band = p.regN;
   }
-  int dev = 0;
-  (void)hipGetDevice(&dev);
   p.hov = kColHov;
-  const int ncol = plan_columns(E, Mb, N, K, dev < 64 ? g_dev[dev].cus : 0, &p.regions);
-  p.ncol = ncol;
-  if (ncol) {
-    rc = get_workspace(dev, ncol, &p.part, &p.flags);
-    if (rc) return rc;
+  p.regions = pl.regions;
+  p.ncol = pl.ncol;
+  if (pl.ncol) {
+    p.flags = (uint32_t*)(wsb + pl.flags_off);
+    p.part = (float*)(wsb + pl.part_off);
   }
-  const dim3 g((unsigned)(ncol ? ncol * kMem : grid)), blk(kThreads);
+  const dim3 g((unsigned)(pl.ncol ? pl.ncol * kMem : grid)), blk(kThreads);
   hipStream_t st = (hipStream_t)stream;
   if (tshift) {
-    if (ncol) hipLaunchKernelGGL((wgrad_kernel<false, true, true>), g, blk, 0, st, p);
-    else hipLaunchKernelGGL((wgrad_kernel<false, false, true>), g, blk, 0, st, p);
-  } else {
-    // E4M3: when the experts are long (M >= 4096 E) or the scale rows are not
-    // 16-byte aligned (M % 512 != 0), shuffle the scale planes and take the
-    // grouped path on them; otherwise read the caller's planes directly
-    // (grouped loads; at short experts the extra pass costs more than the
-    // scattered scale loads do: ~4 us against ~1 us at 1,024 tokens per expert)
-    if (!uses_scale_shuffle(E, Mb)) {
-      p.sAs = p.sBs = nullptr;
-      p.sgroups = 0;
-      if (ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
-      else hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
-      if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
-      return MXW_OK;
+    // bf16: no scales; column mode's counters are cleared by a first kernel
+    if (pl.ncol) {
+      hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, p.flags, pl.ncol * kMem);
+      hipLaunchKernelGGL((wgrad_kernel<false, true, true>), g, blk, 0, st, p);
+    } else {
+      hipLaunchKernelGGL((wgrad_kernel<false, false, true>), g, blk, 0, st, p);
     }
+  } else if (!pl.shuffle) {
+    // the caller's scale planes: 16-byte groups of 8 K-steps when scale rows
+    // are 16-byte aligned (M % 512 == 0), else the two aligned dwords around
+    // each row's 2 K-steps.  (Column mode always shuffles: it needs
+    // M >= 8192 E.)
+    p.sAs = p.sBs = nullptr;
+    p.sgroups = 0;
+    if (pl.ncol) return MXW_ERR_DIM;  // unreachable by construction of the plan
+    if ((Mb & 511) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((wgrad_kernel<false, false>), g, blk, 0, st, p);
+  } else {
+    // long experts (M >= 4096 E) or scale rows not 16-byte aligned
+    // (M % 512 != 0): rewrite the scale planes into the workspace so that the
+    // K-loop's grouped scale loads read consecutive bytes (the same kernel
+    // clears column mode's counters); at short experts the extra pass costs
+    // more than the scattered scale loads do (~4 us against ~1 us at 1,024
+    // tokens per expert)
     ShufArgs sa;
     sa.s[0] = sA;
     sa.s[1] = sB;
@@ -1630,26 +1653,35 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     sa.bands[0] = p.tilesN;
     sa.bands[1] = p.tilesK;
     sa.M = Mb;
-    sa.groups = (Mb + 511) / 512 > 0 ? (Mb + 511) / 512 : 1;
+    sa.groups = pl.sgroups;
     sa.octets = (sa.groups + 7) / 8;
     sa.offs = offs;
     sa.E = E;
-    const size_t bytesA = (size_t)sa.bands[0] * sa.groups * kTile * 16;
-    const size_t bytesB = (size_t)sa.bands[1] * sa.groups * kTile * 16;
-    uint8_t* ws = nullptr;
-    rc = get_scale_workspace(dev, bytesA + bytesB, &ws);
-    if (rc) return rc;
-    sa.out[0] = ws;
-    sa.out[1] = ws + bytesA;
+    sa.out[0] = wsb + pl.scaleA_off;
+    sa.out[1] = wsb + pl.scaleB_off;
+    sa.flags = p.flags;
+    sa.nflags = pl.ncol * kMem;
     p.sAs = sa.out[0];
     p.sBs = sa.out[1];
     p.sgroups = sa.groups;
     hipLaunchKernelGGL(scale_shuffle_kernel, dim3((unsigned)((sa.bands[0] + sa.bands[1]) * sa.octets)), dim3(256), 0, st,
                        sa);
-    if (ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
+    if (pl.ncol) hipLaunchKernelGGL((wgrad_kernel<true, true>), g, blk, 0, st, p);
     else hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
   }
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
+  return MXW_OK;
+}
+
+int check_wgrad_args(const void* A, const void* sA, const void* B, const void* sB, const void* offs, const void* out,
+                     int E, int M, int N, int K, bool bf) {
+  if (!A || (!bf && !sA) || !B || (!bf && !sB) || !offs || !out) return MXW_ERR_NULL;
+  const int mmax = bf ? MXW_MAX_TOKENS / 2 : MXW_MAX_TOKENS;
+  const int mal = bf ? 15 : 31;
+  if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > mmax || (M & mal) || N < 16 || K < 16 || (N & 15) ||
+      (K & 15) || N > 65536 || K > 65536)
+    return MXW_ERR_DIM;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
   return MXW_OK;
 }
 
@@ -1659,11 +1691,11 @@ extern "C" {
 
 int mxw_columns(int E, int M, int N, int K) {
   if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || N < 16 || K < 16) return MXW_ERR_DIM;
-  const int rc = check_device();
+  int cus = 0;
+  const int rc = check_device(&cus);
   if (rc) return rc;
-  int dev = 0, regions = 0;
-  (void)hipGetDevice(&dev);
-  return plan_columns(E, M, N, K, dev < 64 ? g_dev[dev].cus : 0, &regions);
+  int regions = 0;
+  return plan_columns(E, M, N, K, cus, &regions);
 }
 
 int mxw_scale_shuffle(int E, int M) {
@@ -1678,23 +1710,48 @@ int64_t mxw_grid_size(int E, int N, int K) {
 
 int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                         const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream) {
-  if (!A || !sA || !B || !sB || !offs || !out) return MXW_ERR_NULL;
-  if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || (M & 31) || N < 16 || K < 16 ||
-      (N & 15) || (K & 15) || N > 65536 || K > 65536)
+  const int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
+  if (rc) return rc;
+  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, false, nullptr, 0, stream);
+}
+
+int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K) {
+  if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || (M & 31) || N < 16 || K < 16 || (N & 15) ||
+      (K & 15) || N > 65536 || K > 65536)
     return MXW_ERR_DIM;
-  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
-  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, stream);
+  return wgrad_ws_bytes(E, M, 0, N, K);
+}
+
+int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                           const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
+  if (rc) return rc;
+  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, true, workspace, workspace_bytes, stream);
 }
 
 int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
                        uint16_t* out, void* stream) {
-  if (!A || !B || !offs || !out) return MXW_ERR_NULL;
+  const int rc = check_wgrad_args(A, nullptr, B, nullptr, offs, out, E, M, N, K, true);
+  if (rc) return rc;
+  // planned and run in bytes along the token axis: 2 M per row
+  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 1, N, K, out, false,
+                      nullptr, 0, stream);
+}
+
+int64_t bf16_wgrad_workspace_size(int E, int M, int N, int K) {
   if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS / 2 || (M & 15) || N < 16 || K < 16 ||
       (N & 15) || (K & 15) || N > 65536 || K > 65536)
     return MXW_ERR_DIM;
-  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
-  // planned and run in bytes along the token axis: 2 M per row
-  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 1, N, K, out, stream);
+  return wgrad_ws_bytes(E, 2 * M, 1, N, K);
+}
+
+int bf16_wgrad_grouped_ws(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
+                          uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_wgrad_args(A, nullptr, B, nullptr, offs, out, E, M, N, K, true);
+  if (rc) return rc;
+  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 1, N, K, out, true,
+                      workspace, workspace_bytes, stream);
 }
 
 int64_t mxw_fwd_grid_size(int E, int R, int N) {
@@ -1762,10 +1819,11 @@ const char* mxw_strerror(int code) {
     case MXW_ERR_ALIGN: return "A, B or out is not 16-byte aligned";
     case MXW_ERR_DEVICE: return "the current device is not gfx950 (or no device)";
     case MXW_ERR_LAUNCH: return "kernel launch failed";
+    case MXW_ERR_WORKSPACE: return "workspace missing, smaller than the size query returned, or not 256-byte aligned";
     default: return "unknown error";
   }
 }
 
-int mxw_version(void) { return 400; }
+int mxw_version(void) { return 500; }
 
 }  // extern "C"

@@ -26,17 +26,55 @@ def bf16_to_f64(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run_gpu(cfg, poison=True, out=None):
-    """Run the HIP path on the config's device tensors; out is NaN-poisoned first."""
+ENTRIES = ["ws", "plain"]  # mxfp8_wgrad_grouped_ws (workspace), mxfp8_wgrad_grouped (none)
+
+
+def run_gpu(cfg, poison=True, out=None, entry="ws", offs=None):
+    """Run the HIP path on the config's device tensors through one of the two
+    entry points; out is NaN-poisoned first."""
     E, N, K = cfg["E"], cfg["N"], cfg["K"]
     dev = cfg["A"].device
+    offs = cfg["offs"] if offs is None else offs
     if out is None:
-        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((offs.shape[0], N, K), dtype=torch.bfloat16, device=dev)
     if poison:
         out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], offs, out=out, plain=(entry == "plain"))
     torch.cuda.synchronize(dev)
     return out
+
+
+def tile_pairs(cfg, count, seed):
+    """Seeded (tn, tk) output-tile pairs: the four corner tiles (first and
+    last tiles of every expert, the partial last N and K tiles) plus random
+    ones, `count` in all (every pair when there are fewer)."""
+    tN, tK = -(-cfg["N"] // 256), -(-cfg["K"] // 256)
+    allp = [(a, b) for a in range(tN) for b in range(tK)]
+    if count >= len(allp):
+        return allp
+    pick = []
+    for p in [(0, 0), (tN - 1, tK - 1), (tN - 1, 0), (0, tK - 1)]:
+        if p not in pick:
+            pick.append(p)
+    rng = np.random.default_rng(seed)
+    rest = [p for p in allp if p not in pick]
+    for i in rng.permutation(len(rest))[:count - len(pick)]:
+        pick.append(rest[i])
+    return pick
+
+
+def oracle_tiles(host_ops, pairs):
+    """The oracle's fp64 result on whole 256 x 256 output tiles: for each
+    (tn, tk), every expert's tile, from the same definition run on the A rows
+    and B rows of that tile (all tokens).  Returns {(tn, tk): [E, rows, cols]}."""
+    A, sA, B, sB, offs = host_ops
+    res = {}
+    for tn, tk in pairs:
+        n0, k0 = 256 * tn, 256 * tk
+        res[(tn, tk)] = oracle.wgrad_f64(np.ascontiguousarray(A[n0:n0 + 256]), np.ascontiguousarray(sA[n0:n0 + 256]),
+                                         np.ascontiguousarray(B[k0:k0 + 256]), np.ascontiguousarray(sB[k0:k0 + 256]),
+                                         offs)
+    return res
 
 
 def host(cfg):

@@ -30,7 +30,9 @@ def test_library_built():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"mxfp8_wgrad_grouped", "bf16_wgrad_grouped", "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
+    assert set(names) >= {"mxfp8_wgrad_grouped", "mxfp8_wgrad_grouped_ws", "mxfp8_wgrad_workspace_size",
+                          "bf16_wgrad_grouped", "bf16_wgrad_grouped_ws", "bf16_wgrad_workspace_size",
+                          "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
                           "mxw_fwd_grid_size", "mxfp8_quantize_tokens", "mxw_strerror", "mxw_version"}
     lib = ctypes.CDLL(mxw.library_path())
     for n in names:
@@ -52,7 +54,8 @@ def test_grid_size():
 
 def test_strerror_and_version():
     codes = declared_macros()
-    for name in ("MXW_OK", "MXW_ERR_NULL", "MXW_ERR_DIM", "MXW_ERR_ALIGN", "MXW_ERR_DEVICE", "MXW_ERR_LAUNCH"):
+    for name in ("MXW_OK", "MXW_ERR_NULL", "MXW_ERR_DIM", "MXW_ERR_ALIGN", "MXW_ERR_DEVICE", "MXW_ERR_LAUNCH",
+                 "MXW_ERR_WORKSPACE"):
         assert name in codes
         assert mxw.strerror(codes[name])
     assert mxw.strerror(-99) == "unknown error"
@@ -78,6 +81,22 @@ P = 0x10000
 ])
 def test_host_argument_checks(args, code):
     assert mxw.mxfp8_wgrad_grouped(*args) == code
+    # the workspace variant runs the same checks first (any workspace)
+    assert mxw.mxfp8_wgrad_grouped_ws(*args, P, 1 << 30) == code
+    assert mxw.mxfp8_wgrad_grouped_ws(*args, 0, 0) == code
+
+
+def test_workspace_size_host_checks():
+    """Invalid sizes are rejected before any device query; valid ones need the
+    device's CU count, so on a host without a gfx950 they report no device."""
+    assert mxw._load().mxfp8_wgrad_workspace_size(0, 512, 128, 256) == -2
+    assert mxw._load().mxfp8_wgrad_workspace_size(4, 500, 128, 256) == -2
+    assert mxw._load().mxfp8_wgrad_workspace_size(4, 512, 120, 256) == -2
+    assert mxw._load().bf16_wgrad_workspace_size(4, 520, 128, 256) == -2
+    import torch
+    if not torch.cuda.is_available():
+        assert mxw._load().mxfp8_wgrad_workspace_size(8, 196608, 1408, 2048) == -4
+        assert mxw.mxfp8_wgrad_grouped_ws(P, P, P, P, P, 4, 512, 128, 256, P, 0, 0, 0) == -4
 
 
 @pytest.mark.parametrize("args,code", [
@@ -98,6 +117,7 @@ def test_host_argument_checks(args, code):
 ])
 def test_bf16_host_argument_checks(args, code):
     assert mxw.bf16_wgrad_grouped(*args) == code
+    assert mxw.bf16_wgrad_grouped_ws(*args, P, 1 << 30) == code
 
 
 def test_bf16_python_face_validates():

@@ -29,12 +29,12 @@ def u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_bf16(cfg, out=None):
+def run_bf16(cfg, out=None, plain=False):
     E, N, K = cfg["E"], cfg["N"], cfg["K"]
     if out is None:
         out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out)
+    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out, plain=plain)
     torch.cuda.synchronize()
     return out
 
@@ -59,13 +59,14 @@ def test_bf16_ragged_shapes(case):
     E, N, K, M, sizes = BF16_CASES[case]
     cfg = W.make_bf16(E, N, K, M, sizes, seed=2600 + case, device=DEV, std=(1.0, 0.5))
     say("bf16 case %d: E=%d N=%d K=%d M=%d columns(2M)=%d" % (case, E, N, K, M, mxw.columns(E, 2 * M, N, K)))
-    bits = bf16_bits(run_bf16(cfg))
     ref = oracle_full(cfg)
-    stats = check_close(bits, ref, what="bf16 case %d" % case)
-    for g in range(E):
-        if sizes[g] == 0:
-            assert (bits[g] == 0).all()
-    print("bf16 case %d max_rel %.3e" % (case, stats["max_rel"]))
+    for plain in (False, True):
+        bits = bf16_bits(run_bf16(cfg, plain=plain))
+        stats = check_close(bits, ref, what="bf16 case %d plain=%s" % (case, plain))
+        for g in range(E):
+            if sizes[g] == 0:
+                assert (bits[g] == 0).all()
+        print("bf16 case %d plain=%s max_rel %.3e" % (case, plain, stats["max_rel"]))
 
 
 def test_bf16_column_mode_selected():

@@ -55,7 +55,7 @@ def test_wgrad_random_shapes(seed):
                                                                     mxw.columns(E, M, N, K)))
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, plain=bool(seed % 2))
     torch.cuda.synchronize()
     bits = bf16_bits(out)
     ref = oracle.wgrad_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
@@ -127,7 +127,7 @@ def test_bf16_wgrad_random_shapes(seed):
                                                                        mxw.columns(E, 2 * M, N, K)))
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out)
+    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out, plain=bool(seed % 2))
     torch.cuda.synchronize()
     bits = bf16_bits(out)
     u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)

@@ -35,21 +35,23 @@ def u16(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+@pytest.mark.parametrize("entry", ["ws", "plain"])
 @pytest.mark.parametrize("E,N,K,M,mode", [
     (256, 16, 48, 16384, "per_tile"),
     (130, 32, 16, 8192, "per_tile"),
     (70, 16, 16, 8192 * 70, "column"),
 ])
-def test_wgrad_many_experts(E, N, K, M, mode):
+def test_wgrad_many_experts(E, N, K, M, mode, entry):
     rng = np.random.default_rng(4000 + E)
     sizes = sizes_for(rng, E, M, 32)
     cfg = W.make_random(E, N, K, M, sizes, seed=4100 + E, device=DEV)
     ncol = mxw.columns(E, M, N, K)
     assert (ncol > 0) == (mode == "column")
-    say("wgrad many experts: E=%d N=%d K=%d M=%d columns=%d empty=%d" % (E, N, K, M, ncol, int((sizes == 0).sum())))
+    say("wgrad many experts [%s]: E=%d N=%d K=%d M=%d columns=%d empty=%d" % (
+        entry, E, N, K, M, 0 if entry == "plain" else ncol, int((sizes == 0).sum())))
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, plain=(entry == "plain"))
     torch.cuda.synchronize()
     bits = bf16_bits(out)
     ref = oracle.wgrad_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
@@ -57,7 +59,8 @@ def test_wgrad_many_experts(E, N, K, M, mode):
     assert (bits[sizes == 0] == 0).all()
 
 
-def test_bf16_wgrad_256_experts():
+@pytest.mark.parametrize("entry", ["ws", "plain"])
+def test_bf16_wgrad_256_experts(entry):
     E, N, K, M = 256, 16, 32, 8192
     rng = np.random.default_rng(4200)
     sizes = sizes_for(rng, E, M, 16)
@@ -65,11 +68,11 @@ def test_bf16_wgrad_256_experts():
     say("bf16 wgrad 256 experts: M=%d" % M)
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out)
+    mxw.wgrad_bf16(cfg["A"], cfg["B"], cfg["offs"], out=out, plain=(entry == "plain"))
     torch.cuda.synchronize()
     bits = bf16_bits(out)
     ref = oracle.bf16_wgrad_f64(u16(cfg["A"]), u16(cfg["B"]), cfg["offs"].cpu().numpy())
-    check_close(bits, ref, what="bf16 wgrad E=256")
+    check_close(bits, ref, what="bf16 wgrad E=256 [%s]" % entry)
     assert (bits[sizes == 0] == 0).all()
 
 

@@ -2,9 +2,10 @@
 
 Every case runs the C-ABI library through the Python binding on seeded inputs
 that the oracle also consumes, with the output NaN-poisoned before the launch so
-that a skipped store shows.  Small cases are compared element by element over
-the whole output; the full-size workloads (the launch configuration the
-benchmark times) on seeded sample points plus edge-tile points.
+that a skipped store shows, through both weight-gradient entry points
+(mxfp8_wgrad_grouped_ws with a workspace, mxfp8_wgrad_grouped without).
+Cases here are compared element by element over the whole output; the
+full-size workloads are in test_gpu_full.py.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 import mxfp8_ragged_grouped_amd as mxw
 import oracle
 import workloads as W
-from helpers import bf16_bits, check_close, host, run_gpu, sample_points
+from helpers import ENTRIES, bf16_bits, check_close, host, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -26,16 +27,20 @@ def say(msg):
     print("[gpu-case] " + msg, flush=True)
 
 
-def full_compare(cfg, what):
-    say("%s: launch E=%d N=%d K=%d M=%d" % (what, cfg["E"], cfg["N"], cfg["K"], cfg["M"]))
-    out = run_gpu(cfg)
-    bits = bf16_bits(out)
+def full_compare(cfg, what, entries=ENTRIES):
+    """Both entry points (or `entries`) against one oracle run, whole output.
+    Returns {entry: (bits, stats)} and the reference."""
     ref = oracle.wgrad_f64(*host(cfg))
-    stats = check_close(bits, ref, what=what)
-    for g in range(cfg["E"]):
-        if int(cfg["sizes"][g]) == 0:
-            assert (bits[g] == 0).all(), "%s: empty expert %d not exact +0" % (what, g)
-    return out, bits, ref, stats
+    res = {}
+    for entry in entries:
+        say("%s [%s]: launch E=%d N=%d K=%d M=%d" % (what, entry, cfg["E"], cfg["N"], cfg["K"], cfg["M"]))
+        bits = bf16_bits(run_gpu(cfg, entry=entry))
+        stats = check_close(bits, ref, what="%s [%s]" % (what, entry))
+        for g in range(cfg["E"]):
+            if int(cfg["sizes"][g]) == 0:
+                assert (bits[g] == 0).all(), "%s [%s]: empty expert %d not exact +0" % (what, entry, g)
+        res[entry] = (bits, stats)
+    return res, ref
 
 
 def from_numpy(A, sA, B, sB, offs, sizes, device=DEV):
@@ -52,9 +57,11 @@ def from_numpy(A, sA, B, sB, offs, sizes, device=DEV):
 
 def test_tiny_config():
     cfg = W.make_config("tiny", device=DEV)
-    out, bits, ref, stats = full_compare(cfg, "tiny")
-    print("tiny max_rel %.3e" % stats["max_rel"])
-    assert stats["max_rel"] < 2 ** -7
+    res, ref = full_compare(cfg, "tiny")
+    for entry, (bits, stats) in res.items():
+        print("tiny [%s] max_rel %.3e" % (entry, stats["max_rel"]))
+        assert stats["max_rel"] < 2 ** -7
+    np.testing.assert_array_equal(res["ws"][0], res["plain"][0])  # no column mode: the same kernel
 
 
 def test_hand_case_embedded(golden_dir):
@@ -76,13 +83,14 @@ def test_hand_case_embedded(golden_dir):
     sA[:2] = np.array(h["sA"], np.uint8)
     sB[:1] = np.array(h["sB"], np.uint8)
     cfg = from_numpy(A, sA, B, sB, h["offs"], [32, 64])
-    say("hand case")
-    bits = bf16_bits(run_gpu(cfg))
     want = np.zeros((2, N, K), np.uint16)
     for g in range(2):
         for n in range(2):
             want[g, n, 0] = int(h["expected_bf16"][g][n][0], 16)
-    np.testing.assert_array_equal(bits, want)
+    for entry in ENTRIES:
+        say("hand case [%s]" % entry)
+        bits = bf16_bits(run_gpu(cfg, entry=entry))
+        np.testing.assert_array_equal(bits, want)
 
 
 RAGGED_CASES = [
@@ -115,15 +123,18 @@ COLUMN_CASES = [
 
 @pytest.mark.parametrize("case", range(len(COLUMN_CASES)))
 def test_column_mode_cases(case):
-    """Column mode (one workgroup per CU, regions split between columns and
-    summed through FP32 partials), whole output, plus bitwise repeat."""
+    """Column mode of the workspace entry (one workgroup per CU, regions split
+    between columns and summed through FP32 partials), whole output, plus
+    bitwise repeat; the same problem through the entry point without a
+    workspace (one workgroup per tile)."""
     E, N, K, M, sizes = COLUMN_CASES[case]
     assert mxw.columns(E, M, N, K) > 0, "case does not select column mode"
     cfg = W.make_random(E, N, K, M, sizes, seed=700 + case, device=DEV)
-    out, bits, ref, stats = full_compare(cfg, "column case %d" % case)
-    print("column case %d max_rel %.3e" % (case, stats["max_rel"]))
+    res, ref = full_compare(cfg, "column case %d" % case)
+    for entry, (bits, stats) in res.items():
+        print("column case %d [%s] max_rel %.3e" % (case, entry, stats["max_rel"]))
     again = bf16_bits(run_gpu(cfg))
-    np.testing.assert_array_equal(again, bits)
+    np.testing.assert_array_equal(again, res["ws"][0])
 
 
 def test_mode_selection():
@@ -139,8 +150,10 @@ def test_mode_selection():
 def test_16b_1k_full():
     """The 16B expert shape at 1,024 tokens/expert, whole output."""
     cfg = W.make_config("16b_1k", device=DEV)
-    out, bits, ref, stats = full_compare(cfg, "16b_1k")
-    print("16b_1k max_rel %.3e" % stats["max_rel"])
+    res, ref = full_compare(cfg, "16b_1k")
+    for entry, (bits, stats) in res.items():
+        print("16b_1k [%s] max_rel %.3e" % (entry, stats["max_rel"]))
+    np.testing.assert_array_equal(res["ws"][0], res["plain"][0])  # one workgroup per tile in both
 
 
 def _exact_problem(rng, E, N, K, M, sizes):
@@ -152,7 +165,8 @@ def _exact_problem(rng, E, N, K, M, sizes):
     return A, sA, B, sB, offs
 
 
-def test_exact_regime_bitwise():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_exact_regime_bitwise(entry):
     """All partial sums exactly representable in FP32: GPU bf16 == RNE(oracle)
     bit for bit, whatever the MFMA's summation order.  A misplaced scale or
     lane shows as whole wrong rows."""
@@ -160,48 +174,51 @@ def test_exact_regime_bitwise():
     sizes = [96, 0, 448, 1024, 32, 160]
     A, sA, B, sB, offs = _exact_problem(rng, 6, 272, 528, 1920, sizes)
     cfg = from_numpy(A, sA, B, sB, offs, sizes)
-    say("exact regime")
-    bits = bf16_bits(run_gpu(cfg))
+    say("exact regime [%s]" % entry)
+    bits = bf16_bits(run_gpu(cfg, entry=entry))
     ref = oracle.wgrad_f64(A, sA, B, sB, offs)
     np.testing.assert_array_equal(bits, oracle.to_bf16_bits(ref))
 
 
-def test_bitwise_repeat():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_bitwise_repeat(entry):
     cfg = W.make_random(4, 528, 784, 3072, [1056, 0, 992, 960], seed=31, device=DEV)
-    say("bitwise repeat")
-    a = bf16_bits(run_gpu(cfg))
-    b = bf16_bits(run_gpu(cfg))
-    c = bf16_bits(run_gpu(cfg, poison=False))
+    say("bitwise repeat [%s]" % entry)
+    a = bf16_bits(run_gpu(cfg, entry=entry))
+    b = bf16_bits(run_gpu(cfg, entry=entry))
+    c = bf16_bits(run_gpu(cfg, poison=False, entry=entry))
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(a, c)
 
 
-def test_padding_garbage_ignored():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_padding_garbage_ignored(entry):
     """NaN codes and 0xFF scales past offs[E-1] never reach the result (bitwise)."""
     sizes = [160, 0, 288, 96]
     cfg = W.make_random(4, 272, 272, 1024, sizes, seed=9, device=DEV)
     used = int(np.sum(sizes))
-    say("padding garbage")
-    clean = bf16_bits(run_gpu(cfg))
+    say("padding garbage [%s]" % entry)
+    clean = bf16_bits(run_gpu(cfg, entry=entry))
     for key, val in (("A", 0x7F), ("B", 0xFF)):
         cfg[key][:, used:] = val
     for key in ("sA", "sB"):
         cfg[key][:, used // 32:] = 0xFF
-    dirty = bf16_bits(run_gpu(cfg))
+    dirty = bf16_bits(run_gpu(cfg, entry=entry))
     np.testing.assert_array_equal(dirty, clean)
 
 
-def test_scale_shift_doubles_bitwise():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_scale_shift_doubles_bitwise(entry):
     """+1 on every scale exponent of one expert's blocks doubles that expert's
     output exactly (power-of-two scaling commutes with FP32 sums and bf16
     rounding) and leaves the others unchanged."""
     sizes = [192, 416, 96, 320]
     cfg = W.make_random(4, 400, 272, 1024, sizes, seed=17, device=DEV)
-    say("scale shift")
-    base = bf16_bits(run_gpu(cfg)).astype(np.uint32)
+    say("scale shift [%s]" % entry)
+    base = bf16_bits(run_gpu(cfg, entry=entry)).astype(np.uint32)
     lo, hi = 192, 192 + 416  # expert 1
     cfg["sA"][:, lo // 32:hi // 32] += 1
-    shifted = bf16_bits(run_gpu(cfg)).astype(np.uint32)
+    shifted = bf16_bits(run_gpu(cfg, entry=entry)).astype(np.uint32)
     nonzero = (base[1] & 0x7FFF) != 0
     # doubling a bf16 = +1 in the exponent field (no overflow/underflow here)
     np.testing.assert_array_equal(shifted[1][nonzero], base[1][nonzero] + 0x80)
@@ -210,45 +227,22 @@ def test_scale_shift_doubles_bitwise():
         np.testing.assert_array_equal(shifted[g], base[g])
 
 
-def test_out_fully_overwritten_and_empty_zero():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_out_fully_overwritten_and_empty_zero(entry):
     cfg = W.make_random(3, 256, 512, 512, [0, 512, 0], seed=3, device=DEV)
-    say("empty experts")
+    say("empty experts [%s]" % entry)
     out = torch.empty((3, 256, 512), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(0x7FC0)
-    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, plain=(entry == "plain"))
     torch.cuda.synchronize()
     bits = bf16_bits(out)
     assert (bits[0] == 0).all() and (bits[2] == 0).all()
     assert np.isfinite(bits[1].astype(np.uint32)).all() and (bits[1] != 0x7FC0).all()
 
 
-def test_all_experts_empty():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_all_experts_empty(entry):
     cfg = W.make_random(2, 256, 256, 64, [0, 0], seed=1, device=DEV)
-    say("all experts empty")
-    bits = bf16_bits(run_gpu(cfg))
+    say("all experts empty [%s]" % entry)
+    bits = bf16_bits(run_gpu(cfg, entry=entry))
     assert (bits == 0).all()
-
-
-# ----------------------------------------------------------------------------
-# full-size workloads, sampled
-# ----------------------------------------------------------------------------
-
-FULL = ["16b_24k", "671b_gateup", "671b_down", "671b_down_zipf", "16b_24k_skew1.7", "16b_24k_ramp"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    cfg = W.make_config(name, device=DEV)
-    say("%s: launch E=%d N=%d K=%d M=%d" % (name, cfg["E"], cfg["N"], cfg["K"], cfg["M"]))
-    out = run_gpu(cfg)
-    # every element finite (no skipped store), empty experts exact zero
-    assert torch.isfinite(out.float()).all().item()
-    for g in range(cfg["E"]):
-        if int(cfg["sizes"][g]) == 0:
-            assert (out[g].view(torch.int16) == 0).all().item()
-    g, n, k = sample_points(cfg, per_expert=192, seed=1)
-    got = bf16_bits(out)[g, n, k]
-    say("%s: oracle on %d points" % (name, len(g)))
-    ref = oracle.wgrad_points(*host(cfg), g, n, k)
-    stats = check_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what=name)
-    print("%s sampled max_rel %.3e" % (name, stats["max_rel"]))

@@ -1,10 +1,12 @@
-"""The weight gradient's two scale paths (needs an MI355X).
+"""The weight gradient's scale paths (needs an MI355X).
 
-With long experts (M >= 4096 E) or scale rows that are not 16-byte aligned
-(M % 512 != 0) the library first rewrites the scale planes so that each
-workgroup's scale loads read consecutive bytes; otherwise the K-loop reads the
-caller's planes directly.  Both feed the same scale bytes to the same MFMA
-sequence, so on one problem they must give identical bits.
+With a workspace, long experts (M >= 4096 E) or scale rows that are not
+16-byte aligned (M % 512 != 0) make the library first rewrite the scale planes
+so that each workgroup's scale loads read consecutive bytes; otherwise, and
+always without a workspace, the K-loop reads the caller's planes directly (16
+bytes of 8 K-steps per row when rows are 16-byte aligned, else the two aligned
+dwords around a row's 2 K-steps).  All feed the same scale bytes to the same
+MFMA sequence, so on one problem they must give identical bits.
 """
 import numpy as np
 import pytest
@@ -24,30 +26,32 @@ def say(msg):
     print("[gpu-case] " + msg, flush=True)
 
 
-def run(cfg, offs):
+def run(cfg, offs, plain=False):
     E = offs.shape[0]
     out = torch.empty((E, cfg["N"], cfg["K"]), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], offs, out=out)
+    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], offs, out=out, plain=plain)
     torch.cuda.synchronize()
     return out
 
 
-def test_shuffled_and_direct_scales_bitwise_equal():
-    """E = 1 with M = 8192 takes the shuffled path (M >= 4096 E); the same
-    operands with a second, empty expert take the direct one.  N x K is large
-    enough that both run one workgroup per tile."""
-    N, K, M = 8192, 8448, 8192
-    cfg = W.make_random(1, N, K, M, [8192 - 96], seed=3100, device=DEV)
-    cfg["A"][:, 8192 - 96:] = 0x7F  # NaN codes and scales in the padding
-    cfg["sA"][:, (8192 - 96) // 32:] = 0xFF
-    assert mxw.columns(1, M, N, K) == 0 and mxw.columns(2, M, N, K) == 0
-    say("scale paths: E=1 (shuffled) vs E=2 (direct), N=%d K=%d M=%d" % (N, K, M))
-    one = run(cfg, cfg["offs"])
-    two = run(cfg, torch.cat([cfg["offs"], cfg["offs"]]))
-    assert torch.equal(one[0].view(torch.int16), two[0].view(torch.int16))
-    assert (two[1].view(torch.int16) == 0).all().item()
-    assert torch.isfinite(one.float()).all().item()
+@pytest.mark.parametrize("M", [8192, 8192 + 160])
+def test_shuffled_and_direct_scales_bitwise_equal(M):
+    """E = 1 with M >= 4096 takes the shuffled path with a workspace; without
+    one the same problem reads the caller's planes (16-byte groups when
+    M % 512 == 0, aligned dword pairs otherwise).  N x K is large enough that
+    the workspace entry runs one workgroup per tile too."""
+    N, K = 8192, 8448
+    used = 8192 - 96
+    cfg = W.make_random(1, N, K, M, [used], seed=3100, device=DEV)
+    cfg["A"][:, used:] = 0x7F  # NaN codes and scales in the padding
+    cfg["sA"][:, used // 32:] = 0xFF
+    assert mxw.columns(1, M, N, K) == 0 and mxw.scale_shuffle(1, M)
+    say("scale paths: shuffled (workspace) vs direct (none), N=%d K=%d M=%d" % (N, K, M))
+    shuf = run(cfg, cfg["offs"])
+    direct = run(cfg, cfg["offs"], plain=True)
+    assert torch.equal(shuf.view(torch.int16), direct.view(torch.int16))
+    assert torch.isfinite(shuf.float()).all().item()
 
 
 @pytest.mark.parametrize("E,N,K,M,sizes", [
