@@ -46,6 +46,11 @@ extern "C" {
 #define MXW_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError) */
 #define MXW_ERR_WORKSPACE (-6) /* workspace NULL, smaller than its size query,
                                   or not 256-byte aligned */
+#define MXW_ERR_SCRATCH (-7)   /* the shape needs more workspace than
+                                  MXW_SCRATCH_BYTES (no-allocation entry) */
+
+/* Size of the static device scratch of mxfp8_wgrad_grouped_noalloc. */
+#define MXW_SCRATCH_BYTES (160u * 1024u * 1024u)
 
 /* Supported ranges (checked on the host, no device access). */
 #define MXW_MAX_EXPERTS 256
@@ -157,6 +162,30 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K);
 int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                            const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * mxfp8_wgrad_grouped_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP-graph capture, tight serving loops, harnesses that
+ * forbid allocation): mxfp8_wgrad_grouped_ws with its workspace taken from a
+ * static device array of MXW_SCRATCH_BYTES (160 MiB) inside the library, which
+ * every device the library runs on holds until the process ends.
+ *
+ * Arguments and results: as mxfp8_wgrad_grouped_ws without the workspace
+ * arguments; the same plan, kernels and bits.  The caller still passes the
+ * operands and out.  A shape whose workspace size
+ * (mxfp8_wgrad_workspace_size) exceeds MXW_SCRATCH_BYTES returns
+ * MXW_ERR_SCRATCH and launches nothing (the 16B shape with 196,608 tokens
+ * needs 149 MiB, 671B gate/up with 262,144 tokens 88 MiB).  It calls no
+ * allocating routine; the first call on a device looks up that device's
+ * scratch address (hipGetSymbolAddress) once.
+ *
+ * Every call on a device shares that device's scratch: calls that overlap in
+ * time on one device (other streams, overlapping graph replays) race on it
+ * and give wrong results.  Each call initialises what it reads; the scratch
+ * keeps the last call's contents.
+ */
+int mxfp8_wgrad_grouped_noalloc(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                                const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream);
 
 /*
  * bf16_wgrad_grouped -- the same weight gradient on plain bfloat16 operands:

@@ -42,7 +42,7 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["wgrad", "mxfp8_wgrad_grouped", "mxfp8_wgrad_grouped_ws", "workspace_size", "wgrad_bf16",
+__all__ = ["wgrad", "mxfp8_wgrad_grouped", "mxfp8_wgrad_grouped_ws", "mxfp8_wgrad_grouped_noalloc", "workspace_size", "wgrad_bf16",
            "bf16_wgrad_grouped", "bf16_wgrad_grouped_ws", "bf16_workspace_size", "grid_size", "columns",
            "scale_shuffle", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size", "quantize_tokens", "mxfp8_quantize_tokens",
            "strerror", "version", "library_path", "MxwError"]
@@ -72,6 +72,8 @@ def _load():
     S = ctypes.c_size_t
     lib.mxfp8_wgrad_grouped_ws.restype = I
     lib.mxfp8_wgrad_grouped_ws.argtypes = [P, P, P, P, P, I, I, I, I, P, P, S, P]
+    lib.mxfp8_wgrad_grouped_noalloc.restype = I
+    lib.mxfp8_wgrad_grouped_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
     lib.mxfp8_wgrad_workspace_size.restype = ctypes.c_int64
     lib.mxfp8_wgrad_workspace_size.argtypes = [I, I, I, I]
     lib.bf16_wgrad_grouped.restype = I
@@ -141,6 +143,13 @@ def mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, E, M, N, K, out, workspace, works
     lib = _load()
     return lib.mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, workspace,
                                       int(workspace_bytes), stream)
+
+
+def mxfp8_wgrad_grouped_noalloc(A, sA, B, sB, offs, E, M, N, K, out, stream=0):
+    """Raw C-ABI call on device addresses (ints): the workspace entry on the
+    library's static scratch (no allocation).  Returns the status code."""
+    lib = _load()
+    return lib.mxfp8_wgrad_grouped_noalloc(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, stream)
 
 
 def workspace_size(E, M, N, K):

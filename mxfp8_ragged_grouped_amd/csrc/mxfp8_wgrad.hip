@@ -1673,6 +1673,29 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   return MXW_OK;
 }
 
+// The no-allocation entry point's scratch: the workspace of a _ws call, held
+// in a static device array instead (each device the library runs on holds
+// its own copy until the process ends).  Its host-side name is not a device
+// address: host code uses only the address hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+static_assert(MXW_SCRATCH_BYTES % kWsAlign == 0, "scratch size");
+__device__ __align__(256) uint8_t scratch[MXW_SCRATCH_BYTES];
+void* g_scratch[64];
+std::mutex g_scratch_mutex;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MXW_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXW_ERR_LAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MXW_OK;
+}
+
 int check_wgrad_args(const void* A, const void* sA, const void* B, const void* sB, const void* offs, const void* out,
                      int E, int M, int N, int K, bool bf) {
   if (!A || (!bf && !sA) || !B || (!bf && !sB) || !offs || !out) return MXW_ERR_NULL;
@@ -1728,6 +1751,20 @@ int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B
   const int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
   if (rc) return rc;
   return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, true, workspace, workspace_bytes, stream);
+}
+
+int mxfp8_wgrad_grouped_noalloc(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                                const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream) {
+  int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
+  if (rc) return rc;
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+  if (make_plan(E, M, 0, N, K, cus, true).bytes > (size_t)MXW_SCRATCH_BYTES) return MXW_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, true, ws, MXW_SCRATCH_BYTES, stream);
 }
 
 int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
@@ -1820,6 +1857,7 @@ const char* mxw_strerror(int code) {
     case MXW_ERR_DEVICE: return "the current device is not gfx950 (or no device)";
     case MXW_ERR_LAUNCH: return "kernel launch failed";
     case MXW_ERR_WORKSPACE: return "workspace missing, smaller than the size query returned, or not 256-byte aligned";
+    case MXW_ERR_SCRATCH: return "the shape needs more workspace than the library's static scratch (MXW_SCRATCH_BYTES)";
     default: return "unknown error";
   }
 }

@@ -55,7 +55,7 @@ def test_grid_size():
 def test_strerror_and_version():
     codes = declared_macros()
     for name in ("MXW_OK", "MXW_ERR_NULL", "MXW_ERR_DIM", "MXW_ERR_ALIGN", "MXW_ERR_DEVICE", "MXW_ERR_LAUNCH",
-                 "MXW_ERR_WORKSPACE"):
+                 "MXW_ERR_WORKSPACE", "MXW_ERR_SCRATCH"):
         assert name in codes
         assert mxw.strerror(codes[name])
     assert mxw.strerror(-99) == "unknown error"
