@@ -265,8 +265,8 @@ def bench_bf16(args):
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(args.workload)},
         "hbm_gbps_algorithmic": round(W.bf16_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
-        "timing": "%d untimed warm-up steps, an untimed ~2 s back-to-back pre-run, a synchronisation, then exactly "
-                  "%d steps between HIP events on the launch stream" % (args.warmup, args.steps),
+        "timing": "%d untimed warm-up steps, an untimed ~%g s back-to-back pre-run, a synchronisation, then exactly "
+                  "%d steps between HIP events on the launch stream" % (args.warmup, args.prerun, args.steps),
     }
     if not args.no_sustained:
         sus = sustained_leg(step, ms, stream, 1.0 if M // E < 8192 else 3.0, tflops_of_ms=tflops_of,
@@ -483,7 +483,7 @@ def _estimate_ms(step, stream, n=8):
     return max(a.elapsed_time(b) / n, 1e-3)
 
 
-def time_steps(step, args, stream, prerun_s=2.0):
+def time_steps(step, args, stream, prerun_s=None):
     """W untimed warm-up steps; an untimed pre-run of back-to-back steps for
     about prerun_s seconds, so that the timed steps run at the clock and power
     the chip keeps under sustained load (a short window straight after a few
@@ -492,6 +492,8 @@ def time_steps(step, args, stream, prerun_s=2.0):
     wall seconds of the timed region)."""
     import torch
 
+    if prerun_s is None:
+        prerun_s = args.prerun
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -556,6 +558,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 torch._grouped_mm context leg")
     ap.add_argument("--no-power", action="store_true", help="skip the power / energy / clock sampling")
     ap.add_argument("--no-sustained", action="store_true", help="skip the two sustained passes (and power)")
+    ap.add_argument("--prerun", type=float, default=2.0,
+                    help="seconds of untimed back-to-back steps before the timed ones (0 for counter runs)")
     ap.add_argument("--no-plain", action="store_true", help="skip timing the entry point without a workspace")
     ap.add_argument("--entry", choices=("ws", "plain"), default="ws",
                     help="weight-gradient entry point of the headline: mxfp8_wgrad_grouped_ws (default) or "
@@ -646,9 +650,9 @@ def main():
                      "kernels_per_call": kernels, "timed": timed},
         "hbm_gbps_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
-        "timing": "%d untimed warm-up steps, an untimed ~2 s back-to-back pre-run (steady clock and power), a "
+        "timing": "%d untimed warm-up steps, an untimed ~%g s back-to-back pre-run (steady clock and power), a "
                   "synchronisation, then exactly %d steps between HIP events on the launch stream" % (
-                      args.warmup, args.steps),
+                      args.warmup, args.prerun, args.steps),
     }
     if args.workload == "16b_24k":
         res["baseline_note"] = ("vs_baseline = value / 2,174 TFLOP/s, the blog's kernel at the 16B ragged shape on "
@@ -661,7 +665,7 @@ def main():
             res["power"] = sus.pop("power")
         res["sustained"] = sus
     if not args.no_plain and not plain_first:
-        pms, _ = time_steps(step_plain, args, stream, prerun_s=1.0)
+        pms, _ = time_steps(step_plain, args, stream, prerun_s=min(args.prerun, 1.0))
         ptf = tflops_of(pms)
         res["plain_entry"] = {"entry": "mxfp8_wgrad_grouped", "ms_per_step": round(pms, 5),
                               "tflops": round(ptf, 2), "frac": round(ptf / PEAK_TFLOPS, 4),

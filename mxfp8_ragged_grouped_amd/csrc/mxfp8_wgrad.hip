@@ -1261,14 +1261,14 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
 // +-448, zero always encoded as +0.  HBM-bound: each element is read once
 // (2 bytes) and written once (1 byte plus 1/32 of a scale byte).
 //
-// A workgroup takes a tile of 128 tokens x 128 hidden: coalesced 16-byte
-// loads of the token rows (256 bytes each) into LDS; thread (h, b) reduces
-// and encodes hidden column h of blocks b and b + 2 straight from LDS (the 64
-// lanes of a wave read one 128-byte row segment at a time); the codes go back
-// through LDS as 128 hidden rows of 128 bytes, 16-byte chunk c of row r at
-// position c ^ ((r / 2) % 8) (the 16-byte writes of 16 lanes, rows r .. r+15
-// at one chunk, then hit 16 distinct bank groups), so that every global
-// store writes whole 128-byte lines of q.
+// A workgroup takes a tile of 128 tokens x 64 hidden: coalesced 16-byte
+// loads of the token rows (128 bytes each, one line) into LDS; thread (h, b)
+// reduces and encodes hidden column h of 32-token block b straight from LDS
+// (the 64 lanes of a wave read one 128-byte row segment at a time); the codes
+// then overwrite the tile in LDS as 64 hidden rows of 128 bytes, 16-byte chunk
+// c of row r at position c ^ ((r / 2) % 8) (the 16-byte writes of 16 lanes,
+// rows r .. r+15 at one chunk, then hit 16 distinct bank groups), so that
+// every global store writes whole 128-byte lines of q.
 // Per-call scale pre-shuffle for the weight gradient (blog section 5.6 names
 // a per-call scale pre-shuffle; this one exists for the memory path).  In the
 // caller's planes [R, M/32] a workgroup's 16-byte group of 8 K-steps sits in
