@@ -4,9 +4,8 @@ the CPU oracle (needs an MI355X).
 Each case NaN-poisons the output, runs the C-ABI library through the Python
 binding, and compares every row that belongs to an expert with the oracle to
 the same tolerance as the weight gradient; rows past the last expert must keep
-their poison (they are never written).  Small cases cover the whole output;
-the full-size workloads (the benchmark's launch configuration) are checked on
-seeded sample points plus the edges of partial tiles.
+their poison (they are never written).  Every case covers the whole output,
+the full-size workloads (the benchmark's launch configuration) included.
 """
 import numpy as np
 import pytest
@@ -115,39 +114,19 @@ def test_rows_all_experts_empty():
     assert (run_rows(cfg) == BF16_NAN).all()
 
 
-def sample_rows(cfg, n_rand=2048, seed=0):
-    """Seeded (row, column) points: random rows of every expert plus the first
-    and last rows of every expert and of every 256-row tile, against the edge
-    columns of the last partial column tile."""
-    rng = np.random.default_rng(seed)
-    offs = cfg["offs"].cpu().numpy().astype(np.int64)
-    starts = np.concatenate([[0], offs[:-1]])
-    N = cfg["N"]
-    rows, cols = [], []
-    edge_cols = sorted({0, 1, 7, 8, 127, 128, 255, N - 1, N - 8, N - 129, (N // 256) * 256 % N})
-    edge_cols = [c for c in edge_cols if 0 <= c < N]
-    for s, e in zip(starts, offs):
-        if e <= s:
-            continue
-        r = rng.integers(s, e, n_rand // len(offs))
-        rows += r.tolist()
-        cols += rng.integers(0, N, r.shape[0]).tolist()
-        for t0 in range(int(s), int(e), 256):
-            for rr in {t0, min(t0 + 255, int(e) - 1)}:
-                rows += [rr] * len(edge_cols)
-                cols += edge_cols
-    return np.array(rows, np.int64), np.array(cols, np.int32)
-
-
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["16b_fwd", "16b_fwd_down"])
-def test_rows_full_size_sampled(name):
+def test_rows_full_size_whole_output(name):
+    """The 16B gate/up and down widths at full size (196,608 routed rows), in
+    the benchmark's launch configuration: every row of every expert against
+    the oracle (rms over the whole reference), rows past the last expert
+    never written."""
     cfg = W.make_rows_config(name, device=DEV)
-    say("%s: launch R=%d C=%d N=%d (sampled check)" % (name, cfg["R"], cfg["C"], cfg["N"]))
+    say("%s: launch R=%d C=%d N=%d (whole output)" % (name, cfg["R"], cfg["C"], cfg["N"]))
     bits = run_rows(cfg)
-    m, n = sample_rows(cfg, seed=5)
-    ref = oracle.rows_points(*host_rows(cfg), m, n)
     used = int(np.asarray(cfg["sizes"]).sum())
-    rms = float(np.sqrt(np.mean(ref ** 2)))
-    check_close(bits[m, n], ref, rms=rms, what=name)
+    say("%s: oracle on %d x %d outputs" % (name, used, cfg["N"]))
+    ref = oracle.rows_f64(*host_rows(cfg))
+    st = check_close(bits[:used], ref[:used], what=name)
+    print("%s whole output max_rel %.3e" % (name, st["max_rel"]))
     assert (bits[used:] == BF16_NAN).all()
