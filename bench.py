@@ -262,7 +262,8 @@ def bench_bf16(args):
                    "entry": "bf16_wgrad_grouped" if plain else "bf16_wgrad_grouped_ws",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(args.workload)},
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(args.workload + ("_plain" if plain else ""))},
         "hbm_gbps_algorithmic": round(W.bf16_algorithmic_bytes(cfg) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
         "timing": "%d untimed warm-up steps, an untimed ~%g s back-to-back pre-run, a synchronisation, then exactly "
@@ -646,7 +647,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_TFLOPS, 4),
-                     "traffic": None if plain_first else traffic,
+                     "traffic": load_traffic(args.workload + "_plain") if plain_first else traffic,
                      "kernels_per_call": kernels, "timed": timed},
         "hbm_gbps_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
