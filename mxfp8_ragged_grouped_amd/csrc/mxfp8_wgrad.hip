@@ -140,9 +140,6 @@ constexpr int kColWaves = 4;
 constexpr int kColTokens = 8192;
 // the weight gradient shuffles its scale planes when M >= kShufTokens * E
 constexpr int kShufTokens = 4096;
-// E4M3 weight gradient on 128 x 128 tiles, two workgroups per CU, when
-// M < kSmallTokens * E and scale rows are 16-byte aligned
-constexpr int kSmallTokens = 4096;
 // row-ragged GEMM: whole-tile scale blocks in the raw area when C <= kWholeC
 // (256 rows x C / 32 bytes per operand, plus the dword read past a row's last
 // pair, within kWholeOp dwords each)
@@ -1185,342 +1182,6 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   }
 }
 
-// ---- short experts: 128 x 128 tiles, two workgroups per CU ----------------------
-// With ~1,000 tokens per expert a 256 x 256 tile's K-loop is about as long as
-// its fixed costs (setup and first-pair latency, then 128 KiB of bf16 stores),
-// and one workgroup per CU cannot overlap them.  This body computes 128 x 128
-// tiles with half the registers (64 FP32 accumulators per lane: each wave owns
-// 64 x 64) and half the LDS (80 KiB), so two workgroups share a CU and one's
-// prologue and epilogue run under the other's K-loop.  Per 64-token step a CU
-// then moves 1.5x the LDS bytes per MFMA of the large tile (a 128 x 128 tile
-// reads each staged byte 2x, not 4x), so the K-loop is LDS-bound at about two
-// thirds of the MFMA rate; it is used where the fixed costs dominate.  Staging
-// (pairs of K-steps in 128-byte rows, whole-line loads), masking, scales
-// (16-byte groups of 8 K-steps per row, read straight from the caller's
-// planes) and the MFMA sequence per output element are the large tile's, so
-// the two bodies give identical bits.
-constexpr int kSTile = 128;
-constexpr int kSOpBytes = kSTile * kRowBytes;  // 16 KiB per operand per stage
-constexpr int kSDataDma = 8;                   // loads per wave per pair: 4 row groups of A, 4 of B
-constexpr int kSOddLoads = 5;                  // of which the odd step issues 5, the even step 3
-
-struct SmemS {
-  uint8_t data[2][2][kSOpBytes];     // [stage][A|B][128 rows x 128 B], chunk-swizzled as in Smem
-  uint32_t raw[3 * 2 * kSTile * 4];  // scale groups: [group % 3][op][row][4 dwords]
-  int start[MXW_MAX_EXPERTS];
-  int len[MXW_MAX_EXPERTS];
-  uint8_t order[MXW_MAX_EXPERTS];
-};
-static_assert(2 * sizeof(SmemS) <= 160 * 1024, "two workgroups per CU");
-
-// exact +0 over 128 x 128 tile (tn, tk) of expert g's output
-__device__ __forceinline__ void zero_tile_s(const Params& p, int g, int tn, int tk) {
-  const int N = p.N, K = p.K;
-  const int n0 = tn * kSTile, k0 = tk * kSTile;
-  const int rows = min(kSTile, N - n0), cols = min(kSTile, K - k0);
-  const int chunks = cols / 8;
-  const v4i z = {0, 0, 0, 0};
-  uint16_t* o = p.out + (size_t)g * N * K;
-  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
-    const int r = i / chunks, c = i - r * chunks;
-    *(v4i*)(o + (size_t)(n0 + r) * K + k0 + 8 * c) = z;
-  }
-}
-
-// Expert g's window [start, end) into 128 x 128 tile (tn, tk).  Scale rows are
-// 16-byte aligned (M % 512 == 0).
-__device__ __forceinline__ void run_small(const Params& p, SmemS& sm, int g, int tn, int tk, int start, int end) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int M = p.M, N = p.N, K = p.K;
-  const int n0 = tn * kSTile, k0 = tk * kSTile;
-  const int rowsA = min(kSTile, N - n0), rowsB = min(kSTile, K - k0);
-  uint16_t* otile = p.out + (size_t)g * N * K + (size_t)n0 * K + k0;
-  const uint32_t sbytes = (uint32_t)M >> 5;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (size_t)n0 * M, (uint32_t)rowsA * (uint32_t)M);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + (size_t)k0 * M, (uint32_t)rowsB * (uint32_t)M);
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.sA + (size_t)n0 * sbytes, (uint32_t)rowsA * sbytes);
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.sB + (size_t)k0 * sbytes, (uint32_t)rowsB * sbytes);
-
-  // Data DMA: wave w fills row groups 4w .. 4w+3 (8 rows x 128 B each) of both
-  // operands; load q of a pair takes row group (q + rot) % 4 (rot even, so the
-  // parity -- and with it the swizzle of the lane's chunk -- is q's)
-  const int lrow = lane >> 3;
-  const int ch_e = (lane & 7) ^ swz(lrow), ch_o = (lane & 7) ^ swz(8 + lrow);
-  const int rot = 2 * ((tk + tn) & 1);
-  uint32_t vrow[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    vrow[q] = (uint32_t)((wave * 4 + ((q + rot) & 3)) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
-  const int sbl_e = ch_e >> 1, sbl_o = ch_o >> 1;
-  const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_addr(&sm.data[0][0][wave * 4 * 1024]));
-  // load D of pair P into stage buf: row group D / 2 of A (D even) or B (D odd)
-  auto dma_pair = [&](int D, int buf, int P, uint32_t live) {
-    const int qi = D >> 1, op = D & 1;
-    const bool ok = (live >> ((qi & 1) ? sbl_o : sbl_e)) & 1u;
-    dma16(op ? rB : rA, dbase + (uint32_t)((buf * 2 + op) * kSOpBytes + ((qi + rot) & 3) * 1024), ok ? vrow[qi] : kOob,
-          (uint32_t)(P * kPair));
-  };
-  // Scales: wave w loads operand w / 2, rows 64 (w % 2) + lane: one 16-byte
-  // load per wave covers a group (8 K-steps) of its 64 rows
-  const int sop = wave >> 1;
-  const uint32_t srow_off = (uint32_t)(64 * (wave & 1) + lane) * sbytes;
-  auto dma_scale_grp = [&](int G) {
-    const uint32_t dst = lds_addr(&sm.raw[(((G % 3) * 2 + sop) * kSTile + 64 * (wave & 1)) * 4]);
-    dma16(sop ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), srow_off + 16u * (uint32_t)G, 0u);
-  };
-
-  // MFMA geometry: wave (wn, wk) owns A rows 64 wn .. +64 and B rows 64 wk .. +64
-  const int wn = wave >> 1, wk = wave & 1;
-  const int fr = lane & 31, fq = lane >> 5;
-  const int frag_lo0 = fr * kRowBytes + ((fq ^ swz(fr)) << 4);
-  const int frag_hi0 = fr * kRowBytes + (((fq + 2) ^ swz(fr)) << 4);
-  const int frag_lo1 = fr * kRowBytes + (((fq + 4) ^ swz(fr)) << 4);
-  const int frag_hi1 = fr * kRowBytes + (((fq + 6) ^ swz(fr)) << 4);
-  v16f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[i][t] = (v16f){};
-
-  const int s0 = (start / kPair) * 2;
-  const int s_end = (end + kStep - 1) / kStep;
-  const int nsteps = (s_end - s0 + 3) & ~3;
-  const int qs = start >> 5, qn = (end - start) >> 5;
-  {
-    const int G0 = s0 / 8;
-    dma_scale_grp(G0);
-    dma_scale_grp(G0 + 1);
-    const int P0 = s0 >> 1;
-    const uint32_t l0 = live_mask_pair(P0, qs, qn), l1 = live_mask_pair(P0 + 1, qs, qn);
-#pragma unroll
-    for (int D = 0; D < kSDataDma; ++D) dma_pair(D, 0, P0, l0);
-#pragma unroll
-    for (int D = 0; D < kSOddLoads; ++D) dma_pair(D, 1, P0 + 1, l1);
-  }
-  wait_vm<kSOddLoads>();  // this wave's scale groups and pair s0/2 have landed
-  __syncthreads();
-
-  const int msb = lane >> 5;
-  const uint32_t mshift = 8u * (uint32_t)msb;
-  auto read_raw = [&](int x, uint32_t* a2, uint32_t* b2) {  // x: first K-step of a pair
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int RA = wn * 64 + 32 * i + fr, RB = wk * 64 + 32 * i + fr;
-      const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
-      a2[i] = sm.raw[((slot * 2 + 0) * kSTile + RA) * 4 + dw];
-      b2[i] = sm.raw[((slot * 2 + 1) * kSTile + RB) * 4 + dw];
-    }
-  };
-  auto finish_sregs = [&](int x, const uint32_t* a2, const uint32_t* b2, uint32_t* ra2, uint32_t* rb2) {
-    const uint32_t pm = (((live_mask_q(x, qs, qn) >> msb) & 1u) ? 0xFFu : 0u) |
-                        (((live_mask_q(x + 1, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra2[i] = (a2[i] >> mshift) & pm;
-      rb2[i] = (b2[i] >> mshift) & pm;
-    }
-  };
-
-  v8i fa[2][2], fb[2][2];
-  uint32_t sra[2][2], srb[2][2];  // [pair parity][32-row block]
-  uint32_t rawa[2], rawb[2];
-  read_raw(s0, rawa, rawb);
-  finish_sregs(s0, rawa, rawb, sra[0], srb[0]);
-  {
-    const uint8_t* ta = sm.data[0][0] + (wn * 64) * kRowBytes;
-    const uint8_t* tb = sm.data[0][1] + (wk * 64) * kRowBytes;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) fb[0][t] = frag(tb + t * 32 * kRowBytes, frag_lo0, frag_hi0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) fa[0][t] = frag(ta + t * 32 * kRowBytes, frag_lo0, frag_hi0);
-  }
-  uint32_t livep = live_mask_pair((s0 >> 1) + 2, qs, qn);  // pair issued at the next odd step
-  uint32_t va[4];
-  {
-    const uint32_t l1 = live_mask_pair((s0 >> 1) + 1, qs, qn);
-    const bool lok_e = (l1 >> sbl_e) & 1u, lok_o = (l1 >> sbl_o) & 1u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? vrow[q] : kOob;
-  }
-
-  // load D of a pair: odd step U issues the pair after next into stage U / 2,
-  // even step U the rest of the next pair into stage (U / 2 + 1) % 2
-#define MXW_SDMA(D, STG, SOFF) \
-  dma16(((D) & 1) ? rB : rA, dbase + (uint32_t)(((STG) * 2 + ((D) & 1)) * kSOpBytes + (((((D) >> 1) + rot) & 3) * 1024)), \
-        va[(D) >> 1], SOFF)
-  for (int jj = 0;; jj += 4) {
-    // a scale group per two iterations: the even ones load this wave's
-    // operand of group (s0 + 4 jj') / 8 + 2
-    const bool sload = ((jj >> 2) & 1) == 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = jj + u;
-      const int s = s0 + j;
-      const int cur = u & 1, nxt = cur ^ 1;
-      const int nst = ((u + 1) >> 1) & 1, nhalf = (u + 1) & 1;  // stage and half of step j + 1
-      const uint8_t* na = sm.data[nst][0] + (wn * 64) * kRowBytes;
-      const uint8_t* nb = sm.data[nst][1] + (wk * 64) * kRowBytes;
-      const int flo = nhalf ? frag_lo1 : frag_lo0, fhi = nhalf ? frag_hi1 : frag_hi0;
-      __builtin_amdgcn_sched_barrier(0);
-      wait_lgkm_all();  // this step's fragments are in registers
-      __builtin_amdgcn_sched_barrier(0);
-      int sb = s;
-      asm volatile("" : "+s"(sb));
-      const uint32_t soff = (u & 1) ? (uint32_t)(((sb >> 1) + 2) * kPair) : (uint32_t)(((sb >> 1) + 1) * kPair);
-      const int stg = (u & 1) ? (u >> 1) : (((u >> 1) + 1) & 1);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i = m >> 1, t = m & 1;  // B block i, A block t
-        acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
-                                  (int)sra[u >> 1][t]);
-        if (m == 0 && (u & 1)) {
-          const bool lok_e = (livep >> sbl_e) & 1u, lok_o = (livep >> sbl_o) & 1u;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) va[q] = ((q & 1) ? lok_o : lok_e) ? vrow[q] : kOob;
-          __builtin_amdgcn_sched_barrier(0);
-          // the next pair has landed: only the previous even step's scale
-          // load (issued after its data loads) may be outstanding
-          if (u == 1 && sload) wait_vm<1>();
-          else wait_vm<0>();
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // data loads: odd step 0 .. 4 after MFMAs 0, 1, 1, 2, 3; even step 5 .. 7 after MFMAs 0 .. 2
-        if (u & 1) {
-          if (m == 0) MXW_SDMA(0, stg, soff);
-          if (m == 1) { MXW_SDMA(1, stg, soff); MXW_SDMA(2, stg, soff); }
-          if (m == 2) MXW_SDMA(3, stg, soff);
-          if (m == 3) MXW_SDMA(4, stg, soff);
-        } else {
-          if (m == 0) MXW_SDMA(5, stg, soff);
-          if (m == 1) MXW_SDMA(6, stg, soff);
-          if (m == 2) MXW_SDMA(7, stg, soff);
-        }
-        // fragments of step j + 1 (odd steps: after the barrier)
-        if (m == 0) {
-          fa[nxt][0] = frag(na, flo, fhi);
-          fb[nxt][0] = frag(nb, flo, fhi);
-        }
-        if (m == 1) {
-          fa[nxt][1] = frag(na + 32 * kRowBytes, flo, fhi);
-          fb[nxt][1] = frag(nb + 32 * kRowBytes, flo, fhi);
-        }
-        if ((u & 1) && m == 1) {
-          int sq = s;
-          asm volatile("" : "+s"(sq));
-          read_raw(sq + 1, rawa, rawb);  // the next pair's raw scale dwords (landed with it)
-        }
-        if (m == 3) {
-          int sp = s;
-          asm volatile("" : "+s"(sp));
-          if (u & 1) finish_sregs(sp + 1, rawa, rawb, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
-          else livep = live_mask_pair(((sp + 1) >> 1) + 2, qs, qn);
-          if (u == 0 && sload) {  // after the step's data loads (vmcnt order)
-            dma_scale_grp(((s0 + jj) >> 3) + 2);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (jj + 4 >= nsteps) break;
-  }
-#undef MXW_SDMA
-  wait_vm_all();  // no LDS-direct load may outlive the workgroup
-
-  // epilogue: bf16 RNE in registers, then through this wave's 8 KiB of the idle
-  // stage area (64 rows of 128 bytes: 16-byte chunk c of row n at c ^ ((n / 2)
-  // % 8), its 8-byte halves swapped when (n / 16) is odd, so the 8-byte writes
-  // of 32 lanes and the 16-byte reads of 16 lanes hit distinct banks), then
-  // whole 128-byte lines to out.  Block (i, t): lane l register r holds
-  // k = 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, n = 32 t + l % 32.
-  __syncthreads();
-  uint8_t* ep = &sm.data[0][0][0] + wave * 8192;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = 32 * t + fr, c = 4 * i + q;
-        uint2 w;
-        w.x = pack_bf16x2(acc[i][t][4 * q], acc[i][t][4 * q + 1]);
-        w.y = pack_bf16x2(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]);
-        *(uint2*)(ep + nl * 128 + ((c ^ ((nl >> 1) & 7)) << 4) + ((fq ^ ((nl >> 4) & 1)) << 3)) = w;
-      }
-  __syncthreads();
-  const int rsub = lane >> 3, cl = lane & 7;
-  v4i d[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int nl = 8 * x + rsub;
-    d[x] = *(const v4i*)(ep + nl * 128 + ((cl ^ ((nl >> 1) & 7)) << 4));
-  }
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int nl = 8 * x + rsub;
-    if ((nl >> 4) & 1) d[x] = (v4i){d[x].z, d[x].w, d[x].x, d[x].y};
-    const int n = wn * 64 + nl, kk = wk * 64 + cl * 8;
-    if (n < rowsA && kk < rowsB) *(v4i*)(otile + (size_t)n * K + kk) = d[x];
-  }
-}
-
-// The weight gradient on 128 x 128 tiles (see run_small): one workgroup per
-// (expert, tile), longest experts first, XCD rectangles over the 128-tile
-// grid, two workgroups per CU.
-__global__ __launch_bounds__(kThreads, 2) void wgrad_small_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) SmemS sm;
-  const int tid = threadIdx.x;
-  const int E = p.E, M = p.M;
-  const int T = p.tilesN * p.tilesK;
-  const int bid = blockIdx.x;
-  if (tid < E) {
-    int e = min(max(p.offs[tid], 0), M);
-    const int st = tid ? min(max(p.offs[tid - 1], 0), M) : 0;
-    if (e < st) e = st;
-    sm.start[tid] = st;
-    sm.len[tid] = e - st;
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int mine = sm.len[tid];
-    int r = 0;
-    for (int u = 0; u < E; ++u) {
-      const int l = sm.len[u];
-      r += (l > mine) || (l == mine && u < tid);
-    }
-    sm.order[r] = (uint8_t)tid;
-  }
-  __syncthreads();
-  int d, tn, tk;
-  if (p.regN) {
-    const int per = p.regN * p.regK;
-    const int x = bid & 7, i = bid >> 3;
-    d = i / per;
-    const int v = i - d * per;
-    const int bandsz = p.band * p.regK;
-    const int bnd = v / bandsz, w = v - bnd * bandsz;
-    const int hb = min(p.band, p.regN - bnd * p.band);
-    const int c = w / hb;
-    tn = (x / p.regB) * p.regN + bnd * p.band + (w - c * hb);
-    tk = (x % p.regB) * p.regK + c;
-  } else {
-    d = bid / T;
-    const int u = bid - d * T;
-    tn = u / p.tilesK;
-    tk = u - tn * p.tilesK;
-  }
-  const int g = __builtin_amdgcn_readfirstlane((int)sm.order[d]);
-  const int start = __builtin_amdgcn_readfirstlane(sm.start[g]);
-  const int len = __builtin_amdgcn_readfirstlane(sm.len[g]);
-  if (len == 0) {
-    zero_tile_s(p, g, tn, tk);
-    return;
-  }
-  run_small(p, sm, g, tn, tk, start, start + len);
-}
-
 // Row-ragged grouped GEMM (the forward and data-gradient GEMMs of the layer):
 // out[m][n] = sum_c A[m][c] B[g][n][c] for the rows m of expert g.  Expert
 // g's rows [start_g, end_g) are cut into 256-row tiles (the last one
@@ -1856,7 +1517,6 @@ size_t round_ws(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 struct Plan {
   int ncol, regions;
   bool shuffle;
-  bool small;  // 128 x 128 tiles (wgrad_small_kernel)
   int sgroups;
   size_t flags_off, part_off, scaleA_off, scaleB_off, bytes;
 };
@@ -1864,10 +1524,7 @@ struct Plan {
 Plan make_plan(int E, int Mb, int tshift, int N, int K, int cus, bool ws) {
   Plan pl = {};
   const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
-  // short experts (E4M3, 16-byte aligned scale rows): neither column mode
-  // nor the pre-shuffle applies, with or without a workspace
-  pl.small = tshift == 0 && (Mb & 511) == 0 && (int64_t)Mb < (int64_t)kSmallTokens * E;
-  if (!ws || pl.small) {
+  if (!ws) {
     int regions = 0;
     (void)plan_columns(E, Mb, N, K, cus, &regions);
     pl.regions = regions;
@@ -1920,7 +1577,6 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MXW_ERR_WORKSPACE;
   }
   uint8_t* wsb = (uint8_t*)ws;
-  const int tile = pl.small ? kSTile : kTile;
   Params p = {};
   p.A = A;
   p.sA = sA;
@@ -1933,8 +1589,8 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   p.N = N;
   p.K = K;
   p.tshift = tshift;
-  p.tilesN = (N + tile - 1) / tile;
-  p.tilesK = (K + tile - 1) / tile;
+  p.tilesN = (N + kTile - 1) / kTile;
+  p.tilesK = (K + kTile - 1) / kTile;
   // XCD regions: split the tile grid a x b = 8 ways into equal rectangles,
   // the most square split (fewest distinct A + B stripes per rectangle)
   p.regN = p.regK = p.regB = p.band = 0;
@@ -1964,13 +1620,7 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   }
   const dim3 g((unsigned)(pl.ncol ? pl.ncol * kMem : grid)), blk(kThreads);
   hipStream_t st = (hipStream_t)stream;
-  if (pl.small) {
-    const int64_t sgrid = (int64_t)E * p.tilesN * p.tilesK;
-    if (sgrid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
-    p.sAs = p.sBs = nullptr;
-    p.sgroups = 0;
-    hipLaunchKernelGGL(wgrad_small_kernel, dim3((unsigned)sgrid), blk, 0, st, p);
-  } else if (tshift) {
+  if (tshift) {
     // bf16: no scales; column mode's counters are cleared by a first kernel
     if (pl.ncol) {
       hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, p.flags, pl.ncol * kMem);

@@ -246,40 +246,3 @@ def test_all_experts_empty(entry):
     say("all experts empty [%s]" % entry)
     bits = bf16_bits(run_gpu(cfg, entry=entry))
     assert (bits == 0).all()
-
-
-def _pad_tokens(cfg, pad):
-    """The same problem with `pad` more padding tokens (NaN codes, 0xFF scales)."""
-    c = dict(cfg)
-    for k, fill in (("A", 0x7F), ("B", 0xFF)):
-        t = cfg[k]
-        c[k] = torch.cat([t, torch.full((t.shape[0], pad), fill, dtype=t.dtype, device=t.device)], dim=1).contiguous()
-    for k in ("sA", "sB"):
-        t = cfg[k]
-        c[k] = torch.cat([t, torch.full((t.shape[0], pad // 32), 0xFF, dtype=t.dtype, device=t.device)],
-                         dim=1).contiguous()
-    c["M"] = cfg["M"] + pad
-    return c
-
-
-@pytest.mark.parametrize("entry", ENTRIES)
-@pytest.mark.parametrize("case", [
-    # E, N, K, M, sizes, pad: M < 4096 E with 16-byte scale rows selects the 128 x 128
-    # two-workgroups-per-CU body; the padded width selects the 256 x 256 body
-    (8, 1408, 2048, 8192, None, 32),                      # the 16B shape at 1,024 tokens/expert; paired scales
-    (2, 272, 528, 4096, [1824, 2048], 4608),              # padded to 8,704 = 4352 E: grouped scales
-    (5, 144, 400, 2048, [0, 608, 96, 1024, 32], 64),      # partial tiles, empty experts, short groups
-])
-def test_small_and_large_tile_bodies_bitwise(case, entry):
-    """The 128 x 128 body and the 256 x 256 body run the same MFMA sequence for
-    every output element, so they give identical bits."""
-    E, N, K, M, sizes, pad = case
-    if sizes is None:
-        cfg = W.make_config("16b_1k", device=DEV)
-    else:
-        cfg = W.make_random(E, N, K, M, sizes, seed=900 + M, device=DEV)
-    say("tile bodies [%s]: E=%d N=%d K=%d M=%d (+%d)" % (entry, E, N, K, M, pad))
-    small = bf16_bits(run_gpu(cfg, entry=entry))
-    large = bf16_bits(run_gpu(_pad_tokens(cfg, pad), entry=entry))
-    np.testing.assert_array_equal(small, large)
-    check_close(small, oracle.wgrad_f64(*host(cfg)), what="tile bodies")
