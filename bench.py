@@ -484,6 +484,20 @@ def _estimate_ms(step, stream, n=8):
     return max(a.elapsed_time(b) / n, 1e-3)
 
 
+def padded_rows(cfg, ld):
+    """The operands copied into row-strided storage ([rows, ld] buffers whose
+    first M columns hold the values; the rest never read), as [:, :M] views."""
+    import torch
+    c = dict(cfg)
+    M = cfg["M"]
+    for k, div in (("A", 1), ("B", 1), ("sA", 32), ("sB", 32)):
+        t = cfg[k]
+        buf = torch.zeros((t.shape[0], ld // div), dtype=t.dtype, device=t.device)
+        buf[:, :M // div] = t
+        c[k] = buf[:, :M // div]
+    return c
+
+
 def time_steps(step, args, stream, prerun_s=None):
     """W untimed warm-up steps; an untimed pre-run of back-to-back steps for
     about prerun_s seconds, so that the timed steps run at the clock and power
@@ -562,6 +576,9 @@ def main():
     ap.add_argument("--prerun", type=float, default=2.0,
                     help="seconds of untimed back-to-back steps before the timed ones (0 for counter runs)")
     ap.add_argument("--no-plain", action="store_true", help="skip timing the entry point without a workspace")
+    ap.add_argument("--no-padded", action="store_true", help="skip timing the row-padded layout")
+    ap.add_argument("--ld-pad", type=int, default=0,
+                    help="store the operands with rows M + LD_PAD tokens apart (a multiple of 32) for the headline")
     ap.add_argument("--entry", choices=("ws", "plain"), default="ws",
                     help="weight-gradient entry point of the headline: mxfp8_wgrad_grouped_ws (default) or "
                          "mxfp8_wgrad_grouped")
@@ -596,9 +613,14 @@ def main():
     torch.cuda.set_device(dev)
     cfg = W.make_config(args.workload, device=dev)
     E, N, K, M = cfg["E"], cfg["N"], cfg["K"], cfg["M"]
+    if args.ld_pad:
+        if args.entry == "plain":
+            sys.exit("--ld-pad needs the workspace entry (the entry without one takes contiguous operands)")
+        cfg = padded_rows(cfg, M + args.ld_pad)
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-    ws_bytes = mxw.workspace_size(E, M, N, K)
+    ld = cfg["A"].stride(0)
+    ws_bytes = mxw.workspace_size(E, M, N, K, ld)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     plain_first = args.entry == "plain"
 
@@ -642,12 +664,14 @@ def main():
                    "tokens_per_expert_mean": M // E, "busiest_over_mean": round(cfg["skew"], 3),
                    "routing_seed": cfg["routing_seed"], "value_seed": cfg["value_seed"],
                    "entry": "mxfp8_wgrad_grouped" if plain_first else "mxfp8_wgrad_grouped_ws",
+                   "row_stride_tokens": ld,
                    "workspace_bytes": 0 if plain_first else ws_bytes,
                    "columns": 0 if plain_first else mxw.columns(E, M, N, K),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_TFLOPS, 4),
-                     "traffic": load_traffic(args.workload + "_plain") if plain_first else traffic,
+                     "traffic": load_traffic(args.workload + "_plain") if plain_first else (
+                         load_traffic("%s_ld%d" % (args.workload, args.ld_pad)) if args.ld_pad else traffic),
                      "kernels_per_call": kernels, "timed": timed},
         "hbm_gbps_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 3),
@@ -665,6 +689,22 @@ def main():
         if "power" in sus:
             res["power"] = sus.pop("power")
         res["sustained"] = sus
+    if not args.no_padded and not plain_first and not args.ld_pad:
+        # the same operands in row-padded storage (ld = M + 128 tokens: the
+        # layout mxfp8_quantize_tokens writes with ld), the same entry point
+        pc = padded_rows(cfg, M + 128)
+        pws = torch.empty(max(mxw.workspace_size(E, M, N, K, M + 128), 1), dtype=torch.uint8, device=dev)
+        step_pad = lambda: mxw.wgrad(pc["A"], pc["sA"], pc["B"], pc["sB"], pc["offs"], out=out, stream=stream,
+                                     workspace=pws)
+        pdms, _ = time_steps(step_pad, args, stream, prerun_s=min(args.prerun, 1.0))
+        res["padded_rows"] = {"row_stride_tokens": M + 128, "ms_per_step": round(pdms, 5),
+                              "tflops": round(tflops_of(pdms), 2), "frac": round(tflops_of(pdms) / PEAK_TFLOPS, 4),
+                              "traffic": load_traffic("%s_ld128" % args.workload),
+                              "what": "the same call on the same values stored with rows M + 128 tokens apart (no "
+                                      "multiple-of-64 KiB row stride, so the lines a tile reads at once spread over "
+                                      "the L2 sets), same timing method, this process; a layout choice of the "
+                                      "operands' producer, not the headline's layout"}
+        del pc, pws
     if not args.no_plain and not plain_first:
         pms, _ = time_steps(step_plain, args, stream, prerun_s=min(args.prerun, 1.0))
         ptf = tflops_of(pms)

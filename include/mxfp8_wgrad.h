@@ -107,15 +107,16 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
 
 /*
  * mxfp8_wgrad_workspace_size -- bytes of device workspace that
- * mxfp8_wgrad_grouped_ws needs for (E, M, N, K) on the current device (0 if
- * it needs none), or a negative MXW_ERR_* code.  Reads device properties
- * only.  128 MiB of FP32 partial tiles on a 256-CU device when the launch
- * runs in column mode (mxw_columns() > 0), plus (ceil(N/256) + ceil(K/256))
- * * ceil(M/512) * 4 KiB of shuffled scales when it pre-shuffles
- * (mxw_scale_shuffle()): 149 MiB at the 16B shape with 196,608 tokens,
- * 88 MiB at 671B gate/up with 262,144.
+ * mxfp8_wgrad_grouped_ws needs for (E, M, ld, N, K) on the current device (0
+ * if it needs none), or a negative MXW_ERR_* code.  ld is the row stride
+ * described there (0 = M).  Reads device properties only.  128 MiB of FP32
+ * partial tiles on a 256-CU device when the launch runs in column mode
+ * (mxw_columns() > 0), plus (ceil(N/256) + ceil(K/256)) * ceil(M/512) * 4 KiB
+ * of shuffled scales when it pre-shuffles (M >= 4096 E, or ld % 512 != 0):
+ * 149 MiB at the 16B shape with 196,608 tokens, 88 MiB at 671B gate/up with
+ * 262,144.
  */
-int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K);
+int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K);
 
 /*
  * mxfp8_wgrad_grouped_ws -- the same weight gradient, given a caller-owned
@@ -129,14 +130,26 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K);
  *    fixed order through FP32 partial tiles in the workspace: the last of
  *    its pieces to finish (found with a device-scope counter) adds the
  *    others' partials.  No workgroup ever waits for another.
- *  - the scale pre-shuffle (M >= 4096 E or M % 512 != 0): a short first
+ *  - the scale pre-shuffle (M >= 4096 E or ld % 512 != 0): a short first
  *    kernel rewrites sA and sB into the workspace so that the main kernel's
  *    scale loads read consecutive bytes (the blog has a per-call pre-shuffle
  *    too, section 5.6).
  *
  * Arguments: as mxfp8_wgrad_grouped, plus
+ *   ld               the row stride of A and B in bytes (tokens), M <= ld <=
+ *                    MXW_MAX_TOKENS, ld % 32 == 0, or 0 for M; the scale
+ *                    planes' rows are then ld / 32 bytes apart.  A is
+ *                    [N, ld] storage holding the [N, M] matrix in its first M
+ *                    columns (likewise sA, B, sB); columns [M, ld) are never
+ *                    read.  Rows whose stride is a multiple of 64 KiB (the
+ *                    16B shape's M = 3 * 2^16, the 671B shapes' 2^18) put the
+ *                    lines a tile needs at once into few L2 sets; a stride
+ *                    padded by an odd number of 128-token lines
+ *                    (ld = M + 128) avoids that (measured at 671B: 13% fewer
+ *                    HBM reads, 2-3% faster).  mxfp8_quantize_tokens
+ *                    writes such padded rows.
  *   workspace        caller-owned device memory, 256-byte aligned, of at
- *                    least mxfp8_wgrad_workspace_size(E, M, N, K) bytes
+ *                    least mxfp8_wgrad_workspace_size(E, M, ld, N, K) bytes
  *                    (may be NULL when that size is 0).  Its contents are
  *                    undefined on entry and on exit: the call's first kernel
  *                    initialises what the others read.
@@ -160,7 +173,7 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K);
  * missing, short or misaligned workspace).
  */
 int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                           const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* workspace,
+                           const int32_t* offs, int E, int M, int ld, int N, int K, uint16_t* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
 /*
@@ -170,9 +183,9 @@ int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B
  * static device array of MXW_SCRATCH_BYTES (160 MiB) inside the library, which
  * every device the library runs on holds until the process ends.
  *
- * Arguments and results: as mxfp8_wgrad_grouped_ws without the workspace
- * arguments; the same plan, kernels and bits.  The caller still passes the
- * operands and out.  A shape whose workspace size
+ * Arguments and results: as mxfp8_wgrad_grouped_ws (row stride ld included)
+ * without the workspace arguments; the same plan, kernels and bits.  The
+ * caller still passes the operands and out.  A shape whose workspace size
  * (mxfp8_wgrad_workspace_size) exceeds MXW_SCRATCH_BYTES returns
  * MXW_ERR_SCRATCH and launches nothing (the 16B shape with 196,608 tokens
  * needs 149 MiB, 671B gate/up with 262,144 tokens 88 MiB).  It calls no
@@ -185,7 +198,8 @@ int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B
  * keeps the last call's contents.
  */
 int mxfp8_wgrad_grouped_noalloc(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                                const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream);
+                                const int32_t* offs, int E, int M, int ld, int N, int K, uint16_t* out,
+                                void* stream);
 
 /*
  * bf16_wgrad_grouped -- the same weight gradient on plain bfloat16 operands:
@@ -347,20 +361,26 @@ int64_t mxw_fwd_grid_size(int E, int R, int N);
  *   offs  int32  [E]       cumulative expert ends (may be NULL: all tokens).
  *   E     1 <= E <= MXW_MAX_EXPERTS when offs is not NULL.
  *   M     0 <= M <= MXW_MAX_TOKENS, M % 32 == 0.
+ *   ld    row stride of q in bytes (tokens), M <= ld <= MXW_MAX_TOKENS,
+ *         ld % 32 == 0, or 0 for M; s's rows are ld / 32 bytes apart.  A
+ *         padded stride (ld = M + 128) is the layout mxfp8_wgrad_grouped_ws
+ *         reads best (see there); columns [M, ld) of q and [M/32, ld/32) of
+ *         s are not written.
  *   H     16 <= H <= 65536, H % 16 == 0.
- *   q     uint8  [H, M]    codes, row stride M bytes.
- *   s     uint8  [H, M/32] scales, row stride M/32 bytes.
+ *   q     uint8  [H, ld]   codes (the first M bytes of each row).
+ *   s     uint8  [H, ld/32] scales (the first M/32 bytes of each row).
  *   stream  a hipStream_t, passed as void*.
  *
  * Host-checked preconditions return an error code and launch nothing:
  * non-NULL x, q, s; x and q 16-byte aligned; the ranges above; a gfx950
- * device.  Effects: one kernel on `stream`; allocates nothing; q and s are
- * fully overwritten; the result depends only on x and `used`.
+ * device.  Effects: one kernel on `stream`; allocates nothing; the [H, M]
+ * codes and [H, M/32] scales are fully overwritten; the result depends only
+ * on x and `used`.
  *
  * Returns MXW_OK or a negative MXW_ERR_* code.
  */
-int mxfp8_quantize_tokens(const uint16_t* x, const int32_t* offs, int E, int M, int H, uint8_t* q, uint8_t* s,
-                          void* stream);
+int mxfp8_quantize_tokens(const uint16_t* x, const int32_t* offs, int E, int M, int ld, int H, uint8_t* q,
+                          uint8_t* s, void* stream);
 
 /* mxw_strerror -- a static, human-readable message for a return code. */
 const char* mxw_strerror(int code);

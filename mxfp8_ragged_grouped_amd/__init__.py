@@ -71,11 +71,11 @@ def _load():
     lib.mxfp8_wgrad_grouped.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
     S = ctypes.c_size_t
     lib.mxfp8_wgrad_grouped_ws.restype = I
-    lib.mxfp8_wgrad_grouped_ws.argtypes = [P, P, P, P, P, I, I, I, I, P, P, S, P]
+    lib.mxfp8_wgrad_grouped_ws.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, S, P]
     lib.mxfp8_wgrad_grouped_noalloc.restype = I
-    lib.mxfp8_wgrad_grouped_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
+    lib.mxfp8_wgrad_grouped_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P]
     lib.mxfp8_wgrad_workspace_size.restype = ctypes.c_int64
-    lib.mxfp8_wgrad_workspace_size.argtypes = [I, I, I, I]
+    lib.mxfp8_wgrad_workspace_size.argtypes = [I, I, I, I, I]
     lib.bf16_wgrad_grouped.restype = I
     lib.bf16_wgrad_grouped.argtypes = [P, P, P, I, I, I, I, P, P]
     lib.bf16_wgrad_grouped_ws.restype = I
@@ -97,7 +97,7 @@ def _load():
     lib.mxw_fwd_grid_size.restype = ctypes.c_int64
     lib.mxw_fwd_grid_size.argtypes = [I, I, I]
     lib.mxfp8_quantize_tokens.restype = I
-    lib.mxfp8_quantize_tokens.argtypes = [P, P, I, I, I, P, P, P]
+    lib.mxfp8_quantize_tokens.argtypes = [P, P, I, I, I, I, P, P, P]
     _lib = lib
     return lib
 
@@ -138,24 +138,27 @@ def mxfp8_wgrad_grouped(A, sA, B, sB, offs, E, M, N, K, out, stream=0):
     return lib.mxfp8_wgrad_grouped(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, stream)
 
 
-def mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, E, M, N, K, out, workspace, workspace_bytes, stream=0):
-    """Raw C-ABI call on device addresses (ints).  Returns the status code."""
+def mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, E, M, N, K, out, workspace, workspace_bytes, stream=0, ld=0):
+    """Raw C-ABI call on device addresses (ints); ld = row stride (0: M).
+    Returns the status code."""
     lib = _load()
-    return lib.mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, workspace,
+    return lib.mxfp8_wgrad_grouped_ws(A, sA, B, sB, offs, int(E), int(M), int(ld), int(N), int(K), out, workspace,
                                       int(workspace_bytes), stream)
 
 
-def mxfp8_wgrad_grouped_noalloc(A, sA, B, sB, offs, E, M, N, K, out, stream=0):
+def mxfp8_wgrad_grouped_noalloc(A, sA, B, sB, offs, E, M, N, K, out, stream=0, ld=0):
     """Raw C-ABI call on device addresses (ints): the workspace entry on the
-    library's static scratch (no allocation).  Returns the status code."""
+    library's static scratch (no allocation); ld = row stride (0: M).
+    Returns the status code."""
     lib = _load()
-    return lib.mxfp8_wgrad_grouped_noalloc(A, sA, B, sB, offs, int(E), int(M), int(N), int(K), out, stream)
+    return lib.mxfp8_wgrad_grouped_noalloc(A, sA, B, sB, offs, int(E), int(M), int(ld), int(N), int(K), out, stream)
 
 
-def workspace_size(E, M, N, K):
-    """Bytes of workspace mxfp8_wgrad_grouped_ws needs for this shape on the
-    current device (0: none).  Raises MxwError on a status code."""
-    rc = _load().mxfp8_wgrad_workspace_size(int(E), int(M), int(N), int(K))
+def workspace_size(E, M, N, K, ld=0):
+    """Bytes of workspace mxfp8_wgrad_grouped_ws needs for this shape (row
+    stride ld, 0 = M) on the current device (0: none).  Raises MxwError on a
+    status code."""
+    rc = _load().mxfp8_wgrad_workspace_size(int(E), int(M), int(ld), int(N), int(K))
     if rc < 0:
         raise MxwError("mxfp8_wgrad_workspace_size failed: %s" % strerror(rc))
     return int(rc)
@@ -194,11 +197,20 @@ def _as_u8(t, name):
     raise TypeError("%s must be uint8 (or float8_e4m3fn for data), got %s" % (name, t.dtype))
 
 
+def _row_stride(t, name):
+    if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise ValueError("%s must be a 2-D tensor with unit column stride and rows at least a row apart" % name)
+    return t.stride(0)
+
+
 def wgrad(A, sA, B, sB, offs, out=None, stream=None, workspace=None, plain=False):
     """dW [E, N, K] bf16 from MXFP8 operands (see module docstring).
 
     A: [N, M] uint8/float8_e4m3fn, sA: [N, M/32] uint8, B: [K, M], sB: [K, M/32],
-    offs: [E] int32 cumulative expert ends, all on one CUDA(HIP) device and
+    offs: [E] int32 cumulative expert ends, all on one CUDA(HIP) device.  A and
+    B may be row-strided views ([:, :M] of [rows, ld] buffers, the same ld for
+    both, and sA, sB then with row stride ld / 32): the workspace entry reads
+    that layout (see mxfp8_wgrad_grouped_ws); the other tensors are
     contiguous.  `out` (optional) is a contiguous bf16 [E, N, K] tensor that is
     fully overwritten.  Runs on `stream` (default: the current stream) and does
     not synchronise.  plain=True calls mxfp8_wgrad_grouped (no workspace);
@@ -224,8 +236,18 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None, workspace=None, plain=False
     for name, t in (("A", A), ("sA", sA), ("B", B), ("sB", sB), ("offs", offs)):
         if t.device != dev or dev.type != "cuda":
             raise ValueError("%s must be on the same GPU as A" % name)
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+    if not offs.is_contiguous():
+        raise ValueError("offs must be contiguous")
+    ld = _row_stride(A, "A")
+    if N <= 1:
+        ld = M  # a single row: any stride is M's
+    if _row_stride(B, "B") != ld and K > 1 or (ld % 32):
+        raise ValueError("A and B must share one row stride, a multiple of 32 (got %d, %d)" % (ld, B.stride(0)))
+    for name, t, rows in (("sA", sA, N), ("sB", sB, K)):
+        if rows > 1 and _row_stride(t, name) != ld // 32:
+            raise ValueError("%s rows must be ld / 32 = %d bytes apart" % (name, ld // 32))
+    if plain and ld != M:
+        raise ValueError("the entry point without a workspace takes contiguous operands (row stride M)")
     if out is None:
         out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (E, N, K) or not out.is_contiguous() or out.device != dev:
@@ -237,9 +259,9 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None, workspace=None, plain=False
             rc = mxfp8_wgrad_grouped(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
                                      E, M, N, K, out.data_ptr(), stream.cuda_stream)
         else:
-            wp, wb, ws = _workspace(workspace_size(E, M, N, K), dev, stream, workspace)
+            wp, wb, ws = _workspace(workspace_size(E, M, N, K, ld), dev, stream, workspace)
             rc = mxfp8_wgrad_grouped_ws(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
-                                        E, M, N, K, out.data_ptr(), wp, wb, stream.cuda_stream)
+                                        E, M, N, K, out.data_ptr(), wp, wb, stream.cuda_stream, ld=ld)
             del ws
     if rc != 0:
         raise MxwError("mxfp8_wgrad_grouped%s failed (%d): %s" % ("" if plain else "_ws", rc, strerror(rc)))
@@ -359,16 +381,21 @@ def fwd(A, sA, B, sB, offs, out=None, stream=None):
     return out
 
 
-def mxfp8_quantize_tokens(x, offs, E, M, H, q, s, stream=0):
-    """Raw C-ABI call on device addresses (ints; offs may be 0).  Returns the status code."""
-    return _load().mxfp8_quantize_tokens(x, offs, int(E), int(M), int(H), q, s, stream)
+def mxfp8_quantize_tokens(x, offs, E, M, H, q, s, stream=0, ld=0):
+    """Raw C-ABI call on device addresses (ints; offs may be 0; ld = row stride
+    of q, 0 for M).  Returns the status code."""
+    return _load().mxfp8_quantize_tokens(x, offs, int(E), int(M), int(ld), int(H), q, s, stream)
 
 
-def quantize_tokens(x, offs=None, q=None, s=None, stream=None):
+def quantize_tokens(x, offs=None, q=None, s=None, stream=None, ld=None):
     """Token-axis MXFP8 quantisation of bf16 x [M, H] -> (codes uint8 [H, M],
     scales uint8 [H, M/32]), the weight gradient's operand layout.  Tokens at
     or past offs[-1] (all tokens are used when offs is None) become code 0.
-    Runs on `stream` (default: the current stream) and does not synchronise."""
+    With ld (a multiple of 32, >= M) the codes and scales are written into
+    [H, ld] and [H, ld/32] buffers and returned as their [:, :M] and
+    [:, :M/32] views (the padded rows mxfp8_wgrad_grouped_ws reads best);
+    the padding columns are not written.  Runs on `stream` (default: the
+    current stream) and does not synchronise."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or x.device.type != "cuda":
         raise ValueError("x must be a contiguous 2-D bf16 tensor on the GPU")
     M, H = x.shape
@@ -376,20 +403,24 @@ def quantize_tokens(x, offs=None, q=None, s=None, stream=None):
     if offs is not None:
         if offs.dtype != torch.int32 or offs.dim() != 1 or offs.device != dev or not offs.is_contiguous():
             raise ValueError("offs must be a contiguous int32 vector on the same GPU")
+    ld = M if ld is None else int(ld)
+    if ld < M or ld % 32:
+        raise ValueError("ld must be a multiple of 32 and at least M")
     if q is None:
-        q = torch.empty((H, M), dtype=torch.uint8, device=dev)
+        q = torch.empty((H, ld), dtype=torch.uint8, device=dev)[:, :M]
     if s is None:
-        s = torch.empty((H, M // 32), dtype=torch.uint8, device=dev)
-    if tuple(q.shape) != (H, M) or q.dtype != torch.uint8 or not q.is_contiguous() or q.device != dev:
-        raise ValueError("q must be a contiguous uint8 [H, M] tensor on the same GPU")
-    if tuple(s.shape) != (H, M // 32) or s.dtype != torch.uint8 or not s.is_contiguous() or s.device != dev:
-        raise ValueError("s must be a contiguous uint8 [H, M/32] tensor on the same GPU")
+        s = torch.empty((H, ld // 32), dtype=torch.uint8, device=dev)[:, :M // 32]
+    if tuple(q.shape) != (H, M) or q.dtype != torch.uint8 or q.device != dev or q.stride() != (ld, 1):
+        raise ValueError("q must be a uint8 [H, M] tensor with row stride ld on the same GPU")
+    if tuple(s.shape) != (H, M // 32) or s.dtype != torch.uint8 or s.device != dev or (
+            H > 1 and s.stride(0) != ld // 32) or (M >= 64 and s.stride(1) != 1):
+        raise ValueError("s must be a uint8 [H, M/32] tensor with row stride ld / 32 on the same GPU")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         rc = mxfp8_quantize_tokens(x.data_ptr(), 0 if offs is None else offs.data_ptr(),
                                    1 if offs is None else offs.shape[0], M, H, q.data_ptr(), s.data_ptr(),
-                                   stream.cuda_stream)
+                                   stream.cuda_stream, ld=ld)
     if rc != 0:
         raise MxwError("mxfp8_quantize_tokens failed (%d): %s" % (rc, strerror(rc)))
     return q, s

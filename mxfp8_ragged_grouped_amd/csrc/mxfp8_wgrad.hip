@@ -315,6 +315,9 @@ struct Params {
   // weight gradient: A [N, M], B [K, M], out [E, N, K] (contraction M);
   // row-ragged GEMM: A [R, M], B [E, N, M], out [R, N] (contraction M, K unused)
   int E, M, N, K;
+  // row stride of A and B in bytes (>= M; the scale planes' rows are ld / 32
+  // bytes apart): M unless the caller pads its rows
+  int ld;
   int R;  // row-ragged GEMM: rows of A and out
   // log2 of the bytes per token of A and B: 0 for E4M3 codes, 1 for bf16 (M,
   // the row stride and every window are then in bytes: offs are shifted)
@@ -418,7 +421,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   if (COL) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int M = p.M, N = p.N, K = p.K;
+  const int M = p.M, N = p.N, K = p.K, ld = p.ld;
   const int g = pc.g, start = pc.start, end = pc.end, role = pc.role;
   const int col = pc.col, member = pc.member, Q = pc.Q, ra_lin = pc.ra_lin, r_it = pc.r_it;
   // the tile: rows [arow, arow + rowsA) of A, [brow, brow + rowsB) of B, and
@@ -449,9 +452,9 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // in which the 16-byte groups of a band's 256 rows are contiguous (when
   // the host made them: p.sAs != null)
   const bool SHUF = GROUP && !ROWS && !BF && p.sAs != nullptr;
-  const uint32_t sbytes = (uint32_t)M >> 5;  // scale bytes per row
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + arow * M, (uint32_t)rowsA * (uint32_t)M);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + brow * M, (uint32_t)rowsB * (uint32_t)M);
+  const uint32_t sbytes = (uint32_t)ld >> 5;  // scale bytes from one row to the next
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + arow * ld, (uint32_t)rowsA * (uint32_t)ld);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + brow * ld, (uint32_t)rowsB * (uint32_t)ld);
   // scale planes are read as whole dwords; rounding the range up to 4 bytes
   // keeps every dword entirely inside or outside it (bytes past the plane
   // belong to tokens >= M, which are always masked)
@@ -483,7 +486,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   uint32_t vrow[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    vrow[q] = (uint32_t)((wave * 8 + ((q + rot) & 7)) * 8 + lrow) * (uint32_t)M + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
+    vrow[q] = (uint32_t)((wave * 8 + ((q + rot) & 7)) * 8 + lrow) * (uint32_t)ld + (uint32_t)(((q & 1) ? ch_o : ch_e) * 16);
   // Scales: lane l of wave w fetches scale row 64 w + l (shuffled planes: the
   // 16 bytes of that row in each group of 4 KiB)
   const uint32_t srow_off = (uint32_t)(wave * 64 + lane) * (SHUF ? 16u : sbytes);
@@ -810,7 +813,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           const bool ok = 2 * pp < s0 + nsteps && q < 8 && (pp + 1) * kPair <= M;
           // the row group goes into the range-checked (VGPR) offset, the
           // token offset (inside the row) into the scalar one
-          const uint32_t rq = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)q * 8u * (uint32_t)M : kOob);
+          const uint32_t rq = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)q * 8u * (uint32_t)ld : kOob);
           dma4s(k < 2 ? rA : rB, pfdst, vrow[0] + rq, __builtin_amdgcn_readfirstlane(ok ? (uint32_t)(pp * kPair) : 0u));
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
@@ -1289,6 +1292,7 @@ struct ShufArgs {
   int R[2];             // rows of A, B
   int bands[2];         // ceil(R / 256)
   int M, groups, octets;
+  int sstride;  // bytes from one scale row to the next (ld / 32)
   const int32_t* offs;
   int E;
   // column mode's arrival counters, cleared here for the main kernel that
@@ -1304,7 +1308,7 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
   const int op = blk >= a.bands[0] * a.octets;
   if (op) blk -= a.bands[0] * a.octets;
   const int b = blk / a.octets, o = blk - b * a.octets;
-  const uint32_t sb = (uint32_t)a.M >> 5;  // bytes per row
+  const uint32_t sb = (uint32_t)a.sstride;  // bytes from one row to the next
   const int R = a.R[op];
   // tokens past the largest clamped offs belong to no expert's window
   // (offs[E-1] when offs is well formed)
@@ -1322,7 +1326,7 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
       make_rsrc(a.s[op] + (size_t)b * kTile * sb, ((uint32_t)rows * sb + 3u) & ~3u);
   auto keep_bytes = [](uint32_t x, int keep) { return keep >= 4 ? x : (keep <= 0 ? 0u : x & ((1u << (8 * keep)) - 1u)); };
   if ((sb & 15u) == 0) {
-    // 16-byte aligned rows (M % 512 == 0): one load per chunk, all eight in
+    // 16-byte aligned rows (ld % 512 == 0): one load per chunk, all eight in
     // flight before any store (the compiler cannot tell the buffer loads from
     // the global stores, so a load-store loop would wait out each load)
     v4i v[8];
@@ -1383,7 +1387,7 @@ union QSmem {
 };
 
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
-                                                    int E, int M, int H, uint8_t* __restrict__ q,
+                                                    int E, int M, int ld, int H, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) QSmem sm;
   const int tid = threadIdx.x;
@@ -1442,7 +1446,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     const int sw = (h >> 1) & 7;
     *(v4i*)&sm.q[h][((2 * b) ^ sw) * 16] = (v4i){(int)wq[0], (int)wq[1], (int)wq[2], (int)wq[3]};
     *(v4i*)&sm.q[h][((2 * b + 1) ^ sw) * 16] = (v4i){(int)wq[4], (int)wq[5], (int)wq[6], (int)wq[7]};
-    if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(M >> 5) + (m0 >> 5) + b] = (uint8_t)sb;
+    if (h0 + h < H && m0 + 32 * b < M) s[(size_t)(h0 + h) * (size_t)(ld >> 5) + (m0 >> 5) + b] = (uint8_t)sb;
   }
   __syncthreads();
   // ---- store: chunk c = 256 k + tid is hidden row c / 8, tokens 16 (c % 8) .. +15
@@ -1450,7 +1454,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
   for (int k = 0; k < 2; ++k) {
     const int c = k * 256 + tid, r = c >> 3, c8 = c & 7;
     const int h = h0 + r, m = m0 + c8 * 16;
-    if (h < H && m < M) *(v4i*)(q + (size_t)h * M + m) = *(const v4i*)&sm.q[r][(c8 ^ ((r >> 1) & 7)) * 16];
+    if (h < H && m < M) *(v4i*)(q + (size_t)h * ld + m) = *(const v4i*)&sm.q[r][(c8 ^ ((r >> 1) & 7)) * 16];
   }
 }
 
@@ -1480,8 +1484,8 @@ int check_device(int* cus = nullptr) {
 }
 
 // whether an E4M3 weight-gradient call with a workspace pre-shuffles its
-// scales for (E, M)
-bool uses_scale_shuffle(int E, int M) { return (M & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
+// scales for (E, M) and row stride ld
+bool uses_scale_shuffle(int E, int M, int ld) { return (ld & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
 
 // Columns of a column-mode launch (0: one workgroup per work item) and the
 // regions per expert.  Column mode when the work items fill the chip only a
@@ -1521,7 +1525,7 @@ struct Plan {
   size_t flags_off, part_off, scaleA_off, scaleB_off, bytes;
 };
 
-Plan make_plan(int E, int Mb, int tshift, int N, int K, int cus, bool ws) {
+Plan make_plan(int E, int Mb, int ldb, int tshift, int N, int K, int cus, bool ws) {
   Plan pl = {};
   const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
   if (!ws) {
@@ -1531,7 +1535,7 @@ Plan make_plan(int E, int Mb, int tshift, int N, int K, int cus, bool ws) {
     return pl;
   }
   pl.ncol = plan_columns(E, Mb, N, K, cus, &pl.regions);
-  pl.shuffle = tshift == 0 && uses_scale_shuffle(E, Mb);
+  pl.shuffle = tshift == 0 && uses_scale_shuffle(E, Mb, ldb);
   size_t off = 0;
   if (pl.ncol) {
     pl.flags_off = off;
@@ -1552,27 +1556,28 @@ Plan make_plan(int E, int Mb, int tshift, int N, int K, int cus, bool ws) {
 
 // Bytes of workspace a _ws call of this shape needs on the current device
 // (0: none), or a negative MXW_ERR_* code.
-int64_t wgrad_ws_bytes(int E, int Mb, int tshift, int N, int K) {
+int64_t wgrad_ws_bytes(int E, int Mb, int ldb, int tshift, int N, int K) {
   int cus = 0;
   const int rc = check_device(&cus);
   if (rc) return rc;
-  return (int64_t)make_plan(E, Mb, tshift, N, K, cus, true).bytes;
+  return (int64_t)make_plan(E, Mb, ldb, tshift, N, K, cus, true).bytes;
 }
 
 // One weight-gradient launch (E4M3 operands with scales when tshift = 0,
-// bf16 operands when tshift = 1).  Mb: bytes per row of A and B.  use_ws:
+// bf16 operands when tshift = 1).  Mb: bytes of the token axis of A and B,
+// ldb: bytes from one of their rows to the next (>= Mb).  use_ws:
 // the _ws plan on workspace ws of ws_bytes bytes; otherwise the plain plan,
 // which touches no memory but the operands and out.  Sizes and operand
 // pointers are validated by the caller.
 int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const int32_t* offs,
-                 int E, int Mb, int tshift, int N, int K, uint16_t* out, bool use_ws, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 int E, int Mb, int ldb, int tshift, int N, int K, uint16_t* out, bool use_ws, void* ws,
+                 size_t ws_bytes, void* stream) {
   const int64_t grid = (int64_t)E * ((N + kTile - 1) / kTile) * ((K + kTile - 1) / kTile);
   if (grid <= 0 || grid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
   int cus = 0;
   int rc = check_device(&cus);
   if (rc) return rc;
-  const Plan pl = make_plan(E, Mb, tshift, N, K, cus, use_ws);
+  const Plan pl = make_plan(E, Mb, ldb, tshift, N, K, cus, use_ws);
   if (use_ws && pl.bytes) {
     if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MXW_ERR_WORKSPACE;
   }
@@ -1586,6 +1591,7 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   p.out = out;
   p.E = E;
   p.M = Mb;
+  p.ld = ldb;
   p.N = N;
   p.K = K;
   p.tshift = tshift;
@@ -1630,17 +1636,17 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     }
   } else if (!pl.shuffle) {
     // the caller's scale planes: 16-byte groups of 8 K-steps when scale rows
-    // are 16-byte aligned (M % 512 == 0), else the two aligned dwords around
+    // are 16-byte aligned (ld % 512 == 0), else the two aligned dwords around
     // each row's 2 K-steps.  (Column mode always shuffles: it needs
     // M >= 8192 E.)
     p.sAs = p.sBs = nullptr;
     p.sgroups = 0;
     if (pl.ncol) return MXW_ERR_DIM;  // unreachable by construction of the plan
-    if ((Mb & 511) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
+    if ((ldb & 511) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
     else hipLaunchKernelGGL((wgrad_kernel<false, false>), g, blk, 0, st, p);
   } else {
     // long experts (M >= 4096 E) or scale rows not 16-byte aligned
-    // (M % 512 != 0): rewrite the scale planes into the workspace so that the
+    // (ld % 512 != 0): rewrite the scale planes into the workspace so that the
     // K-loop's grouped scale loads read consecutive bytes (the same kernel
     // clears column mode's counters); at short experts the extra pass costs
     // more than the scattered scale loads do (~4 us against ~1 us at 1,024
@@ -1653,6 +1659,7 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     sa.bands[0] = p.tilesN;
     sa.bands[1] = p.tilesK;
     sa.M = Mb;
+    sa.sstride = ldb >> 5;
     sa.groups = pl.sgroups;
     sa.octets = (sa.groups + 7) / 8;
     sa.offs = offs;
@@ -1697,13 +1704,14 @@ int scratch_address(void** out) {
 }
 
 int check_wgrad_args(const void* A, const void* sA, const void* B, const void* sB, const void* offs, const void* out,
-                     int E, int M, int N, int K, bool bf) {
+                     int E, int M, int N, int K, bool bf, int ld = -1) {
   if (!A || (!bf && !sA) || !B || (!bf && !sB) || !offs || !out) return MXW_ERR_NULL;
   const int mmax = bf ? MXW_MAX_TOKENS / 2 : MXW_MAX_TOKENS;
   const int mal = bf ? 15 : 31;
   if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > mmax || (M & mal) || N < 16 || K < 16 || (N & 15) ||
       (K & 15) || N > 65536 || K > 65536)
     return MXW_ERR_DIM;
+  if (ld >= 0 && (ld < M || ld > MXW_MAX_TOKENS || (ld & 31))) return MXW_ERR_DIM;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
   return MXW_OK;
 }
@@ -1723,7 +1731,7 @@ int mxw_columns(int E, int M, int N, int K) {
 
 int mxw_scale_shuffle(int E, int M) {
   if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || (M & 31)) return MXW_ERR_DIM;
-  return uses_scale_shuffle(E, M) ? 1 : 0;
+  return uses_scale_shuffle(E, M, M) ? 1 : 0;
 }
 
 int64_t mxw_grid_size(int E, int N, int K) {
@@ -1735,36 +1743,39 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
                         const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream) {
   const int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
   if (rc) return rc;
-  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, false, nullptr, 0, stream);
+  return launch_wgrad(A, sA, B, sB, offs, E, M, M, 0, N, K, out, false, nullptr, 0, stream);
 }
 
-int64_t mxfp8_wgrad_workspace_size(int E, int M, int N, int K) {
+int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K) {
+  if (ld == 0) ld = M;
   if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS || (M & 31) || N < 16 || K < 16 || (N & 15) ||
-      (K & 15) || N > 65536 || K > 65536)
+      (K & 15) || N > 65536 || K > 65536 || ld < M || ld > MXW_MAX_TOKENS || (ld & 31))
     return MXW_ERR_DIM;
-  return wgrad_ws_bytes(E, M, 0, N, K);
+  return wgrad_ws_bytes(E, M, ld, 0, N, K);
 }
 
 int mxfp8_wgrad_grouped_ws(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                           const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* workspace,
+                           const int32_t* offs, int E, int M, int ld, int N, int K, uint16_t* out, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  const int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
+  if (ld == 0) ld = M;
+  const int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false, ld);
   if (rc) return rc;
-  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, true, workspace, workspace_bytes, stream);
+  return launch_wgrad(A, sA, B, sB, offs, E, M, ld, 0, N, K, out, true, workspace, workspace_bytes, stream);
 }
 
 int mxfp8_wgrad_grouped_noalloc(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                                const int32_t* offs, int E, int M, int N, int K, uint16_t* out, void* stream) {
-  int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false);
+                                const int32_t* offs, int E, int M, int ld, int N, int K, uint16_t* out, void* stream) {
+  if (ld == 0) ld = M;
+  int rc = check_wgrad_args(A, sA, B, sB, offs, out, E, M, N, K, false, ld);
   if (rc) return rc;
   int cus = 0;
   rc = check_device(&cus);
   if (rc) return rc;
-  if (make_plan(E, M, 0, N, K, cus, true).bytes > (size_t)MXW_SCRATCH_BYTES) return MXW_ERR_SCRATCH;
+  if (make_plan(E, M, ld, 0, N, K, cus, true).bytes > (size_t)MXW_SCRATCH_BYTES) return MXW_ERR_SCRATCH;
   void* ws = nullptr;
   rc = scratch_address(&ws);
   if (rc) return rc;
-  return launch_wgrad(A, sA, B, sB, offs, E, M, 0, N, K, out, true, ws, MXW_SCRATCH_BYTES, stream);
+  return launch_wgrad(A, sA, B, sB, offs, E, M, ld, 0, N, K, out, true, ws, MXW_SCRATCH_BYTES, stream);
 }
 
 int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
@@ -1772,23 +1783,23 @@ int bf16_wgrad_grouped(const uint16_t* A, const uint16_t* B, const int32_t* offs
   const int rc = check_wgrad_args(A, nullptr, B, nullptr, offs, out, E, M, N, K, true);
   if (rc) return rc;
   // planned and run in bytes along the token axis: 2 M per row
-  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 1, N, K, out, false,
-                      nullptr, 0, stream);
+  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 2 * M, 1, N, K, out,
+                      false, nullptr, 0, stream);
 }
 
 int64_t bf16_wgrad_workspace_size(int E, int M, int N, int K) {
   if (E < 1 || E > MXW_MAX_EXPERTS || M < 0 || M > MXW_MAX_TOKENS / 2 || (M & 15) || N < 16 || K < 16 ||
       (N & 15) || (K & 15) || N > 65536 || K > 65536)
     return MXW_ERR_DIM;
-  return wgrad_ws_bytes(E, 2 * M, 1, N, K);
+  return wgrad_ws_bytes(E, 2 * M, 2 * M, 1, N, K);
 }
 
 int bf16_wgrad_grouped_ws(const uint16_t* A, const uint16_t* B, const int32_t* offs, int E, int M, int N, int K,
                           uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
   const int rc = check_wgrad_args(A, nullptr, B, nullptr, offs, out, E, M, N, K, true);
   if (rc) return rc;
-  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 1, N, K, out, true,
-                      workspace, workspace_bytes, stream);
+  return launch_wgrad((const uint8_t*)A, nullptr, (const uint8_t*)B, nullptr, offs, E, 2 * M, 2 * M, 1, N, K, out,
+                      true, workspace, workspace_bytes, stream);
 }
 
 int64_t mxw_fwd_grid_size(int E, int R, int N) {
@@ -1816,7 +1827,8 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
   p.offs = offs;
   p.out = out;
   p.E = E;
-  p.M = C;  // the contraction length (and row stride of A and B)
+  p.M = C;  // the contraction length
+  p.ld = C;  // and the row stride of A and B
   p.N = N;
   p.K = 0;
   p.R = R;
@@ -1832,18 +1844,19 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
   return MXW_OK;
 }
 
-int mxfp8_quantize_tokens(const uint16_t* x, const int32_t* offs, int E, int M, int H, uint8_t* q, uint8_t* s,
-                          void* stream) {
+int mxfp8_quantize_tokens(const uint16_t* x, const int32_t* offs, int E, int M, int ld, int H, uint8_t* q,
+                          uint8_t* s, void* stream) {
   if (!x || !q || !s) return MXW_ERR_NULL;
+  if (ld == 0) ld = M;
   if (M < 0 || M > MXW_MAX_TOKENS || (M & 31) || H < 16 || (H & 15) || H > 65536 ||
-      (offs && (E < 1 || E > MXW_MAX_EXPERTS)))
+      (offs && (E < 1 || E > MXW_MAX_EXPERTS)) || ld < M || ld > MXW_MAX_TOKENS || (ld & 31))
     return MXW_ERR_DIM;
   if (((uintptr_t)x | (uintptr_t)q) & 15) return MXW_ERR_ALIGN;
   int rc = check_device();
   if (rc) return rc;
   if (M == 0) return MXW_OK;
   const dim3 grid((unsigned)((M + kQTok - 1) / kQTok), (unsigned)((H + kQHid - 1) / kQHid));
-  hipLaunchKernelGGL(quant_kernel, grid, dim3(256), 0, (hipStream_t)stream, x, offs, E, M, H, q, s);
+  hipLaunchKernelGGL(quant_kernel, grid, dim3(256), 0, (hipStream_t)stream, x, offs, E, M, ld, H, q, s);
   if (hipGetLastError() != hipSuccess) return MXW_ERR_LAUNCH;
   return MXW_OK;
 }

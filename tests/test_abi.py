@@ -89,14 +89,28 @@ def test_host_argument_checks(args, code):
 def test_workspace_size_host_checks():
     """Invalid sizes are rejected before any device query; valid ones need the
     device's CU count, so on a host without a gfx950 they report no device."""
-    assert mxw._load().mxfp8_wgrad_workspace_size(0, 512, 128, 256) == -2
-    assert mxw._load().mxfp8_wgrad_workspace_size(4, 500, 128, 256) == -2
-    assert mxw._load().mxfp8_wgrad_workspace_size(4, 512, 120, 256) == -2
-    assert mxw._load().bf16_wgrad_workspace_size(4, 520, 128, 256) == -2
+    lib = mxw._load()
+    assert lib.mxfp8_wgrad_workspace_size(0, 512, 0, 128, 256) == -2
+    assert lib.mxfp8_wgrad_workspace_size(4, 500, 0, 128, 256) == -2
+    assert lib.mxfp8_wgrad_workspace_size(4, 512, 0, 120, 256) == -2
+    assert lib.mxfp8_wgrad_workspace_size(4, 512, 480, 128, 256) == -2   # ld < M
+    assert lib.mxfp8_wgrad_workspace_size(4, 512, 528, 128, 256) == -2   # ld % 32 != 0
+    assert lib.bf16_wgrad_workspace_size(4, 520, 128, 256) == -2
     import torch
     if not torch.cuda.is_available():
-        assert mxw._load().mxfp8_wgrad_workspace_size(8, 196608, 1408, 2048) == -4
+        assert lib.mxfp8_wgrad_workspace_size(8, 196608, 0, 1408, 2048) == -4
+        assert lib.mxfp8_wgrad_workspace_size(8, 196608, 196608 + 128, 1408, 2048) == -4
         assert mxw.mxfp8_wgrad_grouped_ws(P, P, P, P, P, 4, 512, 128, 256, P, 0, 0, 0) == -4
+
+
+@pytest.mark.parametrize("ld,code", [(480, -2), (528, -2), (16 * 1024 * 1024, -2)])
+def test_row_stride_host_checks(ld, code):
+    """A row stride below M, not a multiple of 32, or beyond the token range is
+    rejected on the host by the workspace entries and the quantiser."""
+    args = (P, P, P, P, P, 4, 512, 128, 256, P)
+    assert mxw.mxfp8_wgrad_grouped_ws(*args, P, 1 << 30, 0, ld=ld) == code
+    assert mxw.mxfp8_wgrad_grouped_noalloc(*args, 0, ld=ld) == code
+    assert mxw.mxfp8_quantize_tokens(P, P, 4, 512, 128, P, P, 0, ld=ld) == code
 
 
 @pytest.mark.parametrize("args,code", [

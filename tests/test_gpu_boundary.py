@@ -277,3 +277,82 @@ def test_malformed_offs(entry, case):
             assert (bits[g] == 0).all(), "expert %d with an empty clamped window not +0" % g
         else:
             check_close(bits[g], expert_ref(hops, start, end), what="malformed offs %s expert %d" % (offs_list, g))
+
+
+def strided(cfg, ld, fill=0x7F):
+    """The operands copied into row-strided storage: [rows, ld] buffers (the
+    padding columns hold NaN codes / 0xFF scales) and their [:, :M] views."""
+    c = dict(cfg)
+    M = cfg["M"]
+    for k in ("A", "B"):
+        t = cfg[k]
+        buf = torch.full((t.shape[0], ld), fill, dtype=torch.uint8, device=t.device)
+        buf[:, :M] = t
+        c[k] = buf[:, :M]
+    for k in ("sA", "sB"):
+        t = cfg[k]
+        buf = torch.full((t.shape[0], ld // 32), 0xFF, dtype=torch.uint8, device=t.device)
+        buf[:, :M // 32] = t
+        c[k] = buf[:, :M // 32]
+    return c
+
+
+@pytest.mark.parametrize("E,N,K,M,sizes,pad", [
+    (8, 1408, 2048, 65536, [12000, 4000, 9600, 0, 11200, 8000, 6400, 14336], 128),  # column mode
+    (3, 272, 528, 2048, [160, 0, 1856], 128),        # short experts: direct scales -> pre-shuffle (ld % 512)
+    (3, 272, 528, 2048, [160, 0, 1856], 512),        # ld % 512 == 0: direct 16-byte scale groups
+    (4, 528, 784, 20480, [4000, 1216, 9600, 2560], 4224),  # long experts, one workgroup per tile
+])
+def test_row_stride_bitwise(E, N, K, M, sizes, pad):
+    """The workspace entry (and the no-allocation one) on padded rows
+    (ld = M + pad) gives the bits of the contiguous call: the same schedule
+    and the same scale bytes, whichever scale path the stride selects."""
+    cfg = W.make_random(E, N, K, M, sizes, seed=2000 + pad + M, device=DEV)
+    ld = M + pad
+    say("row stride: E=%d N=%d K=%d M=%d ld=%d" % (E, N, K, M, ld))
+    base = bf16_bits(run_gpu(cfg))
+    sc = strided(cfg, ld)
+    assert sc["A"].stride(0) == ld and sc["sA"].stride(0) == ld // 32
+    np.testing.assert_array_equal(bf16_bits(run_gpu(sc)), base)
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
+    rc = mxw.mxfp8_wgrad_grouped_noalloc(*(sc[k].data_ptr() for k in ("A", "sA", "B", "sB", "offs")), E, M, N, K,
+                                         out.data_ptr(), torch.cuda.current_stream().cuda_stream, ld=ld)
+    assert rc == 0, mxw.strerror(rc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(out), base)
+    with pytest.raises(ValueError):
+        mxw.wgrad(sc["A"], sc["sA"], sc["B"], sc["sB"], sc["offs"], plain=True)
+    check_close(base, oracle.wgrad_f64(*host(cfg)), what="row stride %d" % ld)
+
+
+def test_quantize_padded_rows_end_to_end():
+    """The quantiser writing padded rows (ld = M + 128): the [H, M] codes and
+    scales equal the contiguous ones bit for bit, the padding columns keep
+    their poison, and the weight gradient of the padded operands equals the
+    contiguous one bit for bit."""
+    E, N, K, M = 4, 400, 528, 8192
+    sizes = [2048, 0, 3584, 2368]
+    offs = torch.tensor(np.cumsum(sizes), dtype=torch.int32, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2100)
+    dy = torch.randn((M, N), generator=g, device=DEV).to(torch.bfloat16)
+    x = (0.5 * torch.randn((M, K), generator=g, device=DEV)).to(torch.bfloat16)
+    ld = M + 128
+    say("quantise into padded rows, then the weight gradient")
+    qa, sa = mxw.quantize_tokens(dy, offs)
+    qb, sb = mxw.quantize_tokens(x, offs)
+    pa_q = torch.full((N, ld), 0x5A, dtype=torch.uint8, device=DEV)
+    pa_s = torch.full((N, ld // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    pb_q = torch.full((K, ld), 0x5A, dtype=torch.uint8, device=DEV)
+    pb_s = torch.full((K, ld // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    mxw.quantize_tokens(dy, offs, q=pa_q[:, :M], s=pa_s[:, :M // 32], ld=ld)
+    mxw.quantize_tokens(x, offs, q=pb_q[:, :M], s=pb_s[:, :M // 32], ld=ld)
+    torch.cuda.synchronize()
+    assert torch.equal(pa_q[:, :M], qa) and torch.equal(pa_s[:, :M // 32], sa)
+    assert torch.equal(pb_q[:, :M], qb) and torch.equal(pb_s[:, :M // 32], sb)
+    assert (pa_q[:, M:] == 0x5A).all().item() and (pb_s[:, M // 32:] == 0x5A).all().item()
+    contiguous = bf16_bits(mxw.wgrad(qa, sa, qb, sb, offs))
+    padded = bf16_bits(mxw.wgrad(pa_q[:, :M], pa_s[:, :M // 32], pb_q[:, :M], pb_s[:, :M // 32], offs))
+    np.testing.assert_array_equal(padded, contiguous)
+    ref = oracle.wgrad_f64(qa.cpu().numpy(), sa.cpu().numpy(), qb.cpu().numpy(), sb.cpu().numpy(), offs.cpu().numpy())
+    check_close(contiguous, ref, what="quantised operands")
