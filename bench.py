@@ -53,13 +53,21 @@ same ragged problem in bf16 through torch._grouped_mm (dY^T [N, M] and X
 way in the same process, as the pages' "x BF16" comparison (context, not the
 metric).
 
+The weight-gradient line also carries `padded_rows`: the same call on the same
+values stored with rows M + 128 tokens apart (the layout the quantiser writes
+when given a row stride; --ld-pad N times that layout as the headline).
+
 The weight-gradient lines also carry `power`: socket power, joules per step and
 the mean shader clock over the first sustained pass (amdsmi, read-only), and
 the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
 
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
-    --no-power           skip the power leg
+    --no-power           skip the power sampling
+    --no-sustained / --no-plain / --no-padded / --no-bf16   skip those legs
+    --prerun S           seconds of untimed pre-run (0 for counter runs)
+    --entry plain        time mxfp8_wgrad_grouped (no workspace) as the headline
+    --ld-pad N           store the operands with rows M + N tokens apart
     --copy-calibration   run a plain 1 GiB device copy (counter calibration)
 """
 import argparse
