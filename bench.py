@@ -142,11 +142,33 @@ def cpu_baseline(cfg, A, sA, B, sB, offs, budget_s=25.0):
     stride = next(s for s in (1, 2, 4, 8) if t_probe * (8 // s) ** 2 <= budget_s or s == 8)
     dt, na, nb = run(stride)
     flops = 2.0 * used * na * nb
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "%s: %s of A and of B (%d x %d of %d x %d outputs per expert, all %d routed "
-                      "tokens), fp64, %.1f s" % (cfg["name"], {1: "every row", 2: "every 2nd row", 4: "every 4th row",
-                                                                8: "every 8th row"}[stride], na, nb,
-                                                cfg["N"], cfg["K"], int(used), dt)}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "%s: %s of A and of B (%d x %d of %d x %d outputs per expert, all %d routed "
+                     "tokens), fp64, %.1f s" % (cfg["name"], {1: "every row", 2: "every 2nd row", 4: "every 4th row",
+                                                               8: "every 8th row"}[stride], na, nb,
+                                               cfg["N"], cfg["K"], int(used), dt)}
+    if float(cfg["M"]) / cfg["E"] < 8192:
+        # the small workloads: the same run on one core as well
+        threads = oracle.max_threads()
+        oracle.set_threads(1)
+        try:
+            dt1, na1, nb1 = run(stride)
+        finally:
+            oracle.set_threads(threads)
+        res["single_core"] = {"value": 2.0 * used * na1 * nb1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "seconds": round(dt1, 2)}
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline_rows(cfg, A, sA, B, sB, offs, budget_s=20.0):

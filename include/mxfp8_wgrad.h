@@ -145,9 +145,12 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K);
  *                    16B shape's M = 3 * 2^16, the 671B shapes' 2^18) put the
  *                    lines a tile needs at once into few L2 sets; a stride
  *                    padded by an odd number of 128-token lines
- *                    (ld = M + 128) avoids that (measured at 671B: 13% fewer
- *                    HBM reads, 2-3% faster).  mxfp8_quantize_tokens
- *                    writes such padded rows.
+ *                    (ld = M + 128) avoids that at long experts (16B shape,
+ *                    196,608 tokens: 35% fewer HBM bytes, 3-4% faster;
+ *                    671B: 13% fewer reads, 2-3% faster).  A stride that is
+ *                    not a multiple of 512 needs the scale pre-shuffle,
+ *                    which loses at short experts (~1,000 tokens each).
+ *                    mxfp8_quantize_tokens writes such padded rows.
  *   workspace        caller-owned device memory, 256-byte aligned, of at
  *                    least mxfp8_wgrad_workspace_size(E, M, ld, N, K) bytes
  *                    (may be NULL when that size is 0).  Its contents are

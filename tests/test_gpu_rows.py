@@ -130,3 +130,34 @@ def test_rows_full_size_whole_output(name):
     st = check_close(bits[:used], ref[:used], what=name)
     print("%s whole output max_rel %.3e" % (name, st["max_rel"]))
     assert (bits[used:] == BF16_NAN).all()
+
+
+@pytest.mark.parametrize("offs_list,exact", [
+    ([600, 300, 1000], ((0, 300, 0), (600, 1000, 2))),   # decreasing: windows [0,600), [600,600), [300,1000)
+    ([-5, 700, 5000], ((0, 700, 1), (700, 1200, 2))),     # negative and past R: clamped to [0, R]
+])
+def test_rows_malformed_offs(offs_list, exact):
+    """Malformed offs: the call returns, nothing outside out is written, rows
+    past every clamped window keep their poison, and rows that one expert's
+    clamped window alone covers equal the oracle for that expert."""
+    E, R, C, N = 3, 1200, 256, 272
+    cfg = W.make_rows(E, R, C, N, [400, 400, 400], seed=870, device=DEV)
+    offs = torch.tensor(offs_list, dtype=torch.int32, device=DEV)
+    guard = 4096
+    big = torch.empty(R * N + 2 * guard, dtype=torch.bfloat16, device=DEV)
+    big.view(torch.int16).fill_(BF16_NAN)
+    out = big[guard:guard + R * N].view(R, N)
+    say("rows malformed offs %s" % offs_list)
+    mxw.fwd(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], offs, out=out)
+    torch.cuda.synchronize()
+    gb = bf16_bits(big)
+    assert (gb[:guard] == BF16_NAN).all() and (gb[-guard:] == BF16_NAN).all(), "store outside out"
+    bits = bf16_bits(out)
+    clamp = [min(max(v, 0), R) for v in offs_list]
+    hi = max(clamp)
+    assert (bits[hi:] == BF16_NAN).all(), "a row past every window was written"
+    A, sA, B, sB, _ = host_rows(cfg)
+    for lo, up, g in exact:
+        # expert g alone, as the only expert of a well-formed call over rows [0, up)
+        ref = oracle.rows_f64(A[:up], sA[:up], B[g:g + 1], sB[g:g + 1], np.array([up], np.int32))
+        check_close(bits[lo:up], ref[lo:up], what="rows malformed offs %s rows %d..%d" % (offs_list, lo, up))
