@@ -238,15 +238,16 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None, workspace=None, plain=False
             raise ValueError("%s must be on the same GPU as A" % name)
     if not offs.is_contiguous():
         raise ValueError("offs must be contiguous")
-    ld = _row_stride(A, "A")
-    if N <= 1:
-        ld = M  # a single row: any stride is M's
-    if _row_stride(B, "B") != ld and K > 1 or (ld % 32):
-        raise ValueError("A and B must share one row stride, a multiple of 32 (got %d, %d)" % (ld, B.stride(0)))
-    for name, t, rows in (("sA", sA, N), ("sB", sB, K)):
-        if rows > 1 and _row_stride(t, name) != ld // 32:
-            raise ValueError("%s rows must be ld / 32 = %d bytes apart" % (name, ld // 32))
-    if plain and ld != M:
+    if M == 0:
+        ld = 0  # no tokens: nothing is read, the stride is moot
+    else:
+        ld = _row_stride(A, "A")
+        if _row_stride(B, "B") != ld or (ld % 32):
+            raise ValueError("A and B must share one row stride, a multiple of 32 (got %d, %d)" % (ld, B.stride(0)))
+        for name, t in (("sA", sA), ("sB", sB)):
+            if _row_stride(t, name) != ld // 32:
+                raise ValueError("%s rows must be ld / 32 = %d bytes apart" % (name, ld // 32))
+    if plain and ld not in (0, M):
         raise ValueError("the entry point without a workspace takes contiguous operands (row stride M)")
     if out is None:
         out = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
@@ -254,14 +255,16 @@ def wgrad(A, sA, B, sB, offs, out=None, stream=None, workspace=None, plain=False
         raise ValueError("out must be a contiguous bf16 [E, N, K] tensor on the same device")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    # with no tokens no operand byte is read (every window is empty and the
+    # kernel writes zeros), but torch gives empty tensors NULL addresses
+    ptrs = [t.data_ptr() if M else out.data_ptr() for t in (A, sA, B, sB)]
     with torch.cuda.device(dev):
         if plain:
-            rc = mxfp8_wgrad_grouped(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
-                                     E, M, N, K, out.data_ptr(), stream.cuda_stream)
+            rc = mxfp8_wgrad_grouped(*ptrs, offs.data_ptr(), E, M, N, K, out.data_ptr(), stream.cuda_stream)
         else:
             wp, wb, ws = _workspace(workspace_size(E, M, N, K, ld), dev, stream, workspace)
-            rc = mxfp8_wgrad_grouped_ws(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), offs.data_ptr(),
-                                        E, M, N, K, out.data_ptr(), wp, wb, stream.cuda_stream, ld=ld)
+            rc = mxfp8_wgrad_grouped_ws(*ptrs, offs.data_ptr(), E, M, N, K, out.data_ptr(), wp, wb,
+                                        stream.cuda_stream, ld=ld)
             del ws
     if rc != 0:
         raise MxwError("mxfp8_wgrad_grouped%s failed (%d): %s" % ("" if plain else "_ws", rc, strerror(rc)))
@@ -410,10 +413,10 @@ def quantize_tokens(x, offs=None, q=None, s=None, stream=None, ld=None):
         q = torch.empty((H, ld), dtype=torch.uint8, device=dev)[:, :M]
     if s is None:
         s = torch.empty((H, ld // 32), dtype=torch.uint8, device=dev)[:, :M // 32]
-    if tuple(q.shape) != (H, M) or q.dtype != torch.uint8 or q.device != dev or q.stride() != (ld, 1):
+    if tuple(q.shape) != (H, M) or q.dtype != torch.uint8 or q.device != dev or (M and q.stride() != (ld, 1)):
         raise ValueError("q must be a uint8 [H, M] tensor with row stride ld on the same GPU")
     if tuple(s.shape) != (H, M // 32) or s.dtype != torch.uint8 or s.device != dev or (
-            H > 1 and s.stride(0) != ld // 32) or (M >= 64 and s.stride(1) != 1):
+            M and (s.stride(0) != ld // 32 or s.stride(1) != 1)):
         raise ValueError("s must be a uint8 [H, M/32] tensor with row stride ld / 32 on the same GPU")
     if stream is None:
         stream = torch.cuda.current_stream(dev)

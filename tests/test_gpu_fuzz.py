@@ -33,7 +33,7 @@ def random_sizes(rng, E, total, unit, empty_prob=0.2):
     return s
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_wgrad_random_shapes(seed):
     rng = np.random.default_rng(2000 + seed)
     if seed % 3 == 0:  # column mode: long experts, few tiles
@@ -51,11 +51,20 @@ def test_wgrad_random_shapes(seed):
     used = int(sizes.sum())
     cfg["A"][:, used:] = 0x7F  # NaN codes past the last expert
     cfg["sB"][:, used // 32:] = 0xFF
-    say("wgrad fuzz %d: E=%d N=%d K=%d M=%d used=%d columns=%d" % (seed, E, N, K, M, used,
-                                                                    mxw.columns(E, M, N, K)))
+    plain = bool(seed % 2)
+    # every fourth workspace case reads row-padded operands (ld = M + 32 k)
+    ld = M + 32 * int(rng.integers(1, 9)) if (not plain and seed % 4 == 2) else M
+    say("wgrad fuzz %d: E=%d N=%d K=%d M=%d ld=%d used=%d columns=%d plain=%s" % (
+        seed, E, N, K, M, ld, used, mxw.columns(E, M, N, K), plain))
+    ops = {k: cfg[k] for k in ("A", "sA", "B", "sB")}
+    if ld != M:
+        for k, div in (("A", 1), ("B", 1), ("sA", 32), ("sB", 32)):
+            buf = torch.full((cfg[k].shape[0], ld // div), 0x7F, dtype=torch.uint8, device=DEV)
+            buf[:, :M // div] = cfg[k]
+            ops[k] = buf[:, :M // div]
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
     out.view(torch.int16).fill_(BF16_NAN)
-    mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, plain=bool(seed % 2))
+    mxw.wgrad(ops["A"], ops["sA"], ops["B"], ops["sB"], cfg["offs"], out=out, plain=plain)
     torch.cuda.synchronize()
     bits = bf16_bits(out)
     ref = oracle.wgrad_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))

@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 
+BF16_NAN_I16 = 0x7FC0
 EXACT_CODES = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x3C, 0xBC, 0x40, 0xC0], np.uint8)  # 0, +-.5, +-1, +-1.5, +-2
 
 
@@ -238,6 +239,21 @@ def test_out_fully_overwritten_and_empty_zero(entry):
     bits = bf16_bits(out)
     assert (bits[0] == 0).all() and (bits[2] == 0).all()
     assert np.isfinite(bits[1].astype(np.uint32)).all() and (bits[1] != 0x7FC0).all()
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_no_tokens(entry):
+    """M = 0: every expert is empty and the output is exact +0 (the kernel
+    writes it; no operand byte is read)."""
+    E, N, K = 3, 272, 528
+    e = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=DEV)
+    offs = torch.zeros(E, dtype=torch.int32, device=DEV)
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(BF16_NAN_I16)
+    say("no tokens [%s]" % entry)
+    mxw.wgrad(e(N, 0), e(N, 0), e(K, 0), e(K, 0), offs, out=out, plain=(entry == "plain"))
+    torch.cuda.synchronize()
+    assert (bf16_bits(out) == 0).all()
 
 
 @pytest.mark.parametrize("entry", ENTRIES)
