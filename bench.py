@@ -57,6 +57,10 @@ The weight-gradient line also carries `padded_rows`: the same call on the same
 values stored with rows M + 128 tokens apart (the layout the quantiser writes
 when given a row stride; --ld-pad N times that layout as the headline).
 
+The weight-gradient line also carries `cold_caches`: 30 calls each timed alone
+after a 1 GiB write that evicts the L2s and the Infinity Cache, beside the same
+per-call timing without it (the pages saw no difference between the two).
+
 The weight-gradient lines also carry `power`: socket power, joules per step and
 the mean shader clock over the first sustained pass (amdsmi, read-only), and
 the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
@@ -64,7 +68,7 @@ the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
     --no-power           skip the power sampling
-    --no-sustained / --no-plain / --no-padded / --no-bf16   skip those legs
+    --no-sustained / --no-plain / --no-padded / --no-cold / --no-bf16   skip those legs
     --prerun S           seconds of untimed pre-run (0 for counter runs)
     --entry plain        time mxfp8_wgrad_grouped (no workspace) as the headline
     --ld-pad N           store the operands with rows M + N tokens apart
@@ -592,6 +596,40 @@ def sustained_leg(step, ms_per_step, stream, seconds, passes=2, chunk=8, tflops_
     return out
 
 
+def cold_leg(step, stream, calls=30, flush_bytes=1 << 30):
+    """Cold caches: each call timed alone (HIP events around the call only,
+    on the launch stream) right after a write of flush_bytes, more than the
+    eight XCD L2s (4 MB each) and the 256 MB Infinity Cache hold together, so
+    the call starts with none of its operands cached; beside it the same
+    per-call timing without the flush.  The pages report no difference
+    between cold and warm caches for their kernel."""
+    import torch
+
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device=stream.device)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+
+    def run(flush):
+        with torch.cuda.stream(stream):
+            for i, (a, b) in enumerate(evs):
+                if flush:
+                    buf.fill_(i & 0xFF)
+                a.record(stream)
+                step()
+                b.record(stream)
+        stream.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    run(False)  # warm the code paths once
+    warm, cold = run(False), run(True)
+    del buf
+    return {"calls": calls, "flush_bytes": flush_bytes,
+            "cold_median_ms": round(float(np.median(cold)), 5), "cold_mean_ms": round(float(cold.mean()), 5),
+            "warm_median_ms": round(float(np.median(warm)), 5), "warm_mean_ms": round(float(warm.mean()), 5),
+            "cold_over_warm": round(float(np.median(cold) / np.median(warm)), 4),
+            "what": "each call timed alone between HIP events, after a write of flush_bytes (evicts the L2s and "
+                    "the Infinity Cache) or without it"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -607,6 +645,7 @@ def main():
                     help="seconds of untimed back-to-back steps before the timed ones (0 for counter runs)")
     ap.add_argument("--no-plain", action="store_true", help="skip timing the entry point without a workspace")
     ap.add_argument("--no-padded", action="store_true", help="skip timing the row-padded layout")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache per-call timing")
     ap.add_argument("--ld-pad", type=int, default=0,
                     help="store the operands with rows M + LD_PAD tokens apart (a multiple of 32) for the headline")
     ap.add_argument("--entry", choices=("ws", "plain"), default="ws",
@@ -742,6 +781,8 @@ def main():
                               "tflops": round(ptf, 2), "frac": round(ptf / PEAK_TFLOPS, 4),
                               "what": "the entry point without a workspace (one workgroup per output tile, scales "
                                       "from the caller's planes), same timing method, this process"}
+    if not args.no_cold:
+        res["cold_caches"] = cold_leg(step, stream)
     if not args.no_bf16:
         res["bf16_context"] = bf16_context(cfg, tflops, args, stream)
     if not args.no_cpu:
