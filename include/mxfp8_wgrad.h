@@ -88,7 +88,8 @@ extern "C" {
  *
  * Effects: enqueues one kernel on `stream` and returns without
  * synchronising.  It allocates nothing, keeps no state between calls, takes
- * no lock and never writes its inputs, so it may run concurrently on any
+ * no lock (the first call on a device reads its properties once, under a
+ * host mutex) and never writes its inputs, so it may run concurrently on any
  * number of streams and be captured into a HIP graph at any time, the very
  * first call included.  `out` is completely overwritten; an expert with no
  * tokens gets exact +0.0.

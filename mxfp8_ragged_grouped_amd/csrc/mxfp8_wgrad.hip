@@ -96,6 +96,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "mxfp8_wgrad.h"
@@ -1459,28 +1460,32 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
 }
 
 struct DeviceInfo {
-  int checked;
-  int ok;
-  int cus;  // compute units
+  std::atomic<int> state;  // 0: not read yet, 1: gfx950, 2: another device
+  int cus;                 // compute units (written before state)
 };
 DeviceInfo g_dev[64];
-std::mutex g_dev_mutex;
+std::mutex g_dev_mutex;  // taken only by the first check of a device
 
-// Reads device properties once per device (no allocation, no stream work).
+// Reads device properties once per device (no allocation, no stream work);
+// after that a check is one atomic load, so calls take no lock.
 int check_device(int* cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MXW_ERR_DEVICE;
-  std::lock_guard<std::mutex> lock(g_dev_mutex);
   DeviceInfo& d = g_dev[dev];
-  if (!d.checked) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXW_ERR_DEVICE;
-    d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    d.cus = prop.multiProcessorCount;
-    d.checked = 1;
+  int st = d.state.load(std::memory_order_acquire);
+  if (st == 0) {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    st = d.state.load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXW_ERR_DEVICE;
+      d.cus = prop.multiProcessorCount;
+      st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+      d.state.store(st, std::memory_order_release);
+    }
   }
   if (cus) *cus = d.cus;
-  return d.ok ? MXW_OK : MXW_ERR_DEVICE;
+  return st == 1 ? MXW_OK : MXW_ERR_DEVICE;
 }
 
 // whether an E4M3 weight-gradient call with a workspace pre-shuffles its
