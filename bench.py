@@ -61,6 +61,11 @@ The weight-gradient line also carries `cold_caches`: 30 calls each timed alone
 after a 1 GiB write that evicts the L2s and the Infinity Cache, beside the same
 per-call timing without it (the pages saw no difference between the two).
 
+The weight-gradient line also carries `graph_replay`: the same call captured
+20 times into one HIP graph and replayed back to back, the device-side time
+per call without the host's per-call argument marshalling (what bounds the
+tiny workload).
+
 The weight-gradient lines also carry `power`: socket power, joules per step and
 the mean shader clock over the first sustained pass (amdsmi, read-only), and
 the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
@@ -68,7 +73,7 @@ the clock-normalised roofline fraction TFLOP/s / (peak x clock / 2.4 GHz).
 Extra modes (profiling helpers, same file so profiles run committed code):
     --no-cpu             skip the oracle leg (for profiler runs)
     --no-power           skip the power sampling
-    --no-sustained / --no-plain / --no-padded / --no-cold / --no-bf16   skip those legs
+    --no-sustained / --no-plain / --no-padded / --no-cold / --no-graph / --no-bf16   skip those legs
     --prerun S           seconds of untimed pre-run (0 for counter runs)
     --entry plain        time mxfp8_wgrad_grouped (no workspace) as the headline
     --ld-pad N           store the operands with rows M + N tokens apart
@@ -630,6 +635,47 @@ def cold_leg(step, stream, calls=30, flush_bytes=1 << 30):
                     "the Infinity Cache) or without it"}
 
 
+def graph_leg(make_step, stream, calls=20, seconds=1.0):
+    """The call captured `calls` times into one HIP graph (on a capture
+    stream, with the workspace allocated beforehand: the entry points record
+    only kernel launches) and the graph replayed back to back for about
+    `seconds`: the device-side time per call without the host's per-call
+    argument marshalling, which is what bounds the tiny workload."""
+    import torch
+
+    cap = torch.cuda.Stream(device=stream.device)
+    cap.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        step = make_step(cap)
+        step()  # one eager call on the capture stream first
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(calls):
+                step()
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.time()
+        g.replay()
+        torch.cuda.synchronize()
+        one = max(time.time() - t0, 1e-6)
+        reps = max(2, int(seconds / one))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * calls)
+    del g
+    return {"calls_per_graph": calls, "replays": reps, "ms_per_call": round(ms, 6),
+            "what": "the same call captured %d times into one HIP graph, replayed back to back (HIP events on the "
+                    "launch stream): device-side time per call without the host's per-call overhead" % calls}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -646,6 +692,7 @@ def main():
     ap.add_argument("--no-plain", action="store_true", help="skip timing the entry point without a workspace")
     ap.add_argument("--no-padded", action="store_true", help="skip timing the row-padded layout")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache per-call timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--ld-pad", type=int, default=0,
                     help="store the operands with rows M + LD_PAD tokens apart (a multiple of 32) for the headline")
     ap.add_argument("--entry", choices=("ws", "plain"), default="ws",
@@ -783,6 +830,16 @@ def main():
                                       "from the caller's planes), same timing method, this process"}
     if not args.no_cold:
         res["cold_caches"] = cold_leg(step, stream)
+    if not args.no_graph:
+        def make_step(st):
+            if plain_first:
+                return lambda: mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=st,
+                                         plain=True)
+            return lambda: mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, stream=st,
+                                     workspace=ws)
+        gr = graph_leg(make_step, stream, seconds=1.0 if small else 2.0)
+        gr["tflops"] = round(tflops_of(gr["ms_per_call"]), 2)
+        res["graph_replay"] = gr
     if not args.no_bf16:
         res["bf16_context"] = bf16_context(cfg, tflops, args, stream)
     if not args.no_cpu:
