@@ -14,7 +14,7 @@ import torch
 import mxfp8_ragged_grouped_amd as mxw
 import oracle
 import workloads as W
-from helpers import ENTRIES, bf16_bits, check_close, host, run_gpu
+from helpers import ENTRIES, bf16_bits, bf16_to_f64, check_close, host, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -206,6 +206,42 @@ def test_padding_garbage_ignored(entry):
         cfg[key][:, used // 32:] = 0xFF
     dirty = bf16_bits(run_gpu(cfg, entry=entry))
     np.testing.assert_array_equal(dirty, clean)
+
+
+NAN_CASES = {
+    # E, N, K, M, sizes, NaN code inside, NaN scale inside (B row, block), a second NaN code inside,
+    # garbage just past offs[E-1] (token)
+    "per_tile": (3, 272, 528, 1024, [96, 0, 800], (5, 10), (300, 5), (9, 500), 900),
+    "column": (2, 512, 768, 16416, [8992, 7392], (5, 10), (300, 400), (9, 9500), 16400),
+}
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("case", sorted(NAN_CASES))
+def test_nan_inside_windows(case, entry):
+    """A NaN code (0x7F, 0xFF) or a NaN scale (0xFF) in a live sub-block makes
+    exactly the outputs that contract over it NaN, as the oracle (IEEE fp64)
+    does: the element's row (or column) of its expert, nothing else.  The same
+    values in the 128-token pair just past offs[E-1] (loaded, then masked)
+    change nothing.  NaN positions must match the oracle's exactly; every
+    other element must be finite and within the tolerance.  (The column case
+    also carries NaN through the FP32 partial tiles of a cut region.)"""
+    E, N, K, M, sizes, a_in, sb_in, a_in2, past = NAN_CASES[case]
+    cfg = W.make_random(E, N, K, M, sizes, seed=4242, device=DEV)
+    if case == "column":
+        assert mxw.columns(E, M, N, K) > 0
+    cfg["A"][a_in] = 0x7F
+    cfg["sB"][sb_in] = 0xFF
+    cfg["A"][a_in2] = 0xFF
+    cfg["A"][7, past] = 0x7F
+    cfg["sB"][301, past // 32] = 0xFF
+    say("NaN inside windows [%s, %s]" % (case, entry))
+    bits = bf16_bits(run_gpu(cfg, entry=entry))
+    ref = oracle.wgrad_f64(*host(cfg))
+    gn, rn = np.isnan(bf16_to_f64(bits)), np.isnan(ref)
+    assert rn.sum() == K + N + K - 1  # a row, a column and a row; one element shared
+    np.testing.assert_array_equal(gn, rn)
+    check_close(np.where(rn, 0, bits).astype(np.uint16), np.where(rn, 0.0, ref), what="NaN case %s" % case)
 
 
 @pytest.mark.parametrize("entry", ENTRIES)
