@@ -14,7 +14,7 @@ import torch
 import mxfp8_ragged_grouped_amd as mxw
 import oracle
 import workloads as W
-from helpers import BF16_NAN, bf16_bits, check_close, tile_pairs
+from helpers import BF16_NAN, bf16_bits, bf16_to_f64, check_close, tile_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +99,31 @@ def test_bf16_bitwise_repeat_and_padding_garbage():
     cfg["A"].view(torch.int16)[:, 896:] = 0x7FC0  # NaN past the last expert
     cfg["B"].view(torch.int16)[:, 896:] = 0x7F80  # +inf
     np.testing.assert_array_equal(bf16_bits(run_bf16(cfg)), a)
+
+
+@pytest.mark.parametrize("plain", [False, True])
+def test_bf16_nan_and_inf_inside_windows(plain):
+    """bf16 NaN and -inf values in live tokens: NaN where the oracle (IEEE
+    fp64) has NaN, +-inf where it has +-inf (a row of expert 0, a column and
+    a row of expert 2), the same values just past offs[E-1] change nothing,
+    everything else finite and within tolerance."""
+    cfg = W.make_bf16(3, 272, 528, 1024, [96, 0, 800], seed=2801, device=DEV)
+    a16, b16 = cfg["A"].view(torch.int16), cfg["B"].view(torch.int16)
+    a16[5, 10] = 0x7FC0     # NaN, expert 0
+    b16[300, 200] = -128    # 0xFF80 = -inf, expert 2
+    a16[9, 500] = 0x7FC0    # NaN, expert 2
+    a16[7, 900] = 0x7FC0    # past offs[E-1] = 896
+    b16[301, 950] = 0x7F80  # +inf, past
+    say("bf16 NaN / inf inside windows [plain=%s]" % plain)
+    bits = bf16_bits(run_bf16(cfg, plain=plain))
+    u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.bf16_wgrad_f64(u16(cfg["A"]), u16(cfg["B"]), cfg["offs"].cpu().numpy())
+    got = bf16_to_f64(bits)
+    bad = ~np.isfinite(ref)
+    assert bad.sum() == 528 + 272 + 528 - 1
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+    check_close(np.where(bad, 0, bits).astype(np.uint16), np.where(bad, 0.0, ref), what="bf16 NaN/inf case")
 
 
 def test_bf16_all_experts_empty():

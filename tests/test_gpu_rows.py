@@ -14,7 +14,7 @@ import torch
 import mxfp8_ragged_grouped_amd as mxw
 import oracle
 import workloads as W
-from helpers import BF16_NAN, bf16_bits, check_close
+from helpers import BF16_NAN, bf16_bits, bf16_to_f64, check_close
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +106,30 @@ def test_rows_padding_garbage_ignored():
     cfg["A"][used:] = 0x7F   # NaN codes
     cfg["sA"][used:] = 0xFF  # NaN scales
     np.testing.assert_array_equal(run_rows(cfg), base)
+
+
+def test_rows_nan_inside_windows():
+    """A NaN code in a live row, a NaN scale in a live expert's weight block
+    and a negative-NaN code in another live row give NaN at exactly the
+    oracle's positions (two output rows and one output column of expert 2's
+    rows); the same values in a row past offs[E-1] and in an empty expert's
+    weights change nothing; everything else finite and within tolerance."""
+    cfg = W.make_rows(3, 700, 256, 272, [300, 0, 290], seed=831, device=DEV)
+    used = 590
+    cfg["A"][17, 40] = 0x7F
+    cfg["sB"][2, 100, 3] = 0xFF
+    cfg["A"][450, 200] = 0xFF
+    cfg["A"][600, 5] = 0x7F      # past the last expert's rows
+    cfg["sB"][1, 50, 0] = 0xFF   # expert 1 has no rows
+    say("rows NaN inside windows: launch")
+    bits = run_rows(cfg)
+    ref = oracle.rows_f64(*host_rows(cfg))[:used]
+    got = bf16_to_f64(bits[:used])
+    gn, rn = np.isnan(got), np.isnan(ref)
+    assert rn.sum() == 272 + 290 + 272 - 1
+    np.testing.assert_array_equal(gn, rn)
+    check_close(np.where(rn, 0, bits[:used]).astype(np.uint16), np.where(rn, 0.0, ref), what="rows NaN case")
+    assert (bits[used:] == BF16_NAN).all()
 
 
 def test_rows_all_experts_empty():
