@@ -699,6 +699,23 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     }
   };
 
+  // whole-tile scale blocks (WHOLE): the next pair's two dwords per row and
+  // operand are read one 32-row block per MFMA slot right after the odd
+  // step's barrier (m = 2 .. 5), and joined, shifted and masked one block per
+  // slot (m = 11 .. 14); formed all at once, the 16 LDS reads, their waits and
+  // ~60 vector instructions sat between two MFMAs (+1.3% at C = 1,408).  The
+  // other scale paths keep the placement below, which measured best for them.
+  uint32_t wlo[8], whi[8];  // [operand * 4 + block]
+  uint32_t wpm = 0;
+  auto whole_read = [&](int x, int i) {
+    const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
+    const uint32_t ba = (uint32_t)RA * sbytes + 2u * (uint32_t)x, bb = (uint32_t)RB * sbytes + 2u * (uint32_t)x;
+    wlo[i] = sm.raw[ba >> 2];
+    whi[i] = sm.raw[(ba >> 2) + 1];
+    wlo[4 + i] = sm.raw[kWholeOp + (bb >> 2)];
+    whi[4 + i] = sm.raw[kWholeOp + (bb >> 2) + 1];
+  };
+
   v8i fa[2][4], fb[2][4];
   uint32_t sra[2][4], srb[2][4];  // [pair parity][32-row block]
   uint32_t rawa[4], rawb[4];
@@ -824,6 +841,24 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           asm volatile("" : "+s"(sq));
           read_raw(sq + 1, rawa, rawb);
         }
+        if (WHOLE && (u & 1) && m >= 2 && m < 6) {
+          int sq = s;
+          asm volatile("" : "+s"(sq));
+          whole_read(sq + 1, m - 2);
+        }
+        if (WHOLE && (u & 1) && m >= 11 && m < 15) {
+          // the 4 bytes of steps x, x + 1 sit at the row's own byte
+          // alignment (x is even)
+          int sq = s;
+          asm volatile("" : "+s"(sq));
+          const int i = m - 11, nb = ((u >> 1) + 1) & 1;
+          if (m == 11)
+            wpm = (((live_mask_q(sq + 1, qs, qn) >> msb) & 1u) ? 0xFFu : 0u) |
+                  (((live_mask_q(sq + 2, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
+          const uint32_t RA = (uint32_t)(wn * 128 + 32 * i + fr), RB = (uint32_t)(wk * 128 + 32 * i + fr);
+          sra[nb][i] = (__builtin_amdgcn_alignbit(whi[i], wlo[i], ((RA * sbytes) & 3u) * 8u) >> mshift) & wpm;
+          srb[nb][i] = (__builtin_amdgcn_alignbit(whi[4 + i], wlo[4 + i], ((RB * sbytes) & 3u) * 8u) >> mshift) & wpm;
+        }
         if (!BF && !WHOLE && m == 15) {  // after the step's data loads (vmcnt order)
           if (!GROUP) {
             dma_scales(sgrp, sreal);
@@ -840,7 +875,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           // with the pair, certified by this step's barrier)
           if (!BF && (u & 1)) {
             if (GROUP) finish_sregs(sp + 1, rawa, rawb, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
-            else load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
+            else if (!WHOLE) load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
           }
           if (!(u & 1)) livep = live_mask_pair(((sp + 1) >> 1) + 2, qs, qn);
           sreal = ((sp + 1) % kGroupSteps) == 0;
