@@ -95,7 +95,10 @@ extern "C" {
  * tokens gets exact +0.0.
  *
  * Scheduling and bits: one workgroup per (expert, 256 x 256 output tile)
- * (blog section 4), experts taken longest first (section 5.4), no atomics.
+ * (blog section 4), experts taken longest first (section 5.4), no atomics;
+ * with short experts and a partly filled last round, that round's tiles run
+ * as two half-tile workgroups each (mxw_tail_split), computing every element
+ * exactly as the whole tile does.
  * Each output element is one workgroup's sum over its expert's window in
  * token order, so the result depends only on that expert's window of A, sA,
  * B and sB: it is bitwise reproducible run to run, and unchanged by the
@@ -272,6 +275,22 @@ int64_t mxw_grid_size(int E, int N, int K);
  * no gfx950 device.
  */
 int mxw_columns(int E, int M, int N, int K);
+
+/*
+ * mxw_tail_split -- how many output tiles mxfp8_wgrad_grouped runs as two
+ * half tiles for (E, M, N, K) on the current device (0: none); the same
+ * holds for mxfp8_wgrad_grouped_ws when it runs one workgroup per tile
+ * without the scale pre-shuffle (mxw_columns() == 0, mxw_scale_shuffle() ==
+ * 0).  When the tiles fill the device only a few times over (more than once,
+ * under 4 times) and experts are short (M <= 2048 E), the tiles of the last,
+ * partly filled round (the last in longest-first order) each run as two
+ * workgroups, one for the even and one for the odd 32-row blocks of the
+ * tile's 256 rows of N, so that round has twice as many workgroups of a
+ * little over half the length.  Each output element is computed exactly as
+ * in the whole tile: the bits do not change.  Returns MXW_ERR_DIM or
+ * MXW_ERR_DEVICE on invalid input or no gfx950 device.
+ */
+int mxw_tail_split(int E, int M, int N, int K);
 
 /*
  * mxw_scale_shuffle -- 1 if mxfp8_wgrad_grouped_ws with (E, M) runs the scale

@@ -44,7 +44,7 @@ from .build import LIB as _LIB_PATH
 
 __all__ = ["wgrad", "mxfp8_wgrad_grouped", "mxfp8_wgrad_grouped_ws", "mxfp8_wgrad_grouped_noalloc", "workspace_size", "wgrad_bf16",
            "bf16_wgrad_grouped", "bf16_wgrad_grouped_ws", "bf16_workspace_size", "grid_size", "columns",
-           "scale_shuffle", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size", "quantize_tokens", "mxfp8_quantize_tokens",
+           "scale_shuffle", "tail_split", "fwd", "mxfp8_grouped_fwd", "fwd_grid_size", "quantize_tokens", "mxfp8_quantize_tokens",
            "strerror", "version", "library_path", "MxwError"]
 
 _lib = None
@@ -90,6 +90,8 @@ def _load():
     lib.mxw_version.argtypes = []
     lib.mxw_columns.restype = I
     lib.mxw_columns.argtypes = [I, I, I, I]
+    lib.mxw_tail_split.restype = I
+    lib.mxw_tail_split.argtypes = [I, I, I, I]
     lib.mxw_scale_shuffle.restype = I
     lib.mxw_scale_shuffle.argtypes = [I, I]
     lib.mxfp8_grouped_fwd.restype = I
@@ -120,6 +122,15 @@ def columns(E, M, N, K):
     rc = _load().mxw_columns(int(E), int(M), int(N), int(K))
     if rc < 0:
         raise MxwError("mxw_columns failed: %s" % strerror(rc))
+    return rc
+
+
+def tail_split(E, M, N, K):
+    """Output tiles an MXFP8 weight-gradient call without column mode or
+    pre-shuffle runs as two half tiles (same bits) on the current device."""
+    rc = _load().mxw_tail_split(int(E), int(M), int(N), int(K))
+    if rc < 0:
+        raise MxwError("mxw_tail_split failed: %s" % strerror(rc))
     return rc
 
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"mxfp8_wgrad_grouped", "mxfp8_wgrad_grouped_ws", "mxfp8_wgrad_workspace_size",
                           "bf16_wgrad_grouped", "bf16_wgrad_grouped_ws", "bf16_wgrad_workspace_size",
-                          "mxw_grid_size", "mxw_columns", "mxfp8_grouped_fwd",
+                          "mxw_grid_size", "mxw_columns", "mxw_tail_split", "mxfp8_grouped_fwd",
                           "mxw_fwd_grid_size", "mxfp8_quantize_tokens", "mxw_strerror", "mxw_version"}
     lib = ctypes.CDLL(mxw.library_path())
     for n in names:

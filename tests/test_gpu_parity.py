@@ -181,6 +181,40 @@ def test_exact_regime_bitwise(entry):
     np.testing.assert_array_equal(bits, oracle.to_bf16_bits(ref))
 
 
+# 320 tiles on a 256-CU device at 512 tokens per expert on average: the last
+# 64 tiles of the longest-first dealing run as two half tiles each
+TAIL_SHAPE = (40, 512, 1024, 20480)
+
+
+def _tail_sizes(rng, E, M):
+    sizes = 32 * rng.integers(0, 33, E)  # 0 .. 1,024 tokens, ragged
+    sizes[rng.choice(E, 3, replace=False)] = 0
+    while sizes.sum() > M:
+        sizes[np.argmax(sizes)] -= 32
+    return sizes
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_tail_split_halves(entry):
+    """A launch whose last round of tiles runs as half tiles (each covering
+    the even or the odd 32-row blocks of a tile's 256 rows), with ragged and
+    empty experts: in the exact-arithmetic regime GPU bf16 == RNE(oracle)
+    bit for bit, and on normal values within the tolerance.  The halves
+    compute every element as the whole tile would, so nothing else changes."""
+    E, N, K, M = TAIL_SHAPE
+    assert mxw.tail_split(E, M, N, K) > 0 or torch.cuda.get_device_properties(0).multi_processor_count >= 320
+    rng = np.random.default_rng(91)
+    sizes = _tail_sizes(rng, E, M)
+    A, sA, B, sB, offs = _exact_problem(rng, E, N, K, M, sizes)
+    say("tail split, exact regime [%s]: %d tiles as halves" % (entry, mxw.tail_split(E, M, N, K)))
+    bits = bf16_bits(run_gpu(from_numpy(A, sA, B, sB, offs, sizes), entry=entry))
+    np.testing.assert_array_equal(bits, oracle.to_bf16_bits(oracle.wgrad_f64(A, sA, B, sB, offs)))
+    cfg = W.make_random(E, N, K, M, _tail_sizes(rng, E, M), seed=92, device=DEV)
+    say("tail split, normal values [%s]" % entry)
+    got = bf16_bits(run_gpu(cfg, entry=entry))
+    check_close(got, oracle.wgrad_f64(*host(cfg)), what="tail split [%s]" % entry)
+
+
 @pytest.mark.parametrize("entry", ENTRIES)
 def test_bitwise_repeat(entry):
     cfg = W.make_random(4, 528, 784, 3072, [1056, 0, 992, 960], seed=31, device=DEV)
