@@ -281,7 +281,8 @@ int mxw_columns(int E, int M, int N, int K);
  * half tiles for (E, M, N, K) on the current device (0: none); the same
  * holds for mxfp8_wgrad_grouped_ws when it runs one workgroup per tile
  * without the scale pre-shuffle (mxw_columns() == 0, mxw_scale_shuffle() ==
- * 0).  When the tiles fill the device only a few times over (more than once,
+ * 0), and for the bf16 entries with M tokens when they run one workgroup per
+ * tile (mxw_columns(E, 2 M, N, K) == 0).  When the tiles fill the device only a few times over (more than once,
  * under 4 times) and experts are short (M <= 2048 E), the tiles of the last,
  * partly filled round (the last in longest-first order) each run as two
  * workgroups, one for the even and one for the odd 32-row blocks of the

@@ -448,7 +448,7 @@ struct Piece {
 // (its 256 A rows and 256 B rows are consecutive rows of the planes, so each
 // block is one contiguous range of 256 C / 32 bytes) are DMA'd once, in the
 // prologue, with coalesced dword loads; the K-loop then loads no scales.
-// HALF (weight gradient, one workgroup per tile, E4M3): a half tile.  The
+// HALF (weight gradient, one workgroup per tile): a half tile.  The
 // workgroup computes only the even 32-row A blocks of each wave's quarter, on
 // an A band that starts 32 pc.half rows below the tile's, so the two halves
 // of a tile cover its even and its odd blocks.  Each computed block is the
@@ -458,7 +458,7 @@ struct Piece {
 // the MFMA work and a quarter less staging per K-step.
 template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false, bool HALF = false>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
-  static_assert(!HALF || (!COL && !ROWS && !BF && !WHOLE), "half tiles: E4M3 weight gradient, one workgroup per tile");
+  static_assert(!HALF || (!COL && !ROWS && !WHOLE), "half tiles: weight gradient, one workgroup per tile");
   int tid = threadIdx.x;
   // opaque per piece: nothing derived from the thread index is hoisted out of
   // the column loop (it would stay live through the K-loop)
@@ -833,8 +833,10 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           // first halves into block m, second halves into block (m + 8) % 16:
           // MFMAs on one accumulator stay 16 instructions apart
           const int i2 = i ^ 2;
-          acc[i][t] = mfma_bf16<0>(fb[cur][i], fa[cur][t], acc[i][t]);
-          acc[i2][t] = mfma_bf16<1>(fb[cur][i2], fa[cur][t], acc[i2][t]);
+          if (!(HALF && (t & 1))) {
+            acc[i][t] = mfma_bf16<0>(fb[cur][i], fa[cur][t], acc[i][t]);
+            acc[i2][t] = mfma_bf16<1>(fb[cur][i2], fa[cur][t], acc[i2][t]);
+          }
         } else if (!(HALF && (t & 1))) {
           acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
                                     (int)sra[u >> 1][t]);
@@ -1219,12 +1221,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       if (half <= 0) zero_tile(p, pc.g, pc.tn, pc.tk);
       return;
     }
-    if constexpr (!BF) {
-      if (half >= 0) {
-        pc.half = half;
-        run_piece<GROUP, false, false, false, false, true>(p, sm, pc);
-        return;
-      }
+    if (half >= 0) {
+      pc.half = half;
+      run_piece<GROUP, false, false, BF, false, true>(p, sm, pc);
+      return;
     }
     run_piece<GROUP, false, false, BF>(p, sm, pc);
   } else {
@@ -1573,7 +1573,7 @@ int check_device(int* cus = nullptr) {
 // scales for (E, M) and row stride ld
 bool uses_scale_shuffle(int E, int M, int ld) { return (ld & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
 
-// One workgroup per tile (E4M3, scales read from the caller's planes): how
+// One workgroup per tile (operands and scales read from the caller's buffers): how
 // many of the last tiles of the dealing (the shortest experts', longest
 // first) run as two half tiles.  When the tiles fill the device only a few
 // times over, the last round leaves compute units idle; with short experts
@@ -1725,9 +1725,9 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     p.flags = (uint32_t*)(wsb + pl.flags_off);
     p.part = (float*)(wsb + pl.part_off);
   }
-  // one workgroup per tile on E4M3 operands read from the caller's planes:
-  // the last tiles of the dealing as half tiles (blocks [nfull, grid))
-  const int nsplit = (!pl.ncol && !tshift && !pl.shuffle) ? tail_split(grid, cus, E, Mb) : 0;
+  // one workgroup per tile with operands (and scales) read from the caller's
+  // buffers: the last tiles of the dealing as half tiles (blocks [nfull, grid))
+  const int nsplit = (!pl.ncol && !pl.shuffle) ? tail_split(grid, cus, E, Mb >> tshift) : 0;
   p.nfull = (int)grid - nsplit;
   const dim3 g((unsigned)(pl.ncol ? pl.ncol * kMem : grid + nsplit)), blk(kThreads);
   hipStream_t st = (hipStream_t)stream;
