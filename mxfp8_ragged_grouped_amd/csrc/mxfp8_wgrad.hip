@@ -1048,13 +1048,25 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     // the 16-byte reads of 16 lanes then all hit distinct banks.
     __syncthreads();  // every wave is done with the stages
     uint8_t* ep = &sm.data[0][0][0] + wave * 32768;
+    const int rsub = lane >> 4, cl = lane & 15;
+    const int kk = wk * 128 + cl * 8;  // within the tile
+    // One 32-row block at a time: its 16 8-byte writes, then its rows read
+    // back (8 reads in flight before their stores: one read, wait, store at a
+    // time left the wave waiting on the LDS 32 times) and stored, so the
+    // first stores go out after a quarter of the writes (a wave's LDS
+    // operations run in order; no other wave touches this area).  The stores
+    // are non-temporal: the output is written once and never read here, and
+    // streaming it past the L2 keeps the operand stripes there (row-ragged
+    // GEMM, whose output is the larger part of its traffic: +2.7% to +4.3%;
+    // weight gradient: within +-0.4%; same bits).
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < 4; ++t) {
+      if (HALF && (t & 1)) continue;  // a half tile's odd blocks belong to the other half
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (HALF && (t & 1)) continue;  // a half tile's odd blocks belong to the other half
           v4f v = {acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
           const int nl = 32 * t + fr, c = 4 * i + q;
           uint2 w;
@@ -1062,28 +1074,17 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           w.y = pack_bf16x2(v.z, v.w);
           *(uint2*)(ep + nl * 256 + ((c ^ (nl & 15)) << 4) + ((fq ^ (nl >> 4)) & 1) * 8) = w;
         }
-    const int rsub = lane >> 4, cl = lane & 15;
-    const int kk = wk * 128 + cl * 8;  // within the tile
-    // 8 reads in flight before their stores (one read, wait, store at a time
-    // left the wave waiting on the LDS 32 times).  The stores are
-    // non-temporal: the output is written once and never read here, and
-    // streaming it past the L2 keeps the operand stripes there (row-ragged
-    // GEMM, whose output is the larger part of its traffic: +2.7% to +4.3%;
-    // weight gradient: within +-0.4%; same bits)
-#pragma unroll
-    for (int x0 = 0; x0 < 32; x0 += 8) {
-      if (HALF && (x0 & 8)) continue;  // rows nl of the odd blocks (nl / 32 = x0 / 8)
       v4i d[8];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const int nl = 4 * (x0 + x) + rsub;
+        const int nl = 4 * (8 * t + x) + rsub;
         d[x] = *(const v4i*)(ep + nl * 256 + ((cl ^ (nl & 15)) << 4));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const int nl = 4 * (x0 + x) + rsub;
+        const int nl = 4 * (8 * t + x) + rsub;
         if ((nl >> 4) & 1) d[x] = (v4i){d[x].z, d[x].w, d[x].x, d[x].y};  // a constant after unrolling
         const int n = wn * 128 + nl;
         if (n < rowsA && kk < rowsB) __builtin_nontemporal_store(d[x], (v4i*)(otile + (size_t)n * ldo + kk));
