@@ -112,6 +112,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 256;                   // output tile edge, N and K
+// short tiles: when N % 256 == 128 the last 384 rows of N are cut into two
+// tiles of 192 rows (96 per wave) instead of a whole and a half-empty one
+constexpr int kShort = 192;
 constexpr int kStep = 64;                    // tokens per K-step (two 32-token sub-blocks)
 constexpr int kPair = 2 * kStep;             // tokens per LDS stage (two K-steps)
 constexpr int kThreads = 256;                // 4 wave64
@@ -343,6 +346,9 @@ struct Params {
   int ncol;
   int regions;  // regions of up to kMem tiles per expert
   int hov;      // per-region cost, in K-steps, added to the split's weights
+  // tiles along N of 256 rows; tiles tn >= tall have kShort rows (starting at
+  // 256 tall + 192 (tn - tall)); tall = tilesN when N has no short tiles
+  int tall;
   // one workgroup per tile: blocks [nfull, grid) are half tiles, two per tile
   // of blocks [nfull, nfull + (grid - nfull) / 2) of the plain dealing (the
   // last tiles in longest-first order); nfull = grid for no split
@@ -457,9 +463,12 @@ struct Piece {
 // so the output bits are the whole tile's.  The A row groups of the odd
 // blocks are neither loaded nor read, and their MFMAs are not issued: half
 // the MFMA work and a quarter less staging per K-step.
-template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false, bool HALF = false>
+template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false, bool HALF = false, bool SHORT = false>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
   static_assert(!HALF || (!COL && !ROWS && !WHOLE), "half tiles: weight gradient, one workgroup per tile");
+  static_assert(!SHORT || (!ROWS && !WHOLE && !HALF), "short tiles: weight gradient");
+  // A rows per wave: its 32-row blocks t < (SHORT ? 3 : 4)
+  constexpr int kWaveA = SHORT ? kShort / 2 : kTile / 2;
   int tid = threadIdx.x;
   // opaque per piece: nothing derived from the thread index is hoisted out of
   // the column loop (it would stay live through the K-loop)
@@ -483,9 +492,10 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     ldo = N;
     otile = p.out + arow * N + c0;
   } else {
-    const int n0 = pc.tn * kTile + (HALF ? 32 * pc.half : 0), k0 = pc.tk * kTile;
+    const int n0 = (SHORT ? p.tall * kTile + (pc.tn - p.tall) * kShort : pc.tn * kTile) + (HALF ? 32 * pc.half : 0),
+              k0 = pc.tk * kTile;
     arow = (size_t)n0;
-    rowsA = min(kTile, N - n0);
+    rowsA = min(SHORT ? kShort : kTile, N - n0);
     // a half band may start past N (none of its rows then exist); the
     // clamp is done in a scalar register, which the descriptors need
     if (HALF) rowsA = __builtin_amdgcn_readfirstlane(rowsA < 0 ? 0 : rowsA);
@@ -501,6 +511,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // the host made them: p.sAs != null)
   const bool SHUF = GROUP && !ROWS && !BF && p.sAs != nullptr;
   const uint32_t sbytes = (uint32_t)ld >> 5;  // scale bytes from one row to the next
+  // (a short tile's A rows past its 192 are out of range: loaded as zeros,
+  // never read)
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + arow * ld, (uint32_t)rowsA * (uint32_t)ld);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + brow * ld, (uint32_t)rowsB * (uint32_t)ld);
   // scale planes are read as whole dwords; rounding the range up to 4 bytes
@@ -704,7 +716,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
                         (((live_mask_q(x + 1, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
+      const int RA = wn * kWaveA + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
       uint32_t a, b;
       if (WHOLE) {
         // the 4 bytes of steps x, x + 1 of each row (x is even)
@@ -732,7 +744,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   auto read_raw = [&](int x, uint32_t* a4, uint32_t* b4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
+      const int RA = wn * kWaveA + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
       const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
       a4[i] = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
       b4[i] = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
@@ -770,13 +782,13 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   uint32_t rawa[4], rawb[4];
   if (!BF) load_sregs(s0, sra[0], srb[0]);
   {
-    const uint8_t* ta = sm.data[0][0] + (wn * 128) * kRowBytes;
+    const uint8_t* ta = sm.data[0][0] + (wn * kWaveA) * kRowBytes;
     const uint8_t* tb = sm.data[0][1] + (wk * 128) * kRowBytes;
 #pragma unroll
     for (int t = 0; t < 4; ++t) fb[0][t] = frag(tb + t * 32 * kRowBytes, frag_lo0, frag_hi0);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      if (!(HALF && (t & 1))) fa[0][t] = frag(ta + t * 32 * kRowBytes, frag_lo0, frag_hi0);
+      if (!(HALF && (t & 1)) && !(SHORT && t == 3)) fa[0][t] = frag(ta + t * 32 * kRowBytes, frag_lo0, frag_hi0);
   }
 
   // per-step scalars of the first step; later steps compute theirs one step ahead
@@ -814,7 +826,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       const int s = s0 + j;
       const int cur = u & 1, nxt = cur ^ 1;
       const int nst = ((u + 1) >> 1) & 1, nhalf = (u + 1) & 1;  // stage and half of step j + 1
-      const uint8_t* na = sm.data[nst][0] + (wn * 128) * kRowBytes;
+      const uint8_t* na = sm.data[nst][0] + (wn * kWaveA) * kRowBytes;
       const uint8_t* nb = sm.data[nst][1] + (wk * 128) * kRowBytes;
       const int flo = nhalf ? frag_lo1 : frag_lo0, fhi = nhalf ? frag_hi1 : frag_hi0;
       __builtin_amdgcn_sched_barrier(0);
@@ -834,11 +846,11 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           // first halves into block m, second halves into block (m + 8) % 16:
           // MFMAs on one accumulator stay 16 instructions apart
           const int i2 = i ^ 2;
-          if (!(HALF && (t & 1))) {
+          if (!(HALF && (t & 1)) && !(SHORT && t == 3)) {
             acc[i][t] = mfma_bf16<0>(fb[cur][i], fa[cur][t], acc[i][t]);
             acc[i2][t] = mfma_bf16<1>(fb[cur][i2], fa[cur][t], acc[i2][t]);
           }
-        } else if (!(HALF && (t & 1))) {
+        } else if (!(HALF && (t & 1)) && !(SHORT && t == 3)) {
           acc[i][t] = mfma_e4m3_sel(2 * (u & 1), 2 * (u & 1), fb[cur][i], fa[cur][t], acc[i][t], (int)srb[u >> 1][i],
                                     (int)sra[u >> 1][t]);
         }
@@ -889,7 +901,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           dma4s(k < 2 ? rA : rB, pfdst, vrow[0] + rq, __builtin_amdgcn_readfirstlane(ok ? (uint32_t)(pp * kPair) : 0u));
         }
         if (m >= 3 && m < 7) fb[nxt][m - 3] = frag(nb + (m - 3) * 32 * kRowBytes, flo, fhi);
-        if (m >= 7 && m < 11 && !(HALF && ((m - 7) & 1))) fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
+        if (m >= 7 && m < 11 && !(HALF && ((m - 7) & 1)) && !(SHORT && m == 10))
+          fa[nxt][m - 7] = frag(na + (m - 7) * 32 * kRowBytes, flo, fhi);
         if (!BF && GROUP && (u & 1) && m == 10) {
           int sq = s;
           asm volatile("" : "+s"(sq));
@@ -1062,6 +1075,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (HALF && (t & 1)) continue;  // a half tile's odd blocks belong to the other half
+      if (SHORT && t == 3) continue;  // a short tile has 3 blocks per wave
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1086,7 +1100,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       for (int x = 0; x < 8; ++x) {
         const int nl = 4 * (8 * t + x) + rsub;
         if ((nl >> 4) & 1) d[x] = (v4i){d[x].z, d[x].w, d[x].x, d[x].y};  // a constant after unrolling
-        const int n = wn * 128 + nl;
+        const int n = wn * kWaveA + nl;
         if (n < rowsA && kk < rowsB) __builtin_nontemporal_store(d[x], (v4i*)(otile + (size_t)n * ldo + kk));
       }
     }
@@ -1227,12 +1241,21 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       if (half <= 0) zero_tile(p, pc.g, pc.tn, pc.tk);
       return;
     }
+    const bool shrt = pc.tn >= p.tall;
     if (half >= 0) {
+      // a short tile is not split: half 0 computes all of it
+      if (shrt) {
+        if (half == 0) run_piece<GROUP, false, false, BF, false, false, true>(p, sm, pc);
+        return;
+      }
       pc.half = half;
       run_piece<GROUP, false, false, BF, false, true>(p, sm, pc);
       return;
     }
-    run_piece<GROUP, false, false, BF>(p, sm, pc);
+    if (shrt)
+      run_piece<GROUP, false, false, BF, false, false, true>(p, sm, pc);
+    else
+      run_piece<GROUP, false, false, BF>(p, sm, pc);
   } else {
     // ---- column mode: the pieces of this column, in sequence order -------------
     for (;;) {
@@ -1268,7 +1291,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       // LDS reads are done in every wave before new loads land
       wait_vm_all();
       __syncthreads();
-      run_piece<GROUP, true, false, BF>(p, sm, pc);
+      if (pc.tn >= p.tall)
+        run_piece<GROUP, true, false, BF, false, false, true>(p, sm, pc);
+      else
+        run_piece<GROUP, true, false, BF>(p, sm, pc);
     }
   }
 }
@@ -1379,6 +1405,7 @@ struct ShufArgs {
   uint8_t* out[2];
   int R[2];             // rows of A, B
   int bands[2];         // ceil(R / 256)
+  int tall[2];          // 256-row bands; bands b >= tall start at 256 tall + 192 (b - tall)
   int M, groups, octets;
   int sstride;  // bytes from one scale row to the next (ld / 32)
   const int32_t* offs;
@@ -1409,9 +1436,12 @@ __global__ __launch_bounds__(256) void scale_shuffle_kernel(ShufArgs a) {
   // this band's rows of the plane, the size rounded up to a dword (offsets
   // below are dword-aligned from this base: every dword is entirely inside
   // or outside the checked range)
-  const int rows = min(kTile, R - b * kTile);
+  // the band of a short tile holds its 192 rows (the rest of its 256 are zero)
+  const int tall = a.tall[op];
+  const int r0 = b < tall ? b * kTile : tall * kTile + (b - tall) * kShort;
+  const int rows = min(b < tall ? kTile : kShort, R - r0);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(a.s[op] + (size_t)b * kTile * sb, ((uint32_t)rows * sb + 3u) & ~3u);
+      make_rsrc(a.s[op] + (size_t)r0 * sb, ((uint32_t)rows * sb + 3u) & ~3u);
   auto keep_bytes = [](uint32_t x, int keep) { return keep >= 4 ? x : (keep <= 0 ? 0u : x & ((1u << (8 * keep)) - 1u)); };
   if ((sb & 15u) == 0) {
     // 16-byte aligned rows (ld % 512 == 0): one load per chunk, all eight in
@@ -1618,6 +1648,16 @@ int plan_columns(int E, int M, int N, int K, int cus, int* regions) {
   return 0;
 }
 
+// Tiles along N of 256 rows in a weight-gradient launch; the rest (two) are
+// short tiles of 192 rows.  With N % 256 == 128 the last 384 rows are two
+// short tiles rather than a whole tile and one with half its rows past N (whose
+// MFMAs would work on nothing): the same tile count, a quarter less MFMA work
+// per short tile.
+int short_tiles_from(int N) {
+  const int tN = (N + kTile - 1) / kTile;
+  return (N % kTile == kTile / 2 && tN >= 2) ? tN - 2 : tN;
+}
+
 constexpr size_t kWsAlign = 4096;
 size_t round_ws(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 
@@ -1706,6 +1746,7 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   p.K = K;
   p.tshift = tshift;
   p.tilesN = (N + kTile - 1) / kTile;
+  p.tall = short_tiles_from(N);
   p.tilesK = (K + kTile - 1) / kTile;
   // XCD regions: split the tile grid a x b = 8 ways into equal rectangles,
   // the most square split (fewest distinct A + B stripes per rectangle)
@@ -1738,6 +1779,9 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   // buffers: the last tiles of the dealing as half tiles (blocks [nfull, grid))
   const int nsplit = (!pl.ncol && !pl.shuffle) ? tail_split(grid, cus, E, Mb >> tshift) : 0;
   p.nfull = (int)grid - nsplit;
+  // a launch with half tiles keeps whole 256-row tiles: a short tile cannot be
+  // halved, and run whole in the last round it delays the round
+  if (nsplit) p.tall = p.tilesN;
   const dim3 g((unsigned)(pl.ncol ? pl.ncol * kMem : grid + nsplit)), blk(kThreads);
   hipStream_t st = (hipStream_t)stream;
   if (tshift) {
@@ -1772,6 +1816,8 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     sa.R[1] = K;
     sa.bands[0] = p.tilesN;
     sa.bands[1] = p.tilesK;
+    sa.tall[0] = p.tall;
+    sa.tall[1] = p.tilesK;
     sa.M = Mb;
     sa.sstride = ldb >> 5;
     sa.groups = pl.sgroups;
