@@ -673,13 +673,22 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     if (BF) {
       // no scales
     } else if (WHOLE) {
-      // A's block into raw[0 ..), B's into raw[kWholeOp ..), 256 bytes per
-      // instruction (each dword entirely inside or outside the checked range)
-      const int nA = (int)((kTile * sbytes + 255u) >> 8);
+      // A's block into raw[0 ..), B's into raw[kWholeOp ..).  The range check
+      // works per dword (each dword entirely inside or outside the checked
+      // range, which is rounded up to 4 bytes), so with 4-byte-aligned blocks
+      // (C % 128 == 0 and 4-byte-aligned planes) 1 KiB per instruction, 16
+      // bytes per lane: a quarter of the instructions of the dword loads
+      // (256 bytes per instruction) that other blocks take
+      const bool wide = ((sbytes & 3u) | ((uint32_t)(uintptr_t)p.sA & 3u) | ((uint32_t)(uintptr_t)p.sB & 3u)) == 0u;
+      const int shift = wide ? 10 : 8;
+      const int nA = (int)((kTile * sbytes + (1u << shift) - 1u) >> shift);
       for (int k = wave; k < 2 * nA; k += 4) {
         const int op = k >= nA, kk = k - op * nA;
-        const uint32_t dst = lds_addr(&sm.raw[op * kWholeOp + kk * 64]);
-        dma4(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), (uint32_t)kk * 256u + 4u * (uint32_t)lane);
+        const uint32_t dst = lds_addr(&sm.raw[op * kWholeOp + (kk << (shift - 2))]);
+        if (wide)
+          dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), (uint32_t)kk * 1024u + 16u * (uint32_t)lane, 0u);
+        else
+          dma4(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst), (uint32_t)kk * 256u + 4u * (uint32_t)lane);
       }
     } else if (GROUP) {
       // groups G0 and G0 + 1; the loop fetches group G + 2 for both operands
