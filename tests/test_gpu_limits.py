@@ -10,7 +10,8 @@ holds NaN codes and 0xFF scales.  Both entry points (column mode with the
 scale pre-shuffle, and one workgroup per tile).  The bf16 weight gradient is
 checked the same way at its own maximum, 2^22 tokens (8 MiB rows); the weight
 gradient at the largest widths (N = K = 65,536: 196,608 workgroups, 8 GiB of
-output per expert); and the row-ragged GEMM at the largest row count (2^23).
+output per expert); the row-ragged GEMM at the largest row count (2^23); and
+the quantiser at the largest token count and hidden width.
 """
 import numpy as np
 import pytest
@@ -173,3 +174,28 @@ def test_max_rows_fwd():
     idx = torch.as_tensor(np.stack([m, nn]), device=DEV)
     got = out[idx[0], idx[1]].view(torch.int16).cpu().numpy().view(np.uint16)
     check_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="max rows")
+
+
+@pytest.mark.parametrize("M,H", [(MAX_TOKENS, 64), (4096, 65536)])
+def test_quantize_limits(M, H):
+    """The quantiser at the largest token count (2^23: 8 MiB code rows) and
+    the largest hidden width (65,536), with offs ending 4,096 tokens before M
+    and NaN in those padding tokens: codes and scales of the first 16 hidden
+    columns (and, at the largest width, the last 16) equal the oracle's
+    byte for byte."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8840 + H)
+    x = torch.randn((M, H), generator=g, device=DEV).to(torch.bfloat16)
+    used = M - 4096 if M > 8192 else M - 512
+    x[used:] = float("nan")
+    offs = torch.tensor([used // 2, used], dtype=torch.int32, device=DEV)
+    say("quantiser limits: M=%d H=%d used=%d" % (M, H, used))
+    q, s = mxw.quantize_tokens(x, offs)
+    torch.cuda.synchronize()
+    for c0 in sorted({0, H - 16}):
+        xs = x[:, c0:c0 + 16].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        rq, rs = oracle.quantize_tokens(xs, used=used)
+        np.testing.assert_array_equal(q[c0:c0 + 16].cpu().numpy(), rq)
+        np.testing.assert_array_equal(s[c0:c0 + 16].cpu().numpy(), rs)
+    del x, q, s
+    torch.cuda.empty_cache()
