@@ -96,9 +96,12 @@ extern "C" {
  *
  * Scheduling and bits: one workgroup per (expert, 256 x 256 output tile)
  * (blog section 4), experts taken longest first (section 5.4), no atomics;
- * with short experts and a partly filled last round, that round's tiles run
- * as two half-tile workgroups each (mxw_tail_split), computing every element
- * exactly as the whole tile does.
+ * when N % 256 == 128 the last 384 rows of N are two tiles of 192 rows
+ * instead of a whole one and one half past N (the same tile count); with
+ * short experts and a partly filled last round, that round's tiles run
+ * as two half-tile workgroups each (mxw_tail_split; such a launch keeps
+ * whole 256-row tiles), computing every element exactly as the whole tile
+ * does.
  * Each output element is one workgroup's sum over its expert's window in
  * token order, so the result depends only on that expert's window of A, sA,
  * B and sB: it is bitwise reproducible run to run, and unchanged by the
