@@ -237,6 +237,21 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Inclusive prefix sum over the 64 lanes of a wave, all of which must be
+// active: log-step shifts inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8;
+// lanes with no source add 0), then lane 15 of rows 0 and 2 added to rows 1
+// and 3 (row_bcast:15) and lane 31 to rows 2 and 3 (row_bcast:31).  Six
+// VALU operations, against six LDS-crossbar round trips for a shuffle scan.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
 // live-sub-block mask of K-step s for window [start, end): bit b set iff tokens
 // [64 s + 32 b, 64 s + 32 b + 32) lie inside the window.
 __device__ __forceinline__ uint32_t live_mask(int s, int start, int end) {
@@ -1158,16 +1173,9 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       const int e = base + lane;
       const int it = (e < E && sm.len[e] > 0) ? window_iters(sm.start[e], sm.len[e]) : 0;
       const int cost = it ? 4 * it + p.hov : 0;
-      int sc = cost, sn = it > 0, sz = (e < E && it == 0);
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int x = __shfl_up(sc, d), y = __shfl_up(sn, d), z = __shfl_up(sz, d);
-        if (lane >= d) {
-          sc += x;
-          sn += y;
-          sz += z;
-        }
-      }
+      const int sc = wave_scan_incl(cost);
+      const int sn = wave_scan_incl(it > 0);
+      const int sz = wave_scan_incl(e < E && it == 0);
       if (it) {
         sm.ne[cn + sn - 1] = e;
         sm.nit[cn + sn - 1] = it;
@@ -1175,9 +1183,9 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
       } else if (e < E) {
         sm.ee[ce + sz - 1] = e;
       }
-      cn += __shfl(sn, 63);
-      ce += __shfl(sz, 63);
-      acc_cost += __shfl(sc, 63);
+      cn += __builtin_amdgcn_readlane(sn, 63);
+      ce += __builtin_amdgcn_readlane(sz, 63);
+      acc_cost += __builtin_amdgcn_readlane(sc, 63);
     }
     if (lane == 0) {
       sm.cnt[0] = cn;
@@ -1324,8 +1332,7 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
   const int lane = tid & 63;
   const int E = p.E, R = p.R;
   const int bid = blockIdx.x;
-  // ---- row windows from offs (clamped to [0, R], monotone) and the exclusive
-  // prefix of their row-tile counts (wave 0 scan) ------------------------------
+  // ---- row windows from offs (clamped to [0, R], monotone) -------------------
   if (tid < E) {
     int e = min(max(p.offs[tid], 0), R);
     const int st = tid ? min(max(p.offs[tid - 1], 0), R) : 0;
@@ -1334,46 +1341,56 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
     sm.len[tid] = e - st;
   }
   __syncthreads();
-  if (tid < 64) {
-    int carry = 0;
-    for (int base = 0; base < E; base += 64) {
-      const int e = base + lane;
-      const int nt = e < E ? (sm.len[e] + kTile - 1) / kTile : 0;
-      int sc = nt;
+  // ---- exclusive prefix of the experts' row-tile counts, in registers --------
+  // Every wave computes it for itself (one scan per 64 experts), so no further
+  // barrier and no LDS round trip stand between the windows and the tile.
+  static_assert(MXW_MAX_EXPERTS <= 4 * 64, "at most four 64-expert chunks");
+  int cst[4], cln[4], cpre[4];
+  int total = 0;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int x = __shfl_up(sc, d);
-        if (lane >= d) sc += x;
-      }
-      if (e < E) sm.pre[e] = carry + sc - nt;
-      carry += __shfl(sc, 63);
+  for (int c = 0; c < 4; ++c) {
+    cst[c] = cln[c] = cpre[c] = 0;
+    if (64 * c < E) {
+      const int e = 64 * c + lane;
+      const int st = e < E ? sm.start[e] : 0;
+      const int ln = e < E ? sm.len[e] : 0;
+      const int ntl = (ln + kTile - 1) / kTile;
+      const int inc = wave_scan_incl(ntl);
+      cst[c] = st;
+      cln[c] = ln;
+      cpre[c] = total + inc - ntl;
+      total += __builtin_amdgcn_readlane(inc, 63);
     }
-    if (lane == 0) sm.cnt[0] = carry;
   }
-  __syncthreads();
-  const int tiles = __builtin_amdgcn_readfirstlane(sm.cnt[0]) * p.tilesN;
+  const int tiles = total * p.tilesN;
   const int per = (tiles + 7) >> 3;  // work items per XCD
   const int t = (bid & 7) * per + (bid >> 3);
   if ((bid >> 3) >= per || t >= tiles) return;
   const int mt = t / p.tilesN, nt = t - mt * p.tilesN;
-  // the expert whose row tiles hold mt: the last non-empty one starting at or before it
-  int g = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const bool hit = e < E && sm.len[e] > 0 && sm.pre[e] <= mt;
-    const uint64_t bal = __ballot(hit);
-    if (bal) g = base + 63 - (int)__builtin_clzll(bal);
+  // the expert whose row tiles hold mt: the last non-empty one starting at or
+  // before it, and its window and prefix, read from the lane that holds them
+  int g = 0, gs = 0, gl = 0, gp = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (64 * c < E) {
+      const uint64_t bal = __ballot(64 * c + lane < E && cln[c] > 0 && cpre[c] <= mt);
+      if (bal) {
+        const int l = 63 - (int)__builtin_clzll(bal);
+        g = 64 * c + l;
+        gs = __builtin_amdgcn_readlane(cst[c], l);
+        gl = __builtin_amdgcn_readlane(cln[c], l);
+        gp = __builtin_amdgcn_readlane(cpre[c], l);
+      }
+    }
   }
-  g = __builtin_amdgcn_readfirstlane(g);
   Piece pc = {};
   pc.g = g;
   pc.tn = mt;
   pc.tk = nt;
   pc.start = 0;
   pc.end = p.M;
-  pc.ar0 = __builtin_amdgcn_readfirstlane(sm.start[g]) + (mt - __builtin_amdgcn_readfirstlane(sm.pre[g])) * kTile;
-  pc.ra = min(kTile, __builtin_amdgcn_readfirstlane(sm.start[g]) + __builtin_amdgcn_readfirstlane(sm.len[g]) - pc.ar0);
-  __syncthreads();  // the scan's LDS words are not reused below, but keep the waves together
+  pc.ar0 = gs + (mt - gp) * kTile;
+  pc.ra = min(kTile, gs + gl - pc.ar0);
   run_piece<GROUP, false, true, false, WHOLE>(p, sm, pc);
 }
 
