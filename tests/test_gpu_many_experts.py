@@ -105,3 +105,56 @@ def test_quantize_256_experts_offs():
     rq, rs = oracle.quantize_tokens(x.view(torch.int16).numpy().view(np.uint16), used=int(offs[-1]))
     np.testing.assert_array_equal(s.cpu().numpy(), rs)
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("E,live", [
+    (65, {64: 777}),
+    (130, {0: 300, 63: 513, 64: 256, 127: 1, 128: 700, 129: 17}),
+    (256, {255: 1000}),
+    (256, {0: 5, 64: 600, 128: 257, 192: 3, 255: 511}),
+])
+def test_rows_chunk_boundaries(E, live):
+    """The row-ragged GEMM's tile prefix runs in 64-expert chunks (a scan per
+    chunk plus the carry) and its expert lookup takes the last hit over the
+    chunks: live experts only on either side of the chunk edges, several of
+    them spanning more than one 256-row tile, every other expert empty."""
+    sizes = np.zeros(E, np.int64)
+    for g, n in live.items():
+        sizes[g] = n
+    used = int(sizes.sum())
+    R, C, N = used + 64, 64, 48
+    cfg = W.make_rows(E, R, C, N, sizes, seed=4500 + E + len(live), device=DEV)
+    say("rows chunk edges: E=%d live=%s R=%d" % (E, sorted(live), R))
+    out = torch.empty((R, N), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(BF16_NAN)
+    mxw.fwd(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out)
+    torch.cuda.synchronize()
+    bits = bf16_bits(out)
+    ref = oracle.rows_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
+    check_close(bits[:used], ref[:used], what="rows chunk edges E=%d" % E)
+    assert (bits[used:] == BF16_NAN).all()
+
+
+def test_wgrad_column_mode_chunk_boundaries():
+    """Column mode's compact lists and cost prefix are built by 64-lane scans
+    with a carry: the live experts sit at 63, 64 and 69 (one long window
+    starting at an odd multiple of 32), the rest are empty."""
+    E, N, K = 70, 16, 16
+    M = 8192 * E
+    sizes = np.zeros(E, np.int64)
+    sizes[0] = 32
+    sizes[63] = 8192 * 20 + 32
+    sizes[64] = 8192 * 30 + 160
+    sizes[69] = 8192 * 10
+    assert mxw.columns(E, M, N, K) > 0
+    cfg = W.make_random(E, N, K, M, sizes, seed=4600, device=DEV)
+    ref = oracle.wgrad_f64(*(cfg[k].cpu().numpy() for k in ("A", "sA", "B", "sB", "offs")))
+    for entry in ("ws", "plain"):
+        say("wgrad column-mode chunk edges [%s]: E=%d M=%d" % (entry, E, M))
+        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
+        out.view(torch.int16).fill_(BF16_NAN)
+        mxw.wgrad(cfg["A"], cfg["sA"], cfg["B"], cfg["sB"], cfg["offs"], out=out, plain=(entry == "plain"))
+        torch.cuda.synchronize()
+        bits = bf16_bits(out)
+        check_close(bits, ref, what="column-mode chunk edges [%s]" % entry)
+        assert (bits[sizes == 0] == 0).all()
