@@ -23,7 +23,9 @@
 //       (longest first, ties to the lower index; blog section 5.4), and
 //       numbers tiles so that the workgroups the dispatcher deals to one XCD
 //       (block index mod 8, blog section 3) cover a compact rectangle of the
-//       same expert's tiles (blog section 5.5);
+//       same expert's tiles (blog section 5.5); with short experts and a
+//       partly filled last round, that round's tiles run as two half-tile
+//       workgroups each (the even and the odd 32-row blocks, same bits);
 //     - column mode (few tiles per CU, long experts): one workgroup per CU;
 //       16 workgroups on one XCD form a column that works through regions of
 //       up to 16 tiles (4 x 4) of one expert, all members on the same tokens
@@ -36,6 +38,9 @@
 //       FP32 partial tiles (no workgroup waits for another).  The tiles of a
 //       column that share a stripe split an L2 prefetch of it between them,
 //       one pair ahead of their loads.
+//     In both modes, when N % 256 == 128 the last 384 rows of N are two short
+//     tiles of 192 rows (three 32-row blocks per wave) rather than a whole
+//     tile and one with half its rows past N.
 //   * staging: an LDS stage holds a pair of K-steps (256 rows x 128 tokens of
 //     A and of B, 64 KiB), filled by 16-byte LDS-direct buffer loads, 8 rows x
 //     128 bytes per instruction, so every memory request is one whole cache
@@ -68,9 +73,10 @@
 //     bytes of 256 rows lie in 256 cache lines, and at long experts that
 //     costs the weight gradient ~6%; it then first rewrites the planes so that
 //     a band's groups are contiguous (scale_shuffle_kernel).  The same runs
-//     when scale rows are not 16-byte aligned (M % 512 != 0); the row-ragged
-//     GEMM reads its planes directly, with the two aligned dwords around a
-//     row's 4 bytes of 2 K-steps when C % 512 != 0.  A scale load per row per
+//     when scale rows are not 16-byte aligned (M % 512 != 0).  The row-ragged
+//     GEMM reads its planes directly: a tile's whole scale blocks once, in the
+//     prologue, when C <= 1,504, otherwise 16-byte groups (C % 512 == 0) or the
+//     two aligned dwords around a row's 4 bytes of 2 K-steps.  A scale load per row per
 //     step would double the number of L1 -> L2 requests of a step (every lane
 //     hits a different row), which measurably slows the data stream.
 //   * contraction: v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
@@ -81,7 +87,8 @@
 //   * epilogue: FP32 -> bf16 round-to-nearest-even in registers (blog
 //     section 5.5), staged through LDS so that every global store writes
 //     whole 128-byte lines (8-byte stores straight from the MFMA layout touch
-//     32 lines per instruction and took ~19k clocks per tile).
+//     32 lines per instruction and took ~19k clocks per tile); the stores are
+//     non-temporal, so the output streams past the L2.
 //
 // MFMA lane layout used here (32x32x64, FP8 operands, checked on gfx950): lane
 // l holds row l % 32 and tokens {16(l/32) + p : p < 16} in bytes 0..15 and
@@ -155,13 +162,15 @@ static_assert(kTile * (kWholeC / 32) / 4 + 2 <= kWholeOp, "whole-tile scale bloc
 struct Smem {
   // [stage][0 = A n-rows, 1 = B k-rows]: 256 rows x 128 tokens, chunk-swizzled
   uint8_t data[2][2][kOpBytes];
-  // raw E8M0 scale bytes as loaded, 24 KiB, in one of two layouts:
+  // raw E8M0 scale bytes as loaded, 24 KiB, in one of three layouts:
   //  grouped (scale rows 16-byte aligned): [group % 3][op][row][4 dwords], the
   //    2 sub-block bytes of 8 consecutive K-steps of a row;
   //  paired (any row alignment): [pair % 4][op][dword][row], the two aligned
   //    dwords that hold a row's 4 bytes of 2 consecutive K-steps (16 KiB),
   //    then 1 KiB taking the out-of-range scale-slot loads of steps that
-  //    have no scale pair to fetch (written with zeros, never read)
+  //    have no scale pair to fetch (written with zeros, never read);
+  //  whole (row-ragged GEMM, C <= kWholeC): [op][kWholeOp dwords], the tile's
+  //    whole scale block of 256 consecutive rows per operand
   uint32_t raw[6144];
   int start[MXW_MAX_EXPERTS];
   int len[MXW_MAX_EXPERTS];
@@ -469,7 +478,8 @@ struct Piece {
 // WHOLE (row-ragged GEMM with C <= kWholeC): the tile's whole scale blocks
 // (its 256 A rows and 256 B rows are consecutive rows of the planes, so each
 // block is one contiguous range of 256 C / 32 bytes) are DMA'd once, in the
-// prologue, with coalesced dword loads; the K-loop then loads no scales.
+// prologue, with 16-byte LDS-direct loads (dword loads when a block is not
+// 4-byte aligned); the K-loop then loads no scales.
 // HALF (weight gradient, one workgroup per tile): a half tile.  The
 // workgroup computes only the even 32-row A blocks of each wave's quarter, on
 // an A band that starts 32 pc.half rows below the tile's, so the two halves
@@ -788,7 +798,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // operand are read one 32-row block per MFMA slot right after the odd
   // step's barrier (m = 2 .. 5), and joined, shifted and masked one block per
   // slot (m = 11 .. 14); formed all at once, the 16 LDS reads, their waits and
-  // ~60 vector instructions sat between two MFMAs (+1.3% at C = 1,408).  The
+  // ~60 vector instructions sat between two MFMAs (+2.0% at C = 1,408).  The
   // other scale paths keep the placement below, which measured best for them.
   uint32_t wlo[8], whi[8];  // [operand * 4 + block]
   uint32_t wpm = 0;
