@@ -81,3 +81,29 @@ def test_full_size_tiles(name):
 def test_16b_24k_plain_entry_tiles():
     cfg = W.make_config("16b_24k", device=DEV)
     check_tiles(cfg, "16b_24k", "plain", tile_pairs(cfg, 12, 23))
+
+
+def test_16b_24k_bitwise_many_calls():
+    """Bitwise reproducibility at the headline configuration under load: 48
+    calls of the workspace entry (column mode, arrival counters, partial tiles,
+    the scale pre-shuffle) back to back on one stream, no synchronisation in
+    between, into four rotating outputs that are compared with the first call
+    on the GPU as they come; then 12 calls of the entry without a workspace
+    the same way."""
+    cfg = W.make_config("16b_24k", device=DEV)
+    E, N, K, M = cfg["E"], cfg["N"], cfg["K"], cfg["M"]
+    args = [cfg[k] for k in ("A", "sA", "B", "sB", "offs")]
+    for plain, calls in ((False, 48), (True, 12)):
+        tag = "plain" if plain else "ws"
+        say("16b_24k [%s]: %d calls back to back, each against the first" % (tag, calls))
+        first = mxw.wgrad(*args, plain=plain)
+        outs = [torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+        diffs = torch.zeros(calls, dtype=torch.int64, device=DEV)
+        for c in range(calls):
+            o = outs[c % 4]
+            o.view(torch.int16).fill_(0x7FC0)
+            mxw.wgrad(*args, out=o, plain=plain)
+            diffs[c] = (o.view(torch.int16) != first.view(torch.int16)).sum()
+        torch.cuda.synchronize()
+        d = diffs.cpu().numpy()
+        assert (d == 0).all(), "%s: calls %s differ from the first (%s elements)" % (tag, np.nonzero(d)[0], d[d != 0])
