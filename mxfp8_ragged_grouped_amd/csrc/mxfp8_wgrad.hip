@@ -488,10 +488,12 @@ struct Piece {
 // so the output bits are the whole tile's.  The A row groups of the odd
 // blocks are neither loaded nor read, and their MFMAs are not issued: half
 // the MFMA work and a quarter less staging per K-step.
-template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false, bool HALF = false, bool SHORT = false>
+template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false, bool HALF = false, bool SHORT = false,
+          bool WALIGN = false>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
   static_assert(!HALF || (!COL && !ROWS && !WHOLE), "half tiles: weight gradient, one workgroup per tile");
   static_assert(!SHORT || (!ROWS && !WHOLE && !HALF), "short tiles: weight gradient");
+  static_assert(!WALIGN || WHOLE, "dword-aligned scale rows: whole-tile scale blocks");
   // A rows per wave: its 32-row blocks t < (SHORT ? 3 : 4)
   constexpr int kWaveA = SHORT ? kShort / 2 : kTile / 2;
   int tid = threadIdx.x;
@@ -753,10 +755,16 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
       const int RA = wn * kWaveA + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
       uint32_t a, b;
       if (WHOLE) {
-        // the 4 bytes of steps x, x + 1 of each row (x is even)
+        // the 4 bytes of steps x, x + 1 of each row (x is even; one aligned
+        // dword when the rows are, WALIGN)
         const uint32_t ba = (uint32_t)RA * sbytes + 2u * (uint32_t)x, bb = (uint32_t)RB * sbytes + 2u * (uint32_t)x;
-        a = __builtin_amdgcn_alignbit(sm.raw[(ba >> 2) + 1], sm.raw[ba >> 2], (ba & 3u) * 8u);
-        b = __builtin_amdgcn_alignbit(sm.raw[kWholeOp + (bb >> 2) + 1], sm.raw[kWholeOp + (bb >> 2)], (bb & 3u) * 8u);
+        if (WALIGN) {
+          a = sm.raw[ba >> 2];
+          b = sm.raw[kWholeOp + (bb >> 2)];
+        } else {
+          a = __builtin_amdgcn_alignbit(sm.raw[(ba >> 2) + 1], sm.raw[ba >> 2], (ba & 3u) * 8u);
+          b = __builtin_amdgcn_alignbit(sm.raw[kWholeOp + (bb >> 2) + 1], sm.raw[kWholeOp + (bb >> 2)], (bb & 3u) * 8u);
+        }
       } else if (GROUP) {
         const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
         a = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
@@ -806,9 +814,11 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
     const int RA = wn * 128 + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
     const uint32_t ba = (uint32_t)RA * sbytes + 2u * (uint32_t)x, bb = (uint32_t)RB * sbytes + 2u * (uint32_t)x;
     wlo[i] = sm.raw[ba >> 2];
-    whi[i] = sm.raw[(ba >> 2) + 1];
     wlo[4 + i] = sm.raw[kWholeOp + (bb >> 2)];
-    whi[4 + i] = sm.raw[kWholeOp + (bb >> 2) + 1];
+    if (!WALIGN) {  // rows of C / 32 bytes not a multiple of 4: the dword after too
+      whi[i] = sm.raw[(ba >> 2) + 1];
+      whi[4 + i] = sm.raw[kWholeOp + (bb >> 2) + 1];
+    }
   };
 
   v8i fa[2][4], fb[2][4];
@@ -957,8 +967,13 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
             wpm = (((live_mask_q(sq + 1, qs, qn) >> msb) & 1u) ? 0xFFu : 0u) |
                   (((live_mask_q(sq + 2, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
           const uint32_t RA = (uint32_t)(wn * 128 + 32 * i + fr), RB = (uint32_t)(wk * 128 + 32 * i + fr);
-          sra[nb][i] = (__builtin_amdgcn_alignbit(whi[i], wlo[i], ((RA * sbytes) & 3u) * 8u) >> mshift) & wpm;
-          srb[nb][i] = (__builtin_amdgcn_alignbit(whi[4 + i], wlo[4 + i], ((RB * sbytes) & 3u) * 8u) >> mshift) & wpm;
+          if (WALIGN) {
+            sra[nb][i] = (wlo[i] >> mshift) & wpm;
+            srb[nb][i] = (wlo[4 + i] >> mshift) & wpm;
+          } else {
+            sra[nb][i] = (__builtin_amdgcn_alignbit(whi[i], wlo[i], ((RA * sbytes) & 3u) * 8u) >> mshift) & wpm;
+            srb[nb][i] = (__builtin_amdgcn_alignbit(whi[4 + i], wlo[4 + i], ((RB * sbytes) & 3u) * 8u) >> mshift) & wpm;
+          }
         }
         if (!BF && !WHOLE && m == 15) {  // after the step's data loads (vmcnt order)
           if (!GROUP) {
@@ -1335,7 +1350,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
 // a row tile (sharing its A rows) and the row tiles of an expert (sharing its
 // B) meet in one L2.  The grid is sized on the host for the most row tiles
 // any offs can give (R / 256 + E); blocks past the actual count exit.
-template <bool GROUP, bool WHOLE = false>
+template <bool GROUP, bool WHOLE = false, bool WALIGN = false>
 __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int tid = threadIdx.x;
@@ -1401,7 +1416,7 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(Params p) {
   pc.end = p.M;
   pc.ar0 = gs + (mt - gp) * kTile;
   pc.ra = min(kTile, gs + gl - pc.ar0);
-  run_piece<GROUP, false, true, false, WHOLE>(p, sm, pc);
+  run_piece<GROUP, false, true, false, WHOLE, false, false, WALIGN>(p, sm, pc);
 }
 
 // ---- token-axis MXFP8 quantiser --------------------------------------------------
@@ -2038,7 +2053,9 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
   p.R = R;
   p.tilesN = (N + kTile - 1) / kTile;
   p.tilesK = 0;
-  if (C <= kWholeC)
+  if (C <= kWholeC && (C & 127) == 0)  // scale rows a whole number of dwords
+    hipLaunchKernelGGL((rows_kernel<false, true, true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  else if (C <= kWholeC)
     hipLaunchKernelGGL((rows_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   else if ((C & 511) == 0)
     hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);

@@ -51,10 +51,10 @@ ROWS_CASES = [
     # E, R, C, N, sizes (sum <= R; rows after them are padding)
     (3, 700, 256, 272, [300, 0, 290]),          # unaligned row boundaries, empty expert, partial N tile, padding
     (1, 16, 32, 16, [16]),                      # the smallest problem
-    (4, 1100, 160, 512, [1, 255, 257, 513]),    # C % 128 != 0 (paired scale path), 1-row and tile-straddling experts
-    (2, 600, 512, 256, [512, 88]),              # C % 512 == 0 (grouped scale path)
+    (4, 1100, 160, 512, [1, 255, 257, 513]),    # whole-tile scale blocks, 5-byte scale rows; 1-row and tile-straddling experts
+    (2, 600, 512, 256, [512, 88]),              # whole-tile scale blocks, dword-aligned scale rows
     (5, 1024, 1408, 336, [200, 0, 0, 600, 224]),  # the 16B down-projection width as C
-    (6, 520, 2048, 1408, [100, 32, 0, 200, 96, 64]),  # 16B gate/up widths
+    (6, 520, 2048, 1408, [100, 32, 0, 200, 96, 64]),  # 16B gate/up widths (C % 512 == 0: grouped scale loads)
     (3, 520, 1440, 272, [0, 260, 200]),         # whole-tile scale blocks, 45-byte scale rows (odd)
     (2, 600, 1504, 128, [300, 257]),            # the largest C with whole-tile scale blocks
     (2, 300, 1568, 160, [150, 100]),            # C % 512 != 0 above it: the paired scale path
