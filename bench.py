@@ -131,6 +131,11 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
+def note(msg):
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
+
+
 def cpu_baseline(cfg, A, sA, B, sB, offs, budget_s=25.0):
     """Time the oracle on a bounded sample of the workload: every s-th row of A
     and of B (1/s^2 of the outputs, every routed token of every expert).  A
@@ -158,15 +163,19 @@ def cpu_baseline(cfg, A, sA, B, sB, offs, budget_s=25.0):
                                                                8: "every 8th row"}[stride], na, nb,
                                                cfg["N"], cfg["K"], int(used), dt)}
     if float(cfg["M"]) / cfg["E"] < 8192:
-        # the small workloads: the same run on one core as well
+        # the small workloads: a run on one core as well, at the smallest
+        # stride (not below the one above) whose estimate stays within budget_s
         threads = oracle.max_threads()
-        oracle.set_threads(1)
-        try:
-            dt1, na1, nb1 = run(stride)
-        finally:
-            oracle.set_threads(threads)
-        res["single_core"] = {"value": 2.0 * used * na1 * nb1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
-                              "seconds": round(dt1, 2)}
+        est1 = lambda s: t_probe * threads * (8 // s) ** 2
+        s1 = next((s for s in (1, 2, 4, 8) if s >= stride and est1(s) <= budget_s), None)
+        if s1 is not None:
+            oracle.set_threads(1)
+            try:
+                dt1, na1, nb1 = run(s1)
+            finally:
+                oracle.set_threads(threads)
+            res["single_core"] = {"value": 2.0 * used * na1 * nb1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                                  "seconds": round(dt1, 2), "stride": s1}
     return res
 
 
@@ -799,12 +808,14 @@ def main():
         res["baseline_note"] = ("vs_baseline = value / 2,174 TFLOP/s, the blog's kernel at the 16B ragged shape on "
                                 "MI355X (their routing: linear ramp / ragged draw at 1.5x; ours: seeded Dirichlet "
                                 "at %.2fx)" % cfg["skew"])
+    note("%s: %.4f ms per step; sustained passes" % (args.workload, ms))
     if not args.no_sustained:
         sus = sustained_leg(step, ms, stream, 1.0 if small else 3.0, tflops_of_ms=tflops_of, peak=PEAK_TFLOPS,
                             power=not args.no_power)
         if "power" in sus:
             res["power"] = sus.pop("power")
         res["sustained"] = sus
+    note("padded rows, the entry without a workspace, cold caches, graph replay")
     if not args.no_padded and not plain_first and not args.ld_pad:
         # the same operands in row-padded storage (ld = M + 128 tokens: the
         # layout mxfp8_quantize_tokens writes with ld), the same entry point
@@ -841,8 +852,10 @@ def main():
         gr["tflops"] = round(tflops_of(gr["ms_per_call"]), 2)
         res["graph_replay"] = gr
     if not args.no_bf16:
+        note("torch bf16 grouped GEMM on the same problem")
         res["bf16_context"] = bf16_context(cfg, tflops, args, stream)
     if not args.no_cpu:
+        note("CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(cfg, cfg["A"].cpu().numpy(), cfg["sA"].cpu().numpy(),
                                            cfg["B"].cpu().numpy(), cfg["sB"].cpu().numpy(),
                                            cfg["offs"].cpu().numpy())

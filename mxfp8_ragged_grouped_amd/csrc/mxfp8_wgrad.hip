@@ -176,8 +176,12 @@ struct Smem {
   int len[MXW_MAX_EXPERTS];
   int order[MXW_MAX_EXPERTS];
   // column mode: non-empty experts in index order (expert, loop iterations,
-  // exclusive prefix of region costs), the empty ones, and their counts
-  int ne[MXW_MAX_EXPERTS];
+  // exclusive prefix of region costs), the empty ones, and their counts; one
+  // workgroup per tile: the experts' ranking keys in place of the first list
+  union {
+    int ne[MXW_MAX_EXPERTS];
+    uint32_t key[MXW_MAX_EXPERTS];
+  };
   int nit[MXW_MAX_EXPERTS];
   int pre[MXW_MAX_EXPERTS];
   int ee[MXW_MAX_EXPERTS];
@@ -1178,17 +1182,19 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
     if (e < s) e = s;
     sm.start[tid] = s;
     sm.len[tid] = e - s;
+    static_assert(MXW_MAX_TOKENS < (1 << 24) && MXW_MAX_EXPERTS <= 256, "ranking key fields");
+    // ranking key: window bytes (< 2^24) above 255 - g, so keys are distinct
+    // and a larger key means a longer window, or an equal one of a lower index
+    if (!COL) sm.key[tid] = ((uint32_t)(e - s) << 8) | (uint32_t)(255 - tid);
   }
   __syncthreads();
   if (!COL) {
     // ---- longest-first ranking: lane g counts the experts ahead of it -------
+    // (one compare and one add per expert)
     if (tid < E) {
-      const int mine = sm.len[tid];
+      const uint32_t mine = sm.key[tid];
       int r = 0;
-      for (int u = 0; u < E; ++u) {
-        const int l = sm.len[u];
-        r += (l > mine) || (l == mine && u < tid);
-      }
+      for (int u = 0; u < E; ++u) r += sm.key[u] > mine;
       sm.order[r] = tid;
     }
   } else if (wave == 0) {
