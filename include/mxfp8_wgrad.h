@@ -41,7 +41,8 @@ extern "C" {
 #define MXW_OK 0
 #define MXW_ERR_NULL (-1)      /* a required pointer is NULL */
 #define MXW_ERR_DIM (-2)       /* a size outside the supported range */
-#define MXW_ERR_ALIGN (-3)     /* A, B or out not 16-byte aligned */
+#define MXW_ERR_ALIGN (-3)     /* A, B or out not 16-byte aligned, or sA / sB
+                                  not 4-byte aligned */
 #define MXW_ERR_DEVICE (-4)    /* current device is not gfx950, or no device */
 #define MXW_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError) */
 #define MXW_ERR_WORKSPACE (-6) /* workspace NULL, smaller than its size query,
@@ -75,8 +76,8 @@ extern "C" {
  *   stream  a hipStream_t (NULL = the default stream), passed as void*.
  *
  * Host-checked preconditions (violations return an error code and launch
- * nothing): non-NULL pointers; A, B and out 16-byte aligned; the ranges above;
- * the current device is gfx950.
+ * nothing): non-NULL pointers; A, B and out 16-byte aligned, sA and sB
+ * 4-byte aligned; the ranges above; the current device is gfx950.
  *
  * Device-data preconditions (not checked on the host, which never reads
  * offs): offs non-decreasing, every offs[g] a multiple of 32, offs[E-1] <= M.
@@ -119,7 +120,7 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
  * described there (0 = M).  Reads device properties only.  128 MiB of FP32
  * partial tiles on a 256-CU device when the launch runs in column mode
  * (mxw_columns() > 0), plus (ceil(N/256) + ceil(K/256)) * ceil(M/512) * 4 KiB
- * of shuffled scales when it pre-shuffles (M >= 4096 E, or ld % 512 != 0):
+ * of shuffled scales when it pre-shuffles (M >= 4096 E, or ld % 128 != 0):
  * 149 MiB at the 16B shape with 196,608 tokens, 88 MiB at 671B gate/up with
  * 262,144.
  */
@@ -137,7 +138,7 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K);
  *    fixed order through FP32 partial tiles in the workspace: the last of
  *    its pieces to finish (found with a device-scope counter) adds the
  *    others' partials.  No workgroup ever waits for another.
- *  - the scale pre-shuffle (M >= 4096 E or ld % 512 != 0): a short first
+ *  - the scale pre-shuffle (M >= 4096 E or ld % 128 != 0): a short first
  *    kernel rewrites sA and sB into the workspace so that the main kernel's
  *    scale loads read consecutive bytes (the blog has a per-call pre-shuffle
  *    too, section 5.6).
@@ -155,7 +156,7 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K);
  *                    (ld = M + 128) avoids that at long experts (16B shape,
  *                    196,608 tokens: 35% fewer HBM bytes, 3-4% faster;
  *                    671B: 13% fewer reads, 2-3% faster).  A stride that is
- *                    not a multiple of 512 needs the scale pre-shuffle,
+ *                    not a multiple of 128 needs the scale pre-shuffle,
  *                    which loses at short experts (~1,000 tokens each).
  *                    mxfp8_quantize_tokens writes such padded rows.
  *   workspace        caller-owned device memory, 256-byte aligned, of at
@@ -298,7 +299,7 @@ int mxw_tail_split(int E, int M, int N, int K);
 
 /*
  * mxw_scale_shuffle -- 1 if mxfp8_wgrad_grouped_ws with (E, M) runs the scale
- * pre-shuffle kernel before the main kernel (M >= 4096 E or M % 512 != 0),
+ * pre-shuffle kernel before the main kernel (M >= 4096 E or M % 128 != 0),
  * 0 if it launches the main kernel alone, MXW_ERR_DIM for invalid sizes.
  * Host-only: no device access.
  */
@@ -337,9 +338,9 @@ int mxw_scale_shuffle(int E, int M);
  *   stream  a hipStream_t (NULL = the default stream), passed as void*.
  *
  * Host-checked preconditions return an error code and launch nothing:
- * non-NULL pointers; A, B and out 16-byte aligned; the ranges above; a
- * gfx950 device.  Device-data preconditions (never read on the host): offs
- * non-decreasing and offs[E-1] <= R; row boundaries need no alignment.
+ * non-NULL pointers; A, B and out 16-byte aligned, sA and sB 4-byte
+ * aligned; the ranges above; a gfx950 device.  Device-data preconditions
+ * (never read on the host): offs non-decreasing and offs[E-1] <= R; row boundaries need no alignment.
  * Rows in [offs[E-1], R) belong to no expert: they are neither read as
  * values nor written.  Malformed offs give unspecified values but no
  * out-of-bounds access (windows are clamped to [0, R], loads range-checked,

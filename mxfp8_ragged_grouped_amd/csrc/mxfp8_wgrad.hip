@@ -73,10 +73,11 @@
 //     bytes of 256 rows lie in 256 cache lines, and at long experts that
 //     costs the weight gradient ~6%; it then first rewrites the planes so that
 //     a band's groups are contiguous (scale_shuffle_kernel).  The same runs
-//     when scale rows are not 16-byte aligned (M % 512 != 0).  The row-ragged
-//     GEMM reads its planes directly: a tile's whole scale blocks once, in the
-//     prologue, when C <= 1,504, otherwise 16-byte groups (C % 512 == 0) or the
-//     two aligned dwords around a row's 4 bytes of 2 K-steps.  A scale load per row per
+//     when scale rows are not a whole number of dwords (M % 128 != 0).  The
+//     row-ragged GEMM reads its planes directly: a tile's whole scale blocks
+//     once, in the prologue, when C <= 1,504, otherwise 16-byte groups
+//     (C % 128 == 0) or the two aligned dwords around a row's 4 bytes of 2
+//     K-steps.  A scale load per row per
 //     step would double the number of L1 -> L2 requests of a step (every lane
 //     hits a different row), which measurably slows the data stream.
 //   * contraction: v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
@@ -163,7 +164,7 @@ struct Smem {
   // [stage][0 = A n-rows, 1 = B k-rows]: 256 rows x 128 tokens, chunk-swizzled
   uint8_t data[2][2][kOpBytes];
   // raw E8M0 scale bytes as loaded, 24 KiB, in one of three layouts:
-  //  grouped (scale rows 16-byte aligned): [group % 3][op][row][4 dwords], the
+  //  grouped (scale rows a whole number of dwords): [group % 3][op][row][4 dwords], the
   //    2 sub-block bytes of 8 consecutive K-steps of a row;
   //  paired (any row alignment): [pair % 4][op][dword][row], the two aligned
   //    dwords that hold a row's 4 bytes of 2 consecutive K-steps (16 KiB),
@@ -614,7 +615,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // Scale loads.  A K-step needs 2 bytes of each of 512 rows; fetching them
   // step by step presents one cache line per row per step to the memory path,
   // as many requests as all of the step's operand data.  So when scale rows
-  // are 16-byte aligned (M % 512 == 0) each row's 16 bytes of 8 consecutive
+  // are a whole number of dwords (M % 128 == 0; a 16-byte LDS-direct load
+  // takes a 4-byte-aligned start) each row's 16 bytes of 8 consecutive
   // K-steps ("group" G = steps 8G .. 8G+7) come in one 16-byte load per lane
   // and operand, into 3 buffers by G % 3: one load per loop iteration (4
   // K-steps), operand k % 2 of group (s0 + 4 (k - k % 2)) / 8 + 2 in
@@ -1160,8 +1162,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   }
 }
 
-// GROUP: scale rows are 16-byte aligned (M % 512 == 0) and scales are loaded
-// 8 K-steps at a time; otherwise 2 K-steps at a time.  COL: column mode (see
+// GROUP: scale rows are a whole number of dwords (M % 128 == 0) and scales
+// are loaded 8 K-steps at a time; otherwise 2 K-steps at a time.  COL: column mode (see
 // Params); otherwise one workgroup per (expert, tile).  BF: bf16 operands.
 template <bool GROUP, bool COL, bool BF = false>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
@@ -1667,7 +1669,7 @@ int check_device(int* cus = nullptr) {
 
 // whether an E4M3 weight-gradient call with a workspace pre-shuffles its
 // scales for (E, M) and row stride ld
-bool uses_scale_shuffle(int E, int M, int ld) { return (ld & 511) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
+bool uses_scale_shuffle(int E, int M, int ld) { return (ld & 127) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
 
 // One workgroup per tile (operands and scales read from the caller's buffers): how
 // many of the last tiles of the dealing (the shortest experts', longest
@@ -1851,17 +1853,18 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     }
   } else if (!pl.shuffle) {
     // the caller's scale planes: 16-byte groups of 8 K-steps when scale rows
-    // are 16-byte aligned (ld % 512 == 0), else the two aligned dwords around
-    // each row's 2 K-steps.  (Column mode always shuffles: it needs
-    // M >= 8192 E.)
+    // are a whole number of dwords (ld % 128 == 0: the 16-byte LDS-direct
+    // loads then start on 4-byte boundaries, which they take, the range check
+    // working per dword), else the two aligned dwords around each row's 2
+    // K-steps.  (Column mode always shuffles: it needs M >= 8192 E.)
     p.sAs = p.sBs = nullptr;
     p.sgroups = 0;
     if (pl.ncol) return MXW_ERR_DIM;  // unreachable by construction of the plan
-    if ((ldb & 511) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
+    if ((ldb & 127) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
     else hipLaunchKernelGGL((wgrad_kernel<false, false>), g, blk, 0, st, p);
   } else {
-    // long experts (M >= 4096 E) or scale rows not 16-byte aligned
-    // (ld % 512 != 0): rewrite the scale planes into the workspace so that the
+    // long experts (M >= 4096 E) or scale rows not a whole number of dwords
+    // (ld % 128 != 0): rewrite the scale planes into the workspace so that the
     // K-loop's grouped scale loads read consecutive bytes (the same kernel
     // clears column mode's counters); at short experts the extra pass costs
     // more than the scattered scale loads do (~4 us against ~1 us at 1,024
@@ -1930,6 +1933,7 @@ int check_wgrad_args(const void* A, const void* sA, const void* B, const void* s
     return MXW_ERR_DIM;
   if (ld >= 0 && (ld < M || ld > MXW_MAX_TOKENS || (ld & 31))) return MXW_ERR_DIM;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
+  if (!bf && (((uintptr_t)sA | (uintptr_t)sB) & 3)) return MXW_ERR_ALIGN;
   return MXW_OK;
 }
 
@@ -2040,6 +2044,7 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
       (N & 15) || N > 65536)
     return MXW_ERR_DIM;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)out) & 15) return MXW_ERR_ALIGN;
+  if (((uintptr_t)sA | (uintptr_t)sB) & 3) return MXW_ERR_ALIGN;
   const int64_t grid = mxw_fwd_grid_size(E, R, N);
   if (grid <= 0 || grid * kThreads > 0xFFFFFFFFLL) return MXW_ERR_DIM;
   int rc = check_device();
@@ -2063,7 +2068,7 @@ int mxfp8_grouped_fwd(const uint8_t* A, const uint8_t* sA, const uint8_t* B, con
     hipLaunchKernelGGL((rows_kernel<false, true, true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   else if (C <= kWholeC)
     hipLaunchKernelGGL((rows_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
-  else if ((C & 511) == 0)
+  else if ((C & 127) == 0)  // 16-byte scale groups from dword-aligned rows
     hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   else
     hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
@@ -2093,7 +2098,7 @@ const char* mxw_strerror(int code) {
     case MXW_OK: return "ok";
     case MXW_ERR_NULL: return "a required pointer is NULL";
     case MXW_ERR_DIM: return "a size (E, M, N, K, R or C) outside the supported range";
-    case MXW_ERR_ALIGN: return "A, B or out is not 16-byte aligned";
+    case MXW_ERR_ALIGN: return "A, B or out is not 16-byte aligned, or sA or sB not 4-byte aligned";
     case MXW_ERR_DEVICE: return "the current device is not gfx950 (or no device)";
     case MXW_ERR_LAUNCH: return "kernel launch failed";
     case MXW_ERR_WORKSPACE: return "workspace missing, smaller than the size query returned, or not 256-byte aligned";

@@ -78,6 +78,8 @@ P = 0x10000
     ((P, P, P, P, P, 4, 16 * 1024 * 1024, 128, 256, P), -2),  # M beyond the supported range
     ((P + 8, P, P, P, P, 4, 512, 128, 256, P), -3),        # A misaligned
     ((P, P, P, P, P, 4, 512, 128, 256, P + 2), -3),        # out misaligned
+    ((P, P + 2, P, P, P, 4, 512, 128, 256, P), -3),        # sA not 4-byte aligned
+    ((P, P, P, P + 1, P, 4, 512, 128, 256, P), -3),        # sB not 4-byte aligned
 ])
 def test_host_argument_checks(args, code):
     assert mxw.mxfp8_wgrad_grouped(*args) == code
@@ -168,7 +170,8 @@ def test_scale_shuffle_rule():
     rows (M % 512 != 0); host-only, no device needed."""
     assert mxw.scale_shuffle(8, 196608) and mxw.scale_shuffle(32, 262144)
     assert not mxw.scale_shuffle(8, 8192)          # 1,024 tokens per expert, aligned rows
-    assert mxw.scale_shuffle(8, 8192 + 32)         # M % 512 != 0
+    assert mxw.scale_shuffle(8, 8192 + 32)         # M % 128 != 0: scale rows not a whole number of dwords
+    assert not mxw.scale_shuffle(8, 8192 + 128)    # M % 512 != 0 but dword-aligned scale rows: direct loads
     assert mxw.scale_shuffle(1, 4096) and not mxw.scale_shuffle(2, 4096)
     with pytest.raises(mxw.MxwError):
         mxw.scale_shuffle(0, 512)
@@ -210,6 +213,8 @@ def test_fwd_grid_size():
     ((P, P, P, P, P, 4, 512, 256, 131072, P), -2),         # N too large
     ((P, P, P + 8, P, P, 4, 512, 256, 128, P), -3),        # B misaligned
     ((P, P, P, P, P, 4, 512, 256, 128, P + 2), -3),        # out misaligned
+    ((P, P + 1, P, P, P, 4, 512, 256, 128, P), -3),        # sA not 4-byte aligned
+    ((P, P, P, P + 2, P, 4, 512, 256, 128, P), -3),        # sB not 4-byte aligned
 ])
 def test_fwd_host_argument_checks(args, code):
     assert mxw.mxfp8_grouped_fwd(*args) == code

@@ -57,7 +57,8 @@ ROWS_CASES = [
     (6, 520, 2048, 1408, [100, 32, 0, 200, 96, 64]),  # 16B gate/up widths (C % 512 == 0: grouped scale loads)
     (3, 520, 1440, 272, [0, 260, 200]),         # whole-tile scale blocks, 45-byte scale rows (odd)
     (2, 600, 1504, 128, [300, 257]),            # the largest C with whole-tile scale blocks
-    (2, 300, 1568, 160, [150, 100]),            # C % 512 != 0 above it: the paired scale path
+    (2, 300, 1568, 160, [150, 100]),            # C % 128 != 0 above it: the paired scale path
+    (3, 400, 1664, 144, [130, 0, 200]),         # C % 128 == 0, C % 512 != 0: 16-byte groups from 4-byte-aligned rows
 ]
 
 
