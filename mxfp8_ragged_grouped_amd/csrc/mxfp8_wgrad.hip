@@ -73,8 +73,9 @@
 //     bytes of 256 rows lie in 256 cache lines, and at long experts that
 //     costs the weight gradient ~6%; it then first rewrites the planes so that
 //     a band's groups are contiguous (scale_shuffle_kernel).  The same runs
-//     when scale rows are not a whole number of dwords (M % 128 != 0).  The
-//     row-ragged GEMM reads its planes directly: a tile's whole scale blocks
+//     when scale rows are not a whole number of dwords (M % 128 != 0); without
+//     a workspace such rows are read a dword early and each word is joined
+//     from two.  The row-ragged GEMM reads its planes directly: a tile's whole scale blocks
 //     once, in the prologue, when C <= 1,504, otherwise 16-byte groups
 //     (C % 128 == 0) or the two aligned dwords around a row's 4 bytes of 2
 //     K-steps.  A scale load per row per
@@ -494,11 +495,12 @@ struct Piece {
 // blocks are neither loaded nor read, and their MFMAs are not issued: half
 // the MFMA work and a quarter less staging per K-step.
 template <bool GROUP, bool COL, bool ROWS, bool BF = false, bool WHOLE = false, bool HALF = false, bool SHORT = false,
-          bool WALIGN = false>
+          bool WALIGN = false, bool GUNAL = false>
 __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece& pc) {
   static_assert(!HALF || (!COL && !ROWS && !WHOLE), "half tiles: weight gradient, one workgroup per tile");
   static_assert(!SHORT || (!ROWS && !WHOLE && !HALF), "short tiles: weight gradient");
   static_assert(!WALIGN || WHOLE, "dword-aligned scale rows: whole-tile scale blocks");
+  static_assert(!GUNAL || (GROUP && !COL && !ROWS && !BF), "grouped loads from unaligned rows: weight gradient, per tile");
   // A rows per wave: its 32-row blocks t < (SHORT ? 3 : 4)
   constexpr int kWaveA = SHORT ? kShort / 2 : kTile / 2;
   int tid = threadIdx.x;
@@ -616,12 +618,13 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // step by step presents one cache line per row per step to the memory path,
   // as many requests as all of the step's operand data.  So when scale rows
   // are a whole number of dwords (M % 128 == 0; a 16-byte LDS-direct load
-  // takes a 4-byte-aligned start) each row's 16 bytes of 8 consecutive
+  // takes a 4-byte-aligned start; GUNAL: any rows, each load starting at the
+  // dword boundary below the group) each row's 16 bytes of 8 consecutive
   // K-steps ("group" G = steps 8G .. 8G+7) come in one 16-byte load per lane
   // and operand, into 3 buffers by G % 3: one load per loop iteration (4
   // K-steps), operand k % 2 of group (s0 + 4 (k - k % 2)) / 8 + 2 in
   // iteration k, so no step carries a load with nothing to fetch.  Otherwise
-  // the two aligned dwords around each row's 4 bytes of 2 consecutive K-steps
+  // (the row-ragged GEMM at C % 128 != 0) the two aligned dwords around each row's 4 bytes of 2 consecutive K-steps
   // ("pair" G = steps 2G, 2G+1) are fetched, 4 loads per wave per pair, into
   // 4 buffers by pair % 4; pair G + 3 is fetched at step 2G, and loads with
   // real == false are out of range (no memory traffic, but address-unit
@@ -632,10 +635,14 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // grouped: one operand's 16 bytes of group g for this lane's row, into
   // slot g % 3 (groups past the row's end read other rows' bytes or nothing;
   // they only reach steps past M, whose sub-blocks are all dead)
+  // (GUNAL: scale rows not a whole number of dwords; each row's group is
+  // loaded from the dword boundary at or below its start, (row offset) % 4
+  // bytes early, and its last bytes are the first of the next group's load)
+  const uint32_t sgrp_off = GUNAL ? (srow_off & ~3u) : srow_off;
   auto dma_scale_grp = [&](int g, int op) {
     const uint32_t dst = lds_addr(&sm.raw[(((g % 3) * 2 + op) * kTile + wave * 64) * 4]);
     dma16(op ? rsB : rsA, __builtin_amdgcn_readfirstlane(dst),
-          srow_off + (SHUF ? (uint32_t)(kTile * 16) : 16u) * (uint32_t)g, 0u);
+          sgrp_off + (SHUF ? (uint32_t)(kTile * 16) : 16u) * (uint32_t)g, 0u);
   };
   auto dma_scales = [&](int grp_idx, bool real) {
     {
@@ -775,6 +782,14 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
         a = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
         b = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
+        if (GUNAL) {
+          // the dword after, in this group's load or the next group's
+          const int ns = dw < 3 ? slot : (slot + 1) % 3, nd = dw < 3 ? dw + 1 : 0;
+          a = __builtin_amdgcn_alignbit(sm.raw[((ns * 2 + 0) * kTile + RA) * 4 + nd], a,
+                                        (((uint32_t)RA * sbytes) & 3u) * 8u);
+          b = __builtin_amdgcn_alignbit(sm.raw[((ns * 2 + 1) * kTile + RB) * 4 + nd], b,
+                                        (((uint32_t)RB * sbytes) & 3u) * 8u);
+        }
       } else {
         const int slot = (x >> 1) & 3;
         a = __builtin_amdgcn_alignbit(sm.raw[((slot * 2 + 0) * 2 + 1) * kTile + RA],
@@ -789,22 +804,34 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 
   // grouped: the raw dwords are read a few MFMAs before they are shifted and
   // masked, so the wave does not wait on the LDS between two MFMAs
-  auto read_raw = [&](int x, uint32_t* a4, uint32_t* b4) {
+  auto read_raw = [&](int x, uint32_t* a4, uint32_t* b4, uint32_t* an4, uint32_t* bn4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int RA = wn * kWaveA + 32 * i + fr, RB = wk * 128 + 32 * i + fr;
       const int slot = (x >> 3) % 3, dw = (x & 7) >> 1;
       a4[i] = sm.raw[((slot * 2 + 0) * kTile + RA) * 4 + dw];
       b4[i] = sm.raw[((slot * 2 + 1) * kTile + RB) * 4 + dw];
+      if (GUNAL) {
+        const int ns = dw < 3 ? slot : (slot + 1) % 3, nd = dw < 3 ? dw + 1 : 0;
+        an4[i] = sm.raw[((ns * 2 + 0) * kTile + RA) * 4 + nd];
+        bn4[i] = sm.raw[((ns * 2 + 1) * kTile + RB) * 4 + nd];
+      }
     }
   };
-  auto finish_sregs = [&](int x, const uint32_t* a4, const uint32_t* b4, uint32_t* ra4, uint32_t* rb4) {
+  auto finish_sregs = [&](int x, const uint32_t* a4, const uint32_t* b4, const uint32_t* an4, const uint32_t* bn4,
+                          uint32_t* ra4, uint32_t* rb4) {
     const uint32_t pm = (((live_mask_q(x, qs, qn) >> msb) & 1u) ? 0xFFu : 0u) |
                         (((live_mask_q(x + 1, qs, qn) >> msb) & 1u) ? 0xFF0000u : 0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra4[i] = (a4[i] >> mshift) & pm;
-      rb4[i] = (b4[i] >> mshift) & pm;
+      uint32_t a = a4[i], b = b4[i];
+      if (GUNAL) {
+        const uint32_t RA = (uint32_t)(wn * kWaveA + 32 * i + fr), RB = (uint32_t)(wk * 128 + 32 * i + fr);
+        a = __builtin_amdgcn_alignbit(an4[i], a, ((RA * sbytes) & 3u) * 8u);
+        b = __builtin_amdgcn_alignbit(bn4[i], b, ((RB * sbytes) & 3u) * 8u);
+      }
+      ra4[i] = (a >> mshift) & pm;
+      rb4[i] = (b >> mshift) & pm;
     }
   };
 
@@ -829,7 +856,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
 
   v8i fa[2][4], fb[2][4];
   uint32_t sra[2][4], srb[2][4];  // [pair parity][32-row block]
-  uint32_t rawa[4], rawb[4];
+  uint32_t rawa[4], rawb[4], rawan[4], rawbn[4];
   if (!BF) load_sregs(s0, sra[0], srb[0]);
   {
     const uint8_t* ta = sm.data[0][0] + (wn * kWaveA) * kRowBytes;
@@ -956,7 +983,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
         if (!BF && GROUP && (u & 1) && m == 10) {
           int sq = s;
           asm volatile("" : "+s"(sq));
-          read_raw(sq + 1, rawa, rawb);
+          read_raw(sq + 1, rawa, rawb, rawan, rawbn);
         }
         if (WHOLE && (u & 1) && m >= 2 && m < 6) {
           int sq = s;
@@ -996,7 +1023,7 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
           // odd step: the next pair's scale registers (its raw bytes landed
           // with the pair, certified by this step's barrier)
           if (!BF && (u & 1)) {
-            if (GROUP) finish_sregs(sp + 1, rawa, rawb, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
+            if (GROUP) finish_sregs(sp + 1, rawa, rawb, rawan, rawbn, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
             else if (!WHOLE) load_sregs(sp + 1, sra[((u >> 1) + 1) & 1], srb[((u >> 1) + 1) & 1]);
           }
           if (!(u & 1)) livep = live_mask_pair(((sp + 1) >> 1) + 2, qs, qn);
@@ -1162,10 +1189,12 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   }
 }
 
-// GROUP: scale rows are a whole number of dwords (M % 128 == 0) and scales
-// are loaded 8 K-steps at a time; otherwise 2 K-steps at a time.  COL: column mode (see
+// GROUP: scales are loaded 8 K-steps (16 bytes per row) at a time, from rows
+// that are a whole number of dwords (M % 128 == 0) or, GUNAL, from the dword
+// boundary below any row's group; otherwise 2 K-steps at a time (the paired
+// path, which only the row-ragged GEMM still takes).  COL: column mode (see
 // Params); otherwise one workgroup per (expert, tile).  BF: bf16 operands.
-template <bool GROUP, bool COL, bool BF = false>
+template <bool GROUP, bool COL, bool BF = false, bool GUNAL = false>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -1295,17 +1324,17 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
     if (half >= 0) {
       // a short tile is not split: half 0 computes all of it
       if (shrt) {
-        if (half == 0) run_piece<GROUP, false, false, BF, false, false, true>(p, sm, pc);
+        if (half == 0) run_piece<GROUP, false, false, BF, false, false, true, false, GUNAL>(p, sm, pc);
         return;
       }
       pc.half = half;
-      run_piece<GROUP, false, false, BF, false, true>(p, sm, pc);
+      run_piece<GROUP, false, false, BF, false, true, false, false, GUNAL>(p, sm, pc);
       return;
     }
     if (shrt)
-      run_piece<GROUP, false, false, BF, false, false, true>(p, sm, pc);
+      run_piece<GROUP, false, false, BF, false, false, true, false, GUNAL>(p, sm, pc);
     else
-      run_piece<GROUP, false, false, BF>(p, sm, pc);
+      run_piece<GROUP, false, false, BF, false, false, false, false, GUNAL>(p, sm, pc);
   } else {
     // ---- column mode: the pieces of this column, in sequence order -------------
     for (;;) {
@@ -1852,16 +1881,18 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
       hipLaunchKernelGGL((wgrad_kernel<false, false, true>), g, blk, 0, st, p);
     }
   } else if (!pl.shuffle) {
-    // the caller's scale planes: 16-byte groups of 8 K-steps when scale rows
-    // are a whole number of dwords (ld % 128 == 0: the 16-byte LDS-direct
-    // loads then start on 4-byte boundaries, which they take, the range check
-    // working per dword), else the two aligned dwords around each row's 2
-    // K-steps.  (Column mode always shuffles: it needs M >= 8192 E.)
+    // the caller's scale planes, 16-byte groups of 8 K-steps per row: from the
+    // row's own offset when scale rows are a whole number of dwords (ld % 128
+    // == 0; the 16-byte LDS-direct loads then start on 4-byte boundaries,
+    // which they take, the range check working per dword), else from the
+    // dword boundary below it, each scale word then joined from two
+    // consecutive dwords (GUNAL).  (Column mode always shuffles: it needs
+    // M >= 8192 E.)
     p.sAs = p.sBs = nullptr;
     p.sgroups = 0;
     if (pl.ncol) return MXW_ERR_DIM;  // unreachable by construction of the plan
     if ((ldb & 127) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
-    else hipLaunchKernelGGL((wgrad_kernel<false, false>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((wgrad_kernel<true, false, false, true>), g, blk, 0, st, p);
   } else {
     // long experts (M >= 4096 E) or scale rows not a whole number of dwords
     // (ld % 128 != 0): rewrite the scale planes into the workspace so that the
