@@ -120,7 +120,7 @@ int mxfp8_wgrad_grouped(const uint8_t* A, const uint8_t* sA, const uint8_t* B, c
  * described there (0 = M).  Reads device properties only.  128 MiB of FP32
  * partial tiles on a 256-CU device when the launch runs in column mode
  * (mxw_columns() > 0), plus (ceil(N/256) + ceil(K/256)) * ceil(M/512) * 4 KiB
- * of shuffled scales when it pre-shuffles (M >= 4096 E, or ld % 128 != 0):
+ * of shuffled scales when it pre-shuffles (M >= 4096 E):
  * 149 MiB at the 16B shape with 196,608 tokens, 88 MiB at 671B gate/up with
  * 262,144.
  */
@@ -138,7 +138,7 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K);
  *    fixed order through FP32 partial tiles in the workspace: the last of
  *    its pieces to finish (found with a device-scope counter) adds the
  *    others' partials.  No workgroup ever waits for another.
- *  - the scale pre-shuffle (M >= 4096 E or ld % 128 != 0): a short first
+ *  - the scale pre-shuffle (M >= 4096 E): a short first
  *    kernel rewrites sA and sB into the workspace so that the main kernel's
  *    scale loads read consecutive bytes (the blog has a per-call pre-shuffle
  *    too, section 5.6).
@@ -155,9 +155,8 @@ int64_t mxfp8_wgrad_workspace_size(int E, int M, int ld, int N, int K);
  *                    padded by an odd number of 128-token lines
  *                    (ld = M + 128) avoids that at long experts (16B shape,
  *                    196,608 tokens: 35% fewer HBM bytes, 3-4% faster;
- *                    671B: 13% fewer reads, 2-3% faster).  A stride that is
- *                    not a multiple of 128 needs the scale pre-shuffle,
- *                    which loses at short experts (~1,000 tokens each).
+ *                    671B: 13% fewer reads, 2-3% faster; within 2% of
+ *                    contiguous rows at ~1,000 tokens per expert).
  *                    mxfp8_quantize_tokens writes such padded rows.
  *   workspace        caller-owned device memory, 256-byte aligned, of at
  *                    least mxfp8_wgrad_workspace_size(E, M, ld, N, K) bytes
@@ -299,7 +298,7 @@ int mxw_tail_split(int E, int M, int N, int K);
 
 /*
  * mxw_scale_shuffle -- 1 if mxfp8_wgrad_grouped_ws with (E, M) runs the scale
- * pre-shuffle kernel before the main kernel (M >= 4096 E or M % 128 != 0),
+ * pre-shuffle kernel before the main kernel (M >= 4096 E),
  * 0 if it launches the main kernel alone, MXW_ERR_DIM for invalid sizes.
  * Host-only: no device access.
  */

@@ -72,10 +72,10 @@
 //     8 K-steps of scales (GROUP = true).  In the caller's planes those 16
 //     bytes of 256 rows lie in 256 cache lines, and at long experts that
 //     costs the weight gradient ~6%; it then first rewrites the planes so that
-//     a band's groups are contiguous (scale_shuffle_kernel).  The same runs
-//     when scale rows are not a whole number of dwords (M % 128 != 0); without
-//     a workspace such rows are read a dword early and each word is joined
-//     from two.  The row-ragged GEMM reads its planes directly: a tile's whole scale blocks
+//     a band's groups are contiguous (scale_shuffle_kernel).  Scale rows that
+//     are not a whole number of dwords (M % 128 != 0) are read a dword early
+//     and each word is joined from two.  The row-ragged GEMM reads its planes
+//     directly: a tile's whole scale blocks
 //     once, in the prologue, when C <= 1,504, otherwise 16-byte groups
 //     (C % 128 == 0) or the two aligned dwords around a row's 4 bytes of 2
 //     K-steps.  A scale load per row per
@@ -1698,7 +1698,7 @@ int check_device(int* cus = nullptr) {
 
 // whether an E4M3 weight-gradient call with a workspace pre-shuffles its
 // scales for (E, M) and row stride ld
-bool uses_scale_shuffle(int E, int M, int ld) { return (ld & 127) != 0 || (int64_t)M >= (int64_t)kShufTokens * E; }
+bool uses_scale_shuffle(int E, int M, int ld) { return (int64_t)M >= (int64_t)kShufTokens * E; }
 
 // One workgroup per tile (operands and scales read from the caller's buffers): how
 // many of the last tiles of the dealing (the shortest experts', longest
@@ -1894,12 +1894,11 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
     if ((ldb & 127) == 0) hipLaunchKernelGGL((wgrad_kernel<true, false>), g, blk, 0, st, p);
     else hipLaunchKernelGGL((wgrad_kernel<true, false, false, true>), g, blk, 0, st, p);
   } else {
-    // long experts (M >= 4096 E) or scale rows not a whole number of dwords
-    // (ld % 128 != 0): rewrite the scale planes into the workspace so that the
-    // K-loop's grouped scale loads read consecutive bytes (the same kernel
-    // clears column mode's counters); at short experts the extra pass costs
-    // more than the scattered scale loads do (~4 us against ~1 us at 1,024
-    // tokens per expert)
+    // long experts (M >= 4096 E): rewrite the scale planes into the workspace
+    // so that the K-loop's grouped scale loads read consecutive bytes (the same
+    // kernel clears column mode's counters); at short experts the extra pass
+    // costs more than the scattered scale loads do (~4 us against ~1 us at
+    // 1,024 tokens per expert, whatever the row alignment)
     ShufArgs sa;
     sa.s[0] = sA;
     sa.s[1] = sB;

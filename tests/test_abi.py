@@ -170,8 +170,9 @@ def test_scale_shuffle_rule():
     rows (M % 512 != 0); host-only, no device needed."""
     assert mxw.scale_shuffle(8, 196608) and mxw.scale_shuffle(32, 262144)
     assert not mxw.scale_shuffle(8, 8192)          # 1,024 tokens per expert, aligned rows
-    assert mxw.scale_shuffle(8, 8192 + 32)         # M % 128 != 0: scale rows not a whole number of dwords
-    assert not mxw.scale_shuffle(8, 8192 + 128)    # M % 512 != 0 but dword-aligned scale rows: direct loads
+    assert not mxw.scale_shuffle(8, 8192 + 32)     # short experts: direct loads, whatever the row alignment
+    assert not mxw.scale_shuffle(8, 8192 + 128)
+    assert mxw.scale_shuffle(2, 8192 + 32)         # long experts: shuffled, whatever the row alignment
     assert mxw.scale_shuffle(1, 4096) and not mxw.scale_shuffle(2, 4096)
     with pytest.raises(mxw.MxwError):
         mxw.scale_shuffle(0, 512)

@@ -97,7 +97,7 @@ def test_hand_case_embedded(golden_dir):
 RAGGED_CASES = [
     # E, N, K, M, sizes (sum <= M; the rest is padding)
     (3, 272, 528, 1024, [96, 0, 800]),          # partial N and K tiles, empty expert, padding
-    (5, 256, 256, 1056, [32, 160, 64, 352, 416]),  # M % 128 != 0 (byte scale path), short groups
+    (5, 256, 256, 1056, [32, 160, 64, 352, 416]),  # M % 128 != 0 (scale rows read a dword early), short groups
     (2, 512, 256, 2048, [1888, 160]),           # long group, tail step inside the last 128 tokens
     (4, 144, 400, 640, [0, 0, 608, 0]),         # only one live expert, odd start
     (1, 16, 16, 32, [32]),                      # the smallest problem

@@ -1,12 +1,11 @@
 """The weight gradient's scale paths (needs an MI355X).
 
-With a workspace, long experts (M >= 4096 E) or scale rows that are not a
-whole number of dwords (M % 128 != 0) make the library first rewrite the scale
-planes so that each workgroup's scale loads read consecutive bytes; otherwise,
-and always without a workspace, the K-loop reads the caller's planes directly
-(16 bytes of 8 K-steps per row when rows are a whole number of dwords, those
-loads then starting on 4-byte boundaries unless M % 512 == 0, else the two
-aligned dwords around a row's 2 K-steps).  All feed the same scale bytes to the same
+With a workspace, long experts (M >= 4096 E) make the library first rewrite
+the scale planes so that each workgroup's scale loads read consecutive bytes;
+otherwise, and always without a workspace, the K-loop reads the caller's planes
+directly, 16 bytes of 8 K-steps per row (from 16-byte or 4-byte aligned rows,
+or, when rows are not a whole number of dwords, from the dword boundary below
+each row's group, every scale word then joined from two dwords).  All feed the same scale bytes to the same
 MFMA sequence, so on one problem they must give identical bits.
 """
 import numpy as np
@@ -39,9 +38,9 @@ def run(cfg, offs, plain=False):
 @pytest.mark.parametrize("M", [8192, 8192 + 128, 8192 + 160])
 def test_shuffled_and_direct_scales_bitwise_equal(M):
     """E = 1 with M >= 4096 takes the shuffled path with a workspace; without
-    one the same problem reads the caller's planes (16-byte groups when
-    M % 128 == 0, from 16-byte or only 4-byte aligned rows; aligned dword
-    pairs otherwise).  N x K is large enough that
+    one the same problem reads the caller's planes (16-byte groups: from
+    16-byte or only 4-byte aligned rows when M % 128 == 0, otherwise read a
+    dword early).  N x K is large enough that
     the workspace entry runs one workgroup per tile too."""
     N, K = 8192, 8448
     used = 8192 - 96

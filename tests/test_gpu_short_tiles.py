@@ -97,13 +97,14 @@ def test_short_tiles_column_mode_and_shuffled_bands():
 
 
 def test_short_tiles_shuffled_and_direct_scales_bitwise_equal():
-    """Scale rows that are not 16-byte aligned (M % 512 != 0) make the
-    workspace entry pre-shuffle the scales of each tile's band (a short tile's
-    band starts at its own first row); the entry without one reads the
-    caller's planes as aligned dword pairs.  One workgroup per tile in both,
-    the same MFMA sequence: identical bits, NaN scales in the padding included."""
-    E, N, K, M = 8, 1408, 1024, 8192 + 160
-    sizes = [1024] * E
+    """Long experts (M >= 4096 E) make the workspace entry pre-shuffle the
+    scales of each tile's band (a short tile's band starts at its own first
+    row); the entry without one reads the caller's planes, whose rows are not
+    a whole number of dwords here (M % 128 != 0), a dword early.  One
+    workgroup per tile in both, the same MFMA sequence: identical bits, NaN
+    scales in the padding included."""
+    E, N, K, M = 2, 1408, 1024, 8192 + 160
+    sizes = [4096] * E
     assert mxw.columns(E, M, N, K) == 0 and mxw.scale_shuffle(E, M)
     cfg = W.make_random(E, N, K, M, sizes, seed=613, device=DEV)
     cfg["sA"][:, 8192 // 32:] = 0xFF
