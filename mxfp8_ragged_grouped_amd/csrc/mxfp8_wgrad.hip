@@ -375,6 +375,7 @@ struct Params {
   uint32_t* flags;  // [ncol][kMem] arrival counters of cut regions, cleared by the call's first kernel
   int ncol;
   int regions;  // regions of up to kMem tiles per expert
+  int rband;    // tile rows per band of regions (see region_tile)
   int hov;      // per-region cost, in K-steps, added to the split's weights
   // tiles along N of 256 rows; tiles tn >= tall have kShort rows (starting at
   // 256 tall + 192 (tn - tall)); tall = tilesN when N has no short tiles
@@ -393,27 +394,29 @@ __device__ __forceinline__ int window_iters(int start, int len) {
 }
 
 // Region r of an expert's tile grid and its member j (0 .. kMem-1): bands of
-// 4 tile rows hold 4 x (kMem / 4) regions; a last band of h < 4 rows holds
-// h x (kMem / h) regions (3 x 5 for h = 3).  A region's tiles share 4 (or h)
-// A stripes and kMem / 4 (or kMem / h) B stripes, which its members stream
-// together through their XCD's L2.  Returns false if member j has no tile.
-__device__ __forceinline__ bool region_tile(int tN, int tK, int r, int j, int& tn, int& tk) {
-  constexpr int wf = kMem / 4;
-  const int full = tN >> 2, rpf = (tK + wf - 1) / wf;
+// H tile rows hold H x (kMem / H) regions; a last band of h < H rows holds
+// h x (kMem / h) regions (3 x 5 for h = 3).  A region's tiles share H (or h)
+// A stripes and kMem / H (or kMem / h) B stripes, which its members stream
+// together through their XCD's L2.  H (4, 8 or 2) is chosen on the host so
+// that the regions leave the fewest members without a tile (region_band).
+// Returns false if member j has no tile.
+__device__ __forceinline__ bool region_tile(int tN, int tK, int H, int r, int j, int& tn, int& tk) {
+  const int wf = kMem / H;
+  const int full = tN / H, rpf = (tK + wf - 1) / wf;
   int band, c, h, w;
   if (r < full * rpf) {
     band = r / rpf;
     c = r - band * rpf;
-    h = 4;
+    h = H;
     w = wf;
   } else {
     band = full;
     c = r - full * rpf;
-    h = tN - 4 * full;
+    h = tN - H * full;
     w = kMem / h;
   }
   if (j >= h * w) return false;
-  tn = 4 * band + j % h;
+  tn = H * band + j % h;
   tk = c * w + j / h;
   return tk < tK;
 }
@@ -595,8 +598,8 @@ __device__ __forceinline__ void run_piece(const Params& p, Smem& sm, const Piece
   // and of B: two instructions per operand per wave.
   int pfa = 8, pfb = 8, pfsa = 8, pfsb = 8;
   if constexpr (COL) {
-    const int full = p.tilesN >> 2, band = pc.tn >> 2;
-    const int rh = band < full ? 4 : p.tilesN - 4 * full;  // region height (tiles along N)
+    const int full = p.tilesN / p.rband, band = pc.tn / p.rband;
+    const int rh = band < full ? p.rband : p.tilesN - p.rband * full;  // region height (tiles along N)
     pfa = __builtin_amdgcn_readfirstlane(member / rh);      // index among the A stripe's sharers
     pfb = __builtin_amdgcn_readfirstlane(member % rh);      // among the B stripe's
     pfsa = __builtin_amdgcn_readfirstlane(kMem / rh);       // A stripe sharers = region width
@@ -1354,7 +1357,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(Params p) {
         ++kx;
       }
       if (lo >= hi) continue;
-      if (!region_tile(p.tilesN, p.tilesK, rcur, member, pc.tn, pc.tk)) continue;
+      if (!region_tile(p.tilesN, p.tilesK, p.rband, rcur, member, pc.tn, pc.tk)) continue;
       const int es = __builtin_amdgcn_readfirstlane(sm.start[pc.g]);
       const int ee = es + __builtin_amdgcn_readfirstlane(sm.len[pc.g]);
       const int es0 = (es / kPair) * 2;
@@ -1721,12 +1724,38 @@ int tail_split(int64_t tiles, int cus, int E, int M) {
 // experts are long enough to amortise the per-piece costs; it needs whole
 // 8-column groups (one column per XCD each), a column mask of at most 64
 // columns and a work sequence that fits in int.
-int plan_columns(int E, int M, int N, int K, int cus, int* regions) {
+// Tile rows per band of column mode's regions (region_tile): the H in
+// {4, 8, 2} whose regions leave the fewest members without a tile, 4 (the
+// squarest regions) on ties.  (16 x 6 tiles: 4-row bands make two 4 x 4 and
+// two 4 x 2 regions per 8 rows, a third of the members idle in the latter;
+// 8-row bands make three full 8 x 2 regions.)
+int region_band(int tN, int tK, int* regions) {
+  int best = 0, idle_best = 1 << 30, r_best = 0;
+  for (const int H : {4, 8, 2}) {
+    const int full = tN / H, h = tN - H * full, wf = kMem / H;
+    const int rpf = (tK + wf - 1) / wf;
+    int R = full * rpf, idle = full * (rpf * kMem - H * tK);
+    if (h) {
+      const int w = kMem / h, rl = (tK + w - 1) / w;
+      R += rl;
+      idle += rl * kMem - h * tK;
+    }
+    if (idle < idle_best) {
+      idle_best = idle;
+      best = H;
+      r_best = R;
+    }
+  }
+  *regions = r_best;
+  return best;
+}
+
+int plan_columns(int E, int M, int N, int K, int cus, int* regions, int* rband = nullptr) {
   const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
-  const int full = tN / 4, h = tN - 4 * full;
-  const int w = h ? kMem / h : 1, wf = kMem / 4;
-  const int R = full * ((tK + wf - 1) / wf) + (h ? (tK + w - 1) / w : 0);
+  int R = 0;
+  const int H = region_band(tN, tK, &R);
   *regions = R;
+  if (rband) *rband = H;
   const int ncol = (cus / kMem) & ~7;
   const int64_t items = (int64_t)E * tN * tK;
   const int64_t wmax = (int64_t)R * (4 * ((int64_t)M / 256 + 2 * E) + (int64_t)E * kColHov);
@@ -1757,7 +1786,7 @@ size_t round_ws(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 //    * 256 KiB][shuffled scale planes of A, then of B]
 // each part starting on a 4 KiB boundary.
 struct Plan {
-  int ncol, regions;
+  int ncol, regions, rband;
   bool shuffle;
   int sgroups;
   size_t flags_off, part_off, scaleA_off, scaleB_off, bytes;
@@ -1768,11 +1797,11 @@ Plan make_plan(int E, int Mb, int ldb, int tshift, int N, int K, int cus, bool w
   const int tN = (N + kTile - 1) / kTile, tK = (K + kTile - 1) / kTile;
   if (!ws) {
     int regions = 0;
-    (void)plan_columns(E, Mb, N, K, cus, &regions);
+    (void)plan_columns(E, Mb, N, K, cus, &regions, &pl.rband);
     pl.regions = regions;
     return pl;
   }
-  pl.ncol = plan_columns(E, Mb, N, K, cus, &pl.regions);
+  pl.ncol = plan_columns(E, Mb, N, K, cus, &pl.regions, &pl.rband);
   pl.shuffle = tshift == 0 && uses_scale_shuffle(E, Mb, ldb);
   size_t off = 0;
   if (pl.ncol) {
@@ -1858,6 +1887,7 @@ int launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
   }
   p.hov = kColHov;
   p.regions = pl.regions;
+  p.rband = pl.rband;
   p.ncol = pl.ncol;
   if (pl.ncol) {
     p.flags = (uint32_t*)(wsb + pl.flags_off);

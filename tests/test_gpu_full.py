@@ -12,7 +12,8 @@ then runs in column mode), against the oracle on whole 256 x 256 output tiles:
     the four corner pairs (first and last tiles of every expert, the partial
     last N tile at 16B) plus seeded random pairs, every expert's tile of each
     pair: 96 to 384 whole tiles per workload; the 256-expert stress at the
-    16B shape: the four corner pairs, 1,024 whole tiles;
+    16B shape: the four corner pairs, 1,024 whole tiles; the 16B down
+    projection (N = 2048, K = 1408: column mode with 8-row bands of regions);
   * the entry point without a workspace on the headline shape, the same way.
 
 Every element must be finite (no skipped store) and empty experts exact +0;
@@ -73,7 +74,7 @@ def test_16b_24k_whole_output():
 
 
 @pytest.mark.parametrize("name", ["16b_24k_skew1.2", "16b_24k_skew1.7", "16b_24k_balanced", "16b_24k_ramp",
-                                  "671b_gateup", "671b_down", "671b_down_zipf", "16b_256e"])
+                                  "671b_gateup", "671b_down", "671b_down_zipf", "16b_256e", "16b_down"])
 def test_full_size_tiles(name):
     cfg = W.make_config(name, device=DEV)
     check_tiles(cfg, name, "ws", tile_pairs(cfg, 4 if cfg["E"] > 64 else 12, 17))

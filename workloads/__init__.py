@@ -57,6 +57,10 @@ CONFIGS = {
     # ragged-edge stress at the 671B down shape: Zipf routing, 4 empty
     # experts, every non-first group start an odd multiple of 32
     "671b_down_zipf": dict(E=32, N=7168, K=2048, M=131072, routing=("zipf", 1.1, 4), values="wide", cid=5),
+    # the 16B down projection's weight gradient (not a configuration of the
+    # pages, which measure gate/up): N = hidden 2048, K = intermediate 1408
+    "16b_down": dict(E=8, N=2048, K=1408, M=196608, routing=("dirichlet", 8.0, (1.45, 1.55), 0), values=(1.0, 0.5),
+                     cid=62),
     # many-expert stress (not a configuration of the pages): 256 experts of the
     # 16B expert shape on one GPU, mean 1,024 tokens/expert, busiest ~1.8x
     "16b_256e": dict(E=256, N=1408, K=2048, M=262144, routing=("dirichlet", 8.0, (1.45, 1.8), 0), values=(1.0, 0.5),
