@@ -120,3 +120,41 @@ def test_quantize_full_size_and_end_to_end():
     w2 = mxw.wgrad(wq_a, ws_a, wq_b, ws_b, cfg["offs"])
     torch.cuda.synchronize()
     assert torch.equal(w1.view(torch.int16), w2.view(torch.int16))
+
+
+STRIDE_CASES = [
+    # M, H, ld - M, byte offset of s in its buffer
+    (640, 272, 128, 0),   # scale rows 4-byte aligned: one 4-byte scale store per hidden row and tile
+    (640, 272, 32, 0),    # ld / 32 odd: scale rows start at any byte, byte stores
+    (640, 272, 0, 1),     # s itself not 4-byte aligned, byte stores
+    (608, 80, 64, 3),     # a partial last token tile as well
+]
+
+
+@pytest.mark.parametrize("case", range(len(STRIDE_CASES)))
+def test_quantize_row_stride_and_scale_alignment(case):
+    """Codes and scales written into [H, ld] / [H, ld/32] rows, the scale
+    plane at any byte offset: every byte equals the oracle's, and the padding
+    columns and the bytes around the scale plane keep their poison."""
+    M, H, pad, soff = STRIDE_CASES[case]
+    ld = M + pad
+    x = make_x(M, H, "normal", 1300 + case)
+    used = M - 32
+    x[used:] = float("nan")
+    offs = torch.tensor([used // 64 * 32, used], dtype=torch.int32, device=DEV)
+    say("quant strides: M=%d H=%d ld=%d s offset %d" % (M, H, ld, soff))
+    qbuf = torch.full((H, ld), 0xAA, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((H * (ld // 32) + 8,), 0xAA, dtype=torch.uint8, device=DEV)
+    s = sbuf[soff:soff + H * (ld // 32)].view(H, ld // 32)[:, :M // 32]
+    q, s2 = mxw.quantize_tokens(x.to(DEV), offs, q=qbuf[:, :M], s=s, ld=ld)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == s.data_ptr()
+    rq, rs = oracle.quantize_tokens(to_bits(x), used=used)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    qh = qbuf.cpu().numpy()
+    assert (qh[:, M:] == 0xAA).all(), "codes written past M"
+    sh = sbuf.cpu().numpy()
+    plane = sh[soff:soff + H * (ld // 32)].reshape(H, ld // 32)
+    assert (plane[:, M // 32:] == 0xAA).all(), "scales written past M / 32"
+    assert (sh[:soff] == 0xAA).all() and (sh[soff + H * (ld // 32):] == 0xAA).all(), "bytes around s written"
