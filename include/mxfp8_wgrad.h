@@ -396,9 +396,9 @@ int64_t mxw_fwd_grid_size(int E, int R, int N);
  *   H     16 <= H <= 65536, H % 16 == 0.
  *   q     uint8  [H, ld]   codes (the first M bytes of each row).
  *   s     uint8  [H, ld/32] scales (the first M/32 bytes of each row); any
- *         alignment, but with s 4-byte aligned and ld % 128 == 0 every
- *         whole 128-token tile's scale bytes go out as one 4-byte store
- *         per row (3 to 6% faster than byte stores).
+ *         alignment, but with s 8-byte aligned and ld % 256 == 0 every
+ *         whole 256-token tile's scale bytes go out as one 8-byte store
+ *         per row (faster than byte stores).
  *   stream  a hipStream_t, passed as void*.
  *
  * Host-checked preconditions return an error code and launch nothing:

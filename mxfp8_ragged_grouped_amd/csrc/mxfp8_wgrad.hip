@@ -1587,22 +1587,23 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
   for (int i = (int)threadIdx.x; i < n; i += 256) p[i] = 0u;
 }
 
-constexpr int kQTok = 128, kQHid = 64;
+constexpr int kQTok = 256, kQHid = 64;
 // The codes overwrite the bf16 tile once every thread holds its encoded
-// block in registers: 16 KiB per workgroup.
+// blocks in registers: 32 KiB per workgroup, 5 workgroups per CU.  (256
+// tokens per tile rather than 128: +2.1% at the 16B shape, +2.6% at 671B.)
 union QSmem {
-  uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (16 KiB)
-  uint8_t q[kQHid][kQTok];   // the codes, hidden rows, swizzled chunks (8 KiB)
+  uint16_t x[kQTok][kQHid];  // the bf16 tile, token rows (32 KiB)
+  uint8_t q[kQHid][kQTok];   // the codes, hidden rows, swizzled chunks (16 KiB)
 };
 
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
                                                     int E, int M, int ld, int H, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) QSmem sm;
-  __shared__ uint32_t sbw[kQHid];  // the 4 scale bytes of each hidden row
+  __shared__ uint2 sbw[kQHid];  // the 8 scale bytes of each hidden row
   const int tid = threadIdx.x;
   // Workgroups are dealt to the 8 XCDs in turn. Each XCD gets one contiguous
-  // run of tiles (token tiles fastest), so the 32 token tiles whose scale
+  // run of tiles (token tiles fastest), so the 16 token tiles whose scale
   // bytes share a 128-byte line of s write it through one L2, which writes
   // it back whole rather than as up to 8 partly dirty copies (+5% at 671B,
   // +6% at the 16B shape, against tiles in launch order).
@@ -1619,73 +1620,84 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
   {
     const int rows = max(0, min(kQTok, used - m0));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)m0 * H, (uint32_t)rows * (uint32_t)H * 2u);
-    v4i v[4];
+    v4i v[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       const int c = k * 256 + tid, r = c >> 3, h = h0 + (c & 7) * 8;
       const uint32_t off = h < H ? ((uint32_t)r * (uint32_t)H + (uint32_t)h) * 2u : kOob;
       v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 2);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       const int c = k * 256 + tid;
       *(v4i*)&sm.x[c >> 3][(c & 7) * 8] = v[k];
     }
   }
   __syncthreads();
-  // ---- encode: thread (h, b) does column h of 32-token block b -------------------
+  // ---- encode: thread (h, b) does column h of 32-token blocks b and b + 4 ----
   {
     const int h = tid & 63, b = tid >> 6;
-    uint32_t wq[8];
-    float v[32];
-    float amax = 0.0f;
+    uint32_t wq[2][8];
+    int sbp[2];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      v[i] = __builtin_bit_cast(float, (uint32_t)sm.x[b * 32 + i][h] << 16);
-      amax = fmaxf(amax, fabsf(v[i]));
+    for (int p = 0; p < 2; ++p) {
+      const int bb = b + 4 * p;
+      float v[32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        v[i] = __builtin_bit_cast(float, (uint32_t)sm.x[bb * 32 + i][h] << 16);
+        amax = fmaxf(amax, fabsf(v[i]));
+      }
+      // floor(log2 amax) = frexp exponent - 1 (exact, subnormals included)
+      int sb = amax == 0.0f ? 127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8 + 127;
+      sb = min(max(sb, 0), 254);
+      sbp[p] = sb;
+      const int sh = 127 - sb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__builtin_ldexpf(v[4 * j + t], sh), -448.0f), 448.0f);
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+        // a code of magnitude 0 (including -0) becomes +0
+        const uint32_t z = (uint32_t)c & 0x7F7F7F7Fu;
+        const uint32_t nz = ((z + 0x7F7F7F7Fu) & 0x80808080u) >> 7;
+        wq[p][j] = (uint32_t)c & (nz * 0xFFu);
+      }
     }
-    // floor(log2 amax) = frexp exponent - 1 (exact, subnormals included)
-    int sb = amax == 0.0f ? 127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8 + 127;
-    sb = min(max(sb, 0), 254);
-    const int sh = 127 - sb;
+    __syncthreads();  // every thread has read its columns of the bf16 tile
+    // 256-byte code rows span all 64 banks: chunk c of row h sits at c ^ (h % 16)
+    const int sw = h & 15;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float y[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__builtin_ldexpf(v[4 * j + t], sh), -448.0f), 448.0f);
-      int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
-      // a code of magnitude 0 (including -0) becomes +0
-      const uint32_t z = (uint32_t)c & 0x7F7F7F7Fu;
-      const uint32_t nz = ((z + 0x7F7F7F7Fu) & 0x80808080u) >> 7;
-      wq[j] = (uint32_t)c & (nz * 0xFFu);
+    for (int p = 0; p < 2; ++p) {
+      const int bb = b + 4 * p;
+      *(v4i*)&sm.q[h][((2 * bb) ^ sw) * 16] = (v4i){(int)wq[p][0], (int)wq[p][1], (int)wq[p][2], (int)wq[p][3]};
+      *(v4i*)&sm.q[h][((2 * bb + 1) ^ sw) * 16] = (v4i){(int)wq[p][4], (int)wq[p][5], (int)wq[p][6], (int)wq[p][7]};
+      ((uint8_t*)sbw)[h * 8 + bb] = (uint8_t)sbp[p];
     }
-    __syncthreads();  // every thread has read its column of the bf16 tile
-    const int sw = (h >> 1) & 7;
-    *(v4i*)&sm.q[h][((2 * b) ^ sw) * 16] = (v4i){(int)wq[0], (int)wq[1], (int)wq[2], (int)wq[3]};
-    *(v4i*)&sm.q[h][((2 * b + 1) ^ sw) * 16] = (v4i){(int)wq[4], (int)wq[5], (int)wq[6], (int)wq[7]};
-    ((uint8_t*)sbw)[h * 4 + b] = (uint8_t)sb;
   }
   __syncthreads();
-  // ---- scales: one 4-byte store per hidden row where the tile is whole and
-  // the row's 4 bytes are dword-aligned, else byte stores (4 byte stores per
-  // row from the 4 waves measured 3 to 6% slower)
+  // ---- scales: one 8-byte store per hidden row where the tile is whole and
+  // the row's 8 bytes are 8-byte aligned, else byte stores (byte stores from
+  // the waves, at 128-token tiles, measured 3 to 6% slower than one store)
   if (tid < kQHid && h0 + tid < H) {
     uint8_t* srow = s + (size_t)(h0 + tid) * (size_t)(ld >> 5) + (m0 >> 5);
-    if (m0 + kQTok <= M && ((((uintptr_t)s) | (uintptr_t)(ld >> 5)) & 3) == 0)
-      *(uint32_t*)srow = sbw[tid];
+    if (m0 + kQTok <= M && ((((uintptr_t)s) | (uintptr_t)(ld >> 5)) & 7) == 0)
+      *(uint2*)srow = sbw[tid];
     else
-      for (int b = 0; b < 4 && m0 + 32 * b < M; ++b) srow[b] = ((const uint8_t*)sbw)[tid * 4 + b];
+      for (int b = 0; b < 8 && m0 + 32 * b < M; ++b) srow[b] = ((const uint8_t*)sbw)[tid * 8 + b];
   }
-  // ---- store: chunk c = 256 k + tid is hidden row c / 8, tokens 16 (c % 8) .. +15
+  // ---- store: chunk c = 256 k + tid is hidden row c / 16, tokens 16 (c % 16) .. +15
   // (non-temporal: the codes are not read again by this kernel, and keeping
   // them out of the L2 leaves it to the input rows: +4.0% at the 16B shape,
   // +1.2% at 671B, same bytes)
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = k * 256 + tid, r = c >> 3, c8 = c & 7;
-    const int h = h0 + r, m = m0 + c8 * 16;
-    if (h < H && m < M) __builtin_nontemporal_store(*(const v4i*)&sm.q[r][(c8 ^ ((r >> 1) & 7)) * 16], (v4i*)(q + (size_t)h * ld + m));
+  for (int k = 0; k < 4; ++k) {
+    const int c = k * 256 + tid, r = c >> 4, c16 = c & 15;
+    const int h = h0 + r, m = m0 + c16 * 16;
+    if (h < H && m < M) __builtin_nontemporal_store(*(const v4i*)&sm.q[r][(c16 ^ (r & 15)) * 16], (v4i*)(q + (size_t)h * ld + m));
   }
 }
 

@@ -124,10 +124,12 @@ def test_quantize_full_size_and_end_to_end():
 
 STRIDE_CASES = [
     # M, H, ld - M, byte offset of s in its buffer
-    (640, 272, 128, 0),   # scale rows 4-byte aligned: one 4-byte scale store per hidden row and tile
+    (640, 272, 128, 0),   # ld % 256 == 0, s 8-byte aligned: one 8-byte scale store per row and whole tile
+    (640, 272, 128, 4),   # s only 4-byte aligned: byte stores
     (640, 272, 32, 0),    # ld / 32 odd: scale rows start at any byte, byte stores
-    (640, 272, 0, 1),     # s itself not 4-byte aligned, byte stores
+    (640, 272, 0, 1),     # s itself not aligned, byte stores
     (608, 80, 64, 3),     # a partial last token tile as well
+    (1024, 64, 0, 0),     # whole tiles only, the 8-byte stores throughout
 ]
 
 
