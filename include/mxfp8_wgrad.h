@@ -398,7 +398,8 @@ int64_t mxw_fwd_grid_size(int E, int R, int N);
  *   s     uint8  [H, ld/32] scales (the first M/32 bytes of each row); any
  *         alignment, but with s 8-byte aligned and ld % 256 == 0 every
  *         whole 256-token tile's scale bytes go out as one 8-byte store
- *         per row (faster than byte stores).
+ *         per row, and with s 4-byte aligned and ld % 128 == 0 as two
+ *         4-byte stores (either way faster than byte stores).
  *   stream  a hipStream_t, passed as void*.
  *
  * Host-checked preconditions return an error code and launch nothing:

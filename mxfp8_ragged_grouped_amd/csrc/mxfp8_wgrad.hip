@@ -1679,15 +1679,22 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     }
   }
   __syncthreads();
-  // ---- scales: one 8-byte store per hidden row where the tile is whole and
-  // the row's 8 bytes are 8-byte aligned, else byte stores (byte stores from
-  // the waves, at 128-token tiles, measured 3 to 6% slower than one store)
+  // ---- scales: where the tile is whole, one 8-byte store per hidden row if
+  // the row's 8 bytes are 8-byte aligned, two 4-byte stores if they are
+  // 4-byte aligned (rows ld = M + 128 tokens apart), else byte stores (byte
+  // stores from the waves, at 128-token tiles, measured 3 to 6% slower than
+  // one store)
   if (tid < kQHid && h0 + tid < H) {
     uint8_t* srow = s + (size_t)(h0 + tid) * (size_t)(ld >> 5) + (m0 >> 5);
-    if (m0 + kQTok <= M && ((((uintptr_t)s) | (uintptr_t)(ld >> 5)) & 7) == 0)
+    const uint32_t mis = (uint32_t)(((uintptr_t)s) | (uintptr_t)(ld >> 5));
+    if (m0 + kQTok <= M && (mis & 7) == 0) {
       *(uint2*)srow = sbw[tid];
-    else
+    } else if (m0 + kQTok <= M && (mis & 3) == 0) {
+      ((uint32_t*)srow)[0] = sbw[tid].x;
+      ((uint32_t*)srow)[1] = sbw[tid].y;
+    } else {
       for (int b = 0; b < 8 && m0 + 32 * b < M; ++b) srow[b] = ((const uint8_t*)sbw)[tid * 8 + b];
+    }
   }
   // ---- store: chunk c = 256 k + tid is hidden row c / 16, tokens 16 (c % 16) .. +15
   // (non-temporal: the codes are not read again by this kernel, and keeping

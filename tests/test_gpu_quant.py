@@ -125,7 +125,8 @@ def test_quantize_full_size_and_end_to_end():
 STRIDE_CASES = [
     # M, H, ld - M, byte offset of s in its buffer
     (640, 272, 128, 0),   # ld % 256 == 0, s 8-byte aligned: one 8-byte scale store per row and whole tile
-    (640, 272, 128, 4),   # s only 4-byte aligned: byte stores
+    (640, 272, 128, 4),   # s only 4-byte aligned: two 4-byte stores
+    (640, 272, 256, 0),   # ld % 256 == 128 (rows M + 128 tokens apart at M % 256 == 0): two 4-byte stores
     (640, 272, 32, 0),    # ld / 32 odd: scale rows start at any byte, byte stores
     (640, 272, 0, 1),     # s itself not aligned, byte stores
     (608, 80, 64, 3),     # a partial last token tile as well
