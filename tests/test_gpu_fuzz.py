@@ -96,22 +96,39 @@ def test_fwd_random_shapes(seed):
     assert (bits[used:] == BF16_NAN).all()
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_quantize_random_shapes(seed):
+    """Random shapes and padding, with row strides (multiples of 256 tokens,
+    those plus 128, M plus a random multiple of 32) and scale-plane offsets
+    (0, 8, 4 or 1 bytes into its buffer) such that the 8-byte, 4-byte and
+    byte scale stores all run; the padding columns and the
+    bytes around the scale plane keep their poison."""
     rng = np.random.default_rng(2400 + seed)
     M = 32 * int(rng.integers(1, 200))
     H = 16 * int(rng.integers(1, 80))
     used = 32 * int(rng.integers(0, M // 32 + 1))
+    # seeds 0-3: ld a multiple of 256; 4-7: a multiple of 256 plus 128; 8-11: M plus a random pad
+    pad = 32 * int(rng.integers(0, 9))
+    ld = [-(-M // 256) * 256, -(-M // 256) * 256 + 128, M + pad][(seed // 4) % 3]
+    soff = [0, 8, 4, 1][seed % 4]
     g = torch.Generator().manual_seed(2500 + seed)
     x = (torch.randn((M, H), generator=g) * torch.exp2(torch.randint(-30, 30, (1, H), generator=g).float()))
     x = x.to(torch.bfloat16)
     x[used:] = float("nan")
-    say("quant fuzz %d: M=%d H=%d used=%d" % (seed, M, H, used))
-    q, s = mxw.quantize_tokens(x.to(DEV), torch.tensor([used], dtype=torch.int32, device=DEV))
+    say("quant fuzz %d: M=%d H=%d used=%d ld=%d s offset %d" % (seed, M, H, used, ld, soff))
+    qbuf = torch.full((H, ld), 0xAA, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((H * (ld // 32) + 16,), 0xAA, dtype=torch.uint8, device=DEV)
+    splane = sbuf[soff:soff + H * (ld // 32)].view(H, ld // 32)
+    q, s = mxw.quantize_tokens(x.to(DEV), torch.tensor([used], dtype=torch.int32, device=DEV),
+                               q=qbuf[:, :M], s=splane[:, :M // 32], ld=ld)
     torch.cuda.synchronize()
     rq, rs = oracle.quantize_tokens(x.view(torch.int16).numpy().view(np.uint16), used=used)
     np.testing.assert_array_equal(s.cpu().numpy(), rs)
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    assert (qbuf[:, M:] == 0xAA).all().item(), "codes written past M"
+    assert (splane[:, M // 32:] == 0xAA).all().item(), "scales written past M / 32"
+    sh = sbuf.cpu().numpy()
+    assert (sh[:soff] == 0xAA).all() and (sh[soff + H * (ld // 32):] == 0xAA).all(), "bytes around s written"
 
 
 @pytest.mark.parametrize("seed", range(8))
